@@ -1,0 +1,152 @@
+"""Seeded synthetic KV workloads (stand-ins for model-produced caches).
+
+The pages measure on caches of SmolLM2-1.7B, Llama-3-8B and Llama-3.1-8B run
+over GSM8K / WikiText-2-like text (QKVShare results; PolyKV section 4). Neither
+models nor datasets are used here: these generators copy only the cache
+shapes and a value structure (heavy tails, outlier channels, an attention
+sink, width runs) and are the single source of inputs for both the CPU
+oracle and the GPU library. No codec arithmetic lives here.
+
+Randomness: numpy PCG64 seeded from SeedSequence([seed, cfg, tensor, layer]),
+tensor 0 = K, 1 = V, 2 = structure / widths; values are drawn per layer in
+float32 and rounded to bf16 (nearest, ties to even). bf16 tensors are numpy
+uint16 arrays of raw bit patterns, shape [L, H, T, d].
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+K_TENSOR, V_TENSOR, STRUCT_TENSOR = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    cfg: int            # workload number, part of every seed
+    name: str
+    L: int
+    H: int
+    T: int
+    d: int
+    recipe: str         # value distribution, see layer_values()
+    mode: str           # "pool" or "card"
+    agents: int = 1     # decode fan-out
+
+    @property
+    def shape(self):
+        return (self.L, self.H, self.T, self.d)
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny-1x4x256x64", 1, 4, 256, 64, "normal_two_channels_x8", "pool"),
+    2: Workload(2, "smollm2-1.7b-2k", 24, 32, 2048, 64, "normal_outliers_x20_sink_x50", "pool"),
+    3: Workload(3, "llama3-8b-gqa-4k", 32, 8, 4096, 128, "student_t5_lognormal_channels", "pool",
+                agents=15),
+    4: Workload(4, "llama3.1-8b-cachecard-8k", 32, 8, 8192, 128, "normal", "card"),
+    5: Workload(5, "llama3-8b-long-32k", 32, 8, 32768, 128, "normal_outliers_x20", "pool"),
+}
+
+
+def rng(seed, cfg, tensor, layer):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, cfg, tensor, layer])))
+
+
+def f32_to_bf16_bits(x, out=None, chunk=1 << 20):
+    """float32 array -> bf16 bit patterns, round to nearest, ties to even.
+
+    Works in chunks with one reused scratch buffer (large fresh temporaries
+    are slow to fault in on some hosts)."""
+    x = np.ascontiguousarray(x, np.float32)
+    u = x.reshape(-1).view(np.uint32)
+    res = np.empty(x.shape, np.uint16) if out is None else out
+    r = res.reshape(-1)
+    tmp = np.empty(min(chunk, u.size), np.uint32)
+    acc = np.empty(min(chunk, u.size), np.uint32)
+    for i in range(0, u.size, chunk):
+        n = min(chunk, u.size - i)
+        a, t = acc[:n], tmp[:n]
+        np.right_shift(u[i:i + n], 16, out=t)
+        np.bitwise_and(t, 1, out=t)
+        np.add(u[i:i + n], 0x7FFF, out=a)
+        np.add(a, t, out=a)
+        np.right_shift(a, 16, out=a)
+        r[i:i + n] = a
+    return res
+
+
+def bf16_bits_to_f32(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def layer_values(recipe, seed, cfg, tensor, layer, H, T, d):
+    """float32 [H, T, d] values of one layer of one tensor."""
+    g = rng(seed, cfg, tensor, layer)
+    if recipe == "normal":
+        return g.standard_normal((H, T, d), dtype=np.float32)
+    if recipe == "normal_two_channels_x8":
+        x = g.standard_normal((H, T, d), dtype=np.float32)
+        s = rng(seed, cfg, STRUCT_TENSOR, 1000 + tensor)
+        ch = s.choice(d, size=2, replace=False)
+        x[:, :, ch] *= np.float32(8.0)
+        return x
+    if recipe in ("normal_outliers_x20", "normal_outliers_x20_sink_x50"):
+        x = g.standard_normal((H, T, d), dtype=np.float32)
+        s = rng(seed, cfg, STRUCT_TENSOR, 1000 * (tensor + 1) + layer)
+        n_out = int(round(0.02 * H * d))
+        flat = s.choice(H * d, size=n_out, replace=False)
+        x[flat // d, :, flat % d] *= np.float32(20.0)
+        if recipe.endswith("sink_x50"):
+            x[:, 0, :] *= np.float32(50.0)
+        return x
+    if recipe == "student_t5_lognormal_channels":
+        x = g.standard_t(5.0, size=(H, T, d)).astype(np.float32)
+        s = rng(seed, cfg, STRUCT_TENSOR, 1000 * (tensor + 1) + layer)
+        scale = np.exp(0.5 * s.standard_normal((H, 1, d))).astype(np.float32)
+        return x * scale
+    raise ValueError(f"unknown recipe {recipe}")
+
+
+def tensor_bits(w, seed, tensor, shape=None, layers=None, threads=8):
+    """bf16 bits [L', H, T, d] of one tensor (K or V) of a workload.
+
+    shape overrides the workload's (L, H, T, d) (same recipe, smaller size);
+    layers selects a subset of layer indices (default: all)."""
+    L, H, T, d = shape if shape is not None else w.shape
+    layers = list(range(L)) if layers is None else list(layers)
+    out = np.empty((len(layers), H, T, d), np.uint16)
+
+    def one(i):
+        f32_to_bf16_bits(layer_values(w.recipe, seed, w.cfg, tensor, layers[i], H, T, d), out=out[i])
+
+    if len(layers) > 1 and threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(len(layers))))
+    else:
+        for i in range(len(layers)):
+            one(i)
+    return out
+
+
+def kv_bits(w, seed=0, shape=None, layers=None, threads=8):
+    """(K, V) bf16 bits of a workload."""
+    return (tensor_bits(w, seed, K_TENSOR, shape, layers, threads),
+            tensor_bits(w, seed, V_TENSOR, shape, layers, threads))
+
+
+WIDTHS = np.array([2, 4, 8, 16], np.uint8)
+WIDTH_PROBS = np.array([0.4, 0.3, 0.2, 0.1])
+
+
+def card_widths(w, seed=0, T=None, mean_run=16.0):
+    """Per-token widths in {2, 4, 8, 16}: runs of geometric length (mean
+    `mean_run`), each run's width drawn with probabilities .4/.3/.2/.1."""
+    T = w.T if T is None else T
+    g = rng(seed, w.cfg, STRUCT_TENSOR, 0)
+    out = np.empty(T, np.uint8)
+    t = 0
+    while t < T:
+        n = int(g.geometric(1.0 / mean_run))
+        out[t:t + n] = g.choice(WIDTHS, p=WIDTH_PROBS)
+        t += n
+    return out

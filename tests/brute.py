@@ -1,0 +1,162 @@
+"""Brute-force references used to pin the CPU oracle (tiny inputs only).
+
+These are written from the definitions, in a different style from the oracle
+(dense matrices from scipy, nearest-level argmin in float64, exact rational
+rounding with fractions.Fraction, numpy bit twiddling), so that a plausible
+slip in the oracle (a dropped term, a transposed index, a wrong bit order)
+shows up as a disagreement.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+
+from agent_handoff_amd.synth import bf16_bits_to_f32
+
+
+def hadamard(d):
+    """Sylvester-order Hadamard matrix (entries +-1), from scipy."""
+    return scipy.linalg.hadamard(d).astype(np.float64)
+
+
+def exact_round_to_bf16(x):
+    """Nearest bf16 to the real number x (Fraction or float), ties to even,
+    by exact rational comparison of the two neighbouring bf16 values."""
+    if isinstance(x, float) and x == 0.0:
+        return 0x8000 if math.copysign(1.0, x) < 0 else 0
+    x = Fraction(x)
+    if x == 0:
+        return 0
+    sign = 0x8000 if x < 0 else 0
+    ax = abs(x)
+    # exponent of the leading bit
+    e = math.floor(math.log2(ax))
+    if Fraction(2) ** e > ax:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= ax:
+        e += 1
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 7)
+    lo = (ax // q) * q
+    hi = lo + q
+    if ax - lo < hi - ax:
+        r = lo
+    elif ax - lo > hi - ax:
+        r = hi
+    else:
+        r = lo if (lo / q) % 2 == 0 else hi
+    f = np.float32(float(r))  # exact
+    return sign | int(f.view(np.uint32) >> np.uint32(16))
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (normal range)."""
+    ax = abs(float(x))
+    if ax == 0:
+        return 2.0 ** -133
+    e = max(math.floor(math.log2(ax)), -126)
+    return 2.0 ** (e - 7)
+
+
+# ------------------------------------------------------------------ pool mode
+
+def k_codes_brute(k_bits):
+    """Per-layer int8 codes by rounding x*127/m in float64 (ties to even)."""
+    x = bf16_bits_to_f32(k_bits).astype(np.float64)
+    L = x.shape[0]
+    out = np.zeros(x.shape, np.int8)
+    near_tie = np.zeros(x.shape, bool)
+    scales = np.zeros(L)
+    for l in range(L):
+        m = np.max(np.abs(x[l]))
+        scales[l] = m / 127.0
+        if m == 0:
+            continue
+        u = x[l] * 127.0 / m
+        out[l] = np.clip(np.rint(u), -127, 127).astype(np.int8)
+        near_tie[l] = np.abs(np.abs(u - np.floor(u)) - 0.5) < 1e-5
+    return out, scales, near_tie
+
+
+def v_codes_brute(v_bits, levels, thresholds):
+    """3-bit codes of every value vector, float64 pipeline:
+    rms in float64, s = fp16(rms) via numpy, y = H x via scipy's matrix,
+    z = y / (sqrt(d) s), code = index of the nearest level.
+
+    Returns (codes, scale_bits, near): `near` marks coordinates whose z lies
+    within 1e-5 of a decision threshold, or vectors whose rms sits within
+    1e-6 (relative) of an fp16 rounding boundary."""
+    x = bf16_bits_to_f32(v_bits).astype(np.float64)
+    shp = x.shape
+    d = shp[-1]
+    xv = x.reshape(-1, d)
+    rms = np.sqrt(np.mean(xv * xv, axis=1))
+    s16 = np.minimum(rms, 65504.0).astype(np.float16)
+    s = s16.astype(np.float64)
+    y = xv @ hadamard(d).T
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.where(s[:, None] > 0, y / (math.sqrt(d) * s[:, None]), 0.0)
+    lv = np.asarray(levels, np.float64)
+    codes = np.argmin(np.abs(z[:, :, None] - lv[None, None, :]), axis=2).astype(np.uint8)
+    thr = np.asarray(thresholds, np.float64)
+    near = np.min(np.abs(z[:, :, None] - thr[None, None, :]), axis=2) < 1e-5
+    # fp16 rounding boundary of the scale: midpoint between neighbours
+    up = np.nextafter(s16, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(s16, np.float16(-np.inf)).astype(np.float64)
+    mid_hi, mid_lo = 0.5 * (s + up), 0.5 * (s + dn)
+    rel = np.minimum(np.abs(rms - mid_hi), np.abs(rms - mid_lo)) / np.maximum(rms, 1e-30)
+    near |= (rel < 1e-6)[:, None]
+    return (codes.reshape(shp), s16.view(np.uint16).reshape(shp[:-1]), near.reshape(shp))
+
+
+def v_decode_brute(codes, scale_bits, levels):
+    """float64 reconstruction (before bf16 rounding): (s/sqrt(d)) * H @ level[codes]."""
+    d = codes.shape[-1]
+    c = np.asarray(levels, np.float64)[codes.reshape(-1, d)]
+    s = np.asarray(scale_bits, np.uint16).reshape(-1).view(np.float16).astype(np.float64)
+    y = (c @ hadamard(d).T) * (s / math.sqrt(d))[:, None]
+    return y.reshape(codes.shape)
+
+
+def unpack_v_codes(section, L, H, T, d):
+    """Unpack the v_codes section from the format definition with numpy:
+    blocks of 16 tokens per (layer, head); 3 planes x d/4 u64 words; bit
+    4v+m of word [p][k] = bit p of the code of coordinate m*(d/4)+k of
+    token v of the block."""
+    nblk = (T + 15) // 16
+    slots = d // 4
+    words = np.frombuffer(section.tobytes(), dtype="<u8")[: L * H * nblk * 3 * slots]
+    words = words.reshape(L, H, nblk, 3, slots)
+    bits = (words[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
+    bits = bits.reshape(L, H, nblk, 3, slots, 16, 4)          # [.., p, k, v, m]
+    codes = (bits[:, :, :, 0] | (bits[:, :, :, 1] << np.uint64(1)) | (bits[:, :, :, 2] << np.uint64(2)))
+    codes = codes.transpose(0, 1, 2, 4, 5, 3)                 # [L, H, blk, v, m, k]
+    codes = codes.reshape(L, H, nblk * 16, d)[:, :, :T].astype(np.uint8)
+    return codes
+
+
+# ------------------------------------------------------------------ CacheCard
+
+def card_record_size(d, b):
+    if b == 16:
+        return 2 * d
+    raw = 4 * (d // 32) + d * b // 8
+    return -(-raw // 16) * 16
+
+
+def card_quant_brute(x_bits, b):
+    """One group of 32 bf16 values: (scale fp16 bits, min bf16 bits, codes)
+    following the min-max definition with numpy float32 scalars."""
+    x = bf16_bits_to_f32(x_bits)
+    mn, mx = np.float32(x.min()), np.float32(x.max())
+    mn = np.float32(mn + np.float32(0.0))
+    mx = np.float32(mx + np.float32(0.0))
+    qmax = np.float32(2 ** b - 1)
+    s = np.float32(np.float32(mx - mn) / qmax)
+    s16 = np.float16(min(s, np.float32(65504.0)))
+    sf = np.float32(s16)
+    inv = np.float32(0.0) if sf == 0 else np.float32(np.float32(1.0) / sf)
+    q = np.minimum(np.rint((x - mn) * inv), qmax).astype(np.uint8)
+    return int(s16.view(np.uint16)), int(np.float32(mn).view(np.uint32) >> np.uint32(16)), q

@@ -1,0 +1,314 @@
+"""Pins of the pool-mode oracle (oracle/kvoracle.c, PolyKV section 2.B)
+against brute force, worked examples, closed forms and the page's figures."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from agent_handoff_amd import synth
+from agent_handoff_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+from brute import (bf16_ulp, exact_round_to_bf16, hadamard, k_codes_brute, unpack_v_codes,
+                   v_codes_brute, v_decode_brute)
+from oracle import codebook
+
+LEVELS, THRESH = codebook.codec_table()
+
+
+def _bits(x):
+    return f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _sections(pool, shape):
+    L, H, T, d = shape
+    off = oracle.pool_layout(L, H, T, d)
+    k_scale = pool[off[0]:off[0] + 4 * L].view(np.float32)
+    k_codes = pool[off[1]:off[1] + L * H * T * d].view(np.int8).reshape(L, H, T, d)
+    v_scale = pool[off[2]:off[2] + 2 * L * H * T].view(np.uint16).reshape(L, H, T)
+    v_codes = pool[off[3]:off[4]]
+    return k_scale, k_codes, v_scale, v_codes
+
+
+def _random_kv(shape, seed, outliers=True):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal(shape).astype(np.float32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    if outliers:
+        k[..., 3] *= 9
+        v[..., 5] *= 17
+        v[:, :, 0, :] *= 40
+    return _bits(k), _bits(v)
+
+
+# ----------------------------------------------------------------- layout
+
+@pytest.mark.parametrize("shape", [(1, 4, 256, 64), (24, 32, 2048, 64), (32, 8, 4096, 128),
+                                   (32, 8, 32768, 128), (2, 3, 37, 128), (1, 1, 1, 64)])
+def test_pool_size_closed_form(shape):
+    L, H, T, d = shape
+    off = oracle.pool_layout(*shape)
+    n_vec = L * H * T
+    payload_k = n_vec * d                       # int8
+    payload_v = 3 * L * H * (-(-T // 16)) * 16 * d // 8
+    scales = 4 * L + 2 * n_vec
+    total = oracle.pool_bytes(*shape)
+    assert total == off[4]
+    assert all(o % 256 == 0 for o in off)
+    # sections hold exactly their payload, padding is below 256 bytes each
+    assert off[1] - off[0] >= 4 * L and off[1] - off[0] - 4 * L < 256
+    assert off[2] - off[1] >= payload_k and off[2] - off[1] - payload_k < 256
+    assert off[3] - off[2] >= 2 * n_vec and off[3] - off[2] - 2 * n_vec < 256
+    assert off[4] - off[3] >= payload_v and off[4] - off[3] - payload_v < 256
+    assert total - (payload_k + payload_v + scales) < 5 * 256
+
+
+def test_pool_ratio_matches_polykv_closed_form(golden):
+    g = golden("polykv_figures.txt")
+    ratio = g["ratio_numerator_bits"] / ((g["key_bits"] + g["value_bits"]) / 2)
+    assert round(ratio, 2) == g["ratio_printed"]
+    for L, H, T, d, with_scales in [(32, 8, 4096, 128, 2.8764), (24, 32, 2048, 64, 2.8443)]:
+        bf16 = 2 * L * H * T * d * 2
+        payload = L * H * T * d + L * H * T * d * 3 // 8
+        assert bf16 / payload == pytest.approx(16 / 5.5, rel=1e-12)
+        assert bf16 / oracle.pool_bytes(L, H, T, d) == pytest.approx(with_scales, abs=1e-3)
+
+
+def test_pool_vs_page_memory_figures(golden):
+    """PolyKV section 4: 15 agents share one pool. The printed 19.8 GB ->
+    0.45 GB is a ratio of 44.0, i.e. 15 x 2.93; our Llama-3-8B 4K pool gives
+    15 x 2.876. Only the ratio is comparable (the page gives no token count
+    or precision for the absolute sizes)."""
+    g = golden("polykv_figures.txt")
+    page_ratio = g["gb_before"] / g["gb_after"]
+    assert 1 - g["gb_after"] / g["gb_before"] == pytest.approx(g["reduction_percent"] / 100, abs=5e-4)
+    L, H, T, d = 32, 8, 4096, 128
+    ours = g["agents"] * (2 * L * H * T * d * 2) / oracle.pool_bytes(L, H, T, d)
+    assert ours == pytest.approx(page_ratio, rel=0.03)
+    # 2K-context pool of 0.116 GB: SmolLM2-1.7B shape at the 1,851-token
+    # document of section 4 gives a payload of 0.1165 GiB.
+    payload = 1851 * 24 * 32 * 64 * 2 * (5.5 / 8)
+    assert payload / 2 ** 30 == pytest.approx(g["pool_gb_2k"], abs=1e-3)
+
+
+# ----------------------------------------------------------------- K path
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_k_codes_against_brute_force(seed):
+    shape = (3, 2, 40, 64)
+    k, v = _random_kv(shape, seed)
+    pool = oracle.pool_encode(k, v)
+    k_scale, k_codes, _, _ = _sections(pool, shape)
+    ref, ref_scale, near = k_codes_brute(k)
+    assert np.all(k_codes[~near] == ref[~near])
+    assert np.mean(near) < 1e-3
+    np.testing.assert_allclose(k_scale, ref_scale, rtol=2 ** -23)
+    x = bf16_bits_to_f32(k)
+    for l in range(shape[0]):
+        # the max-abs element maps to +-127
+        i = np.unravel_index(np.argmax(np.abs(x[l])), x[l].shape)
+        assert abs(int(k_codes[l][i])) == 127
+        # reconstruction error bound |x - q s| <= s/2 (1 + 2^-20)
+        err = np.abs(x[l].astype(np.float64) - k_codes[l].astype(np.float64) * float(k_scale[l]))
+        assert np.all(err <= 0.5 * float(k_scale[l]) * (1 + 2 ** -20))
+
+
+def test_k_exact_ties_round_to_even():
+    """With absmax 127 the scale is 1: x = +-0.5, +-1.5, +-2.5 are exact ties."""
+    shape = (1, 1, 1, 64)
+    x = np.zeros(64, np.float32)
+    x[:8] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]
+    k = _bits(x).reshape(shape)
+    pool = oracle.pool_encode(k, k)
+    _, k_codes, _, _ = _sections(pool, shape)
+    assert list(k_codes.reshape(-1)[:8]) == [127, 0, 2, 2, 0, -2, -2, 4]
+
+
+def test_k_layers_are_independent():
+    shape = (4, 2, 32, 64)
+    k, v = _random_kv(shape, 9)
+    k[2] = _bits(bf16_bits_to_f32(k[2]) * 100)
+    perm = [2, 0, 3, 1]
+    p1 = oracle.pool_encode(k, v)
+    p2 = oracle.pool_encode(np.ascontiguousarray(k[perm]), np.ascontiguousarray(v[perm]))
+    s1, c1, _, _ = _sections(p1, shape)
+    s2, c2, _, _ = _sections(p2, shape)
+    np.testing.assert_array_equal(s2, s1[perm])
+    np.testing.assert_array_equal(c2, c1[perm])
+
+
+def test_k_zero_layer():
+    shape = (2, 1, 16, 64)
+    k, v = _random_kv(shape, 1)
+    k[1] = 0
+    pool = oracle.pool_encode(k, v)
+    s, c, _, _ = _sections(pool, shape)
+    assert s[1] == 0 and np.all(c[1] == 0)
+    ko, _ = oracle.pool_decode(pool, shape)
+    assert np.all(ko[1] == 0)
+
+
+def test_k_decode_is_correctly_rounded_product():
+    shape = (2, 2, 24, 64)
+    k, v = _random_kv(shape, 3)
+    pool = oracle.pool_encode(k, v)
+    s, c, _, _ = _sections(pool, shape)
+    ko, _ = oracle.pool_decode(pool, shape)
+    flat_c = c.reshape(2, -1)
+    flat_o = ko.reshape(2, -1)
+    for l in range(2):
+        for i in range(0, flat_c.shape[1], 97):
+            from fractions import Fraction
+            exact = Fraction(int(flat_c[l, i])) * Fraction(float(s[l]))
+            assert flat_o[l, i] == exact_round_to_bf16(exact)
+
+
+# ----------------------------------------------------------------- V path
+
+def test_v_one_hot_worked_example():
+    """v = a e_j: y = a H[:, j] = +-a, s = |a|/sqrt(d), z = +-1 (one rounding
+    away), so codes are 5 (+) or 2 (-) with the sign of H[i, j] =
+    (-1)^popcount(i & j); the decode is bf16(level5 * a) at j, 0 elsewhere."""
+    for d, a, j in [(64, 1.0, 5), (64, -3.0, 63), (128, 0.375, 77), (128, 2.0, 0)]:
+        v = np.zeros(d, np.float32)
+        v[j] = a
+        sh, codes = oracle.v_encode_vector(_bits(v))
+        assert np.float16(abs(a) / math.sqrt(d)) == np.uint16(sh).view(np.float16)
+        signs = np.array([(-1) ** bin(i & j).count("1") for i in range(d)]) * np.sign(a)
+        np.testing.assert_array_equal(codes, np.where(signs > 0, 5, 2))
+        out = bf16_bits_to_f32(oracle.v_decode_vector(codes, sh))
+        expect = np.zeros(d, np.float32)
+        expect[j] = bf16_bits_to_f32(np.array([exact_round_to_bf16(
+            LEVELS[5] * float(np.uint16(sh).view(np.float16)) * math.sqrt(d) * np.sign(a))], np.uint16))[0]
+        np.testing.assert_array_equal(out, expect)
+
+
+def test_v_constant_vector_worked_example():
+    """a * ones: y = (a d, 0, ..., 0), s = |a|, z_0 = +-sqrt(d) -> code 7 or 0,
+    every other z is exactly 0 -> code 4 (ties go to the upper cell)."""
+    for d, a in [(64, 1.5), (128, -0.25)]:
+        sh, codes = oracle.v_encode_vector(_bits(np.full(d, a, np.float32)))
+        assert float(np.uint16(sh).view(np.float16)) == abs(a)
+        assert codes[0] == (7 if a > 0 else 0)
+        assert np.all(codes[1:] == 4)
+
+
+def test_v_zero_vector():
+    for d in (64, 128):
+        sh, codes = oracle.v_encode_vector(np.zeros(d, np.uint16))
+        assert sh == 0 and np.all(codes == 4)
+        assert np.all(oracle.v_decode_vector(codes, sh) == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_v_codes_against_brute_force(d, seed):
+    shape = (2, 3, 33, d)
+    k, v = _random_kv(shape, seed)
+    pool = oracle.pool_encode(k, v)
+    _, _, v_scale, _ = _sections(pool, shape)
+    codes = oracle.pool_v_codes(pool, shape)
+    ref_codes, ref_scale, near = v_codes_brute(v, LEVELS, THRESH)
+    vec_near = near.any(axis=-1)
+    np.testing.assert_array_equal(v_scale[~vec_near], ref_scale[~vec_near])
+    assert np.all(codes[~near] == ref_codes[~near])
+    # whole vectors are set aside when their rms sits next to an fp16 rounding
+    # boundary (about 0.4% of vectors); single coordinates far more rarely
+    assert np.mean(near) < 0.03
+
+
+def test_v_section_layout_against_numpy_unpacker():
+    for shape in [(1, 2, 16, 64), (2, 1, 45, 128), (1, 1, 3, 64)]:
+        L, H, T, d = shape
+        k, v = _random_kv(shape, 5)
+        pool = oracle.pool_encode(k, v)
+        _, _, _, v_sec = _sections(pool, shape)
+        ref_codes, _, near = v_codes_brute(v, LEVELS, THRESH)
+        codes = unpack_v_codes(v_sec, L, H, T, d)
+        assert np.all(codes[~near] == ref_codes[~near])
+        # padding tokens of the last block carry zero bits
+        nblk = -(-T // 16)
+        words = v_sec[: L * H * nblk * 6 * d].view("<u8").reshape(L, H, nblk, 3, d // 4)
+        tail = T - (nblk - 1) * 16
+        if tail < 16:
+            mask = np.uint64(((1 << 64) - 1) ^ ((1 << (4 * tail)) - 1))
+            assert np.all(words[:, :, -1] & mask == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_decode_against_brute_force(d):
+    shape = (2, 2, 20, d)
+    k, v = _random_kv(shape, 11)
+    pool = oracle.pool_encode(k, v)
+    _, _, v_scale, _ = _sections(pool, shape)
+    codes = oracle.pool_v_codes(pool, shape)
+    _, vo = oracle.pool_decode(pool, shape)
+    y = v_decode_brute(codes, v_scale, LEVELS)
+    got = bf16_bits_to_f32(vo).astype(np.float64)
+    ulp = np.vectorize(bf16_ulp)(y)
+    assert np.all(np.abs(got - y) <= 0.5 * ulp * (1 + 1e-9))
+
+
+def test_fwht_matrix_facts():
+    for d in (64, 128):
+        Hm = hadamard(d)
+        np.testing.assert_array_equal(Hm @ Hm.T, d * np.eye(d))
+        np.testing.assert_array_equal(Hm, Hm.T)
+        x = np.random.default_rng(d).standard_normal(d)
+        y = Hm @ x / math.sqrt(d)
+        assert np.dot(y, y) == pytest.approx(np.dot(x, x), rel=1e-12)
+        np.testing.assert_allclose(Hm @ y / math.sqrt(d), x, atol=1e-12)
+
+
+def test_decode_range_and_layer_subset():
+    shape = (4, 2, 24, 64)
+    k, v = _random_kv(shape, 2)
+    pool = oracle.pool_encode(k, v)
+    ka, va = oracle.pool_decode(pool, shape)
+    kb, vb = oracle.pool_decode(pool, shape, 1, 3)
+    np.testing.assert_array_equal(kb, ka[1:3])
+    np.testing.assert_array_equal(vb, va[1:3])
+    ke, ve = oracle.pool_decode(pool, shape, 2, 2)
+    assert ke.shape[0] == 0 and ve.shape[0] == 0
+    bad = pool.copy()
+    bad[0] ^= 1
+    with pytest.raises(ValueError):
+        oracle.pool_decode(bad, shape)
+
+
+def test_v_reconstruction_mse_matches_lloyd_max_distortion():
+    """On iid N(0,1) values the rotation keeps N(0,1); the relative MSE per
+    head is the quantiser's distortion D = 0.03455 (plus the small fp16
+    scale and bf16 output rounding)."""
+    shape = (1, 4, 1024, 128)
+    rng = np.random.default_rng(0)
+    v = _bits(rng.standard_normal(shape).astype(np.float32))
+    pool = oracle.pool_encode(v, v)
+    _, vo = oracle.pool_decode(pool, shape)
+    x = bf16_bits_to_f32(v).astype(np.float64)
+    y = bf16_bits_to_f32(vo).astype(np.float64)
+    D = codebook.distortion(*codebook.lloyd_max_gaussian()[:2])
+    for h in range(4):
+        rel = np.sum((x[0, h] - y[0, h]) ** 2) / np.sum(x[0, h] ** 2)
+        assert rel == pytest.approx(D, rel=0.04)
+
+
+def test_rotation_gaussianises_heavy_tailed_vectors():
+    """PolyKV 2.B: the rotation spreads outliers so rotated coordinates are
+    close to N(0,1). Student-t(5) values (kurtosis 9) become near-Gaussian
+    (kurtosis near 3); a single x20 outlier channel is spread over all
+    coordinates (rotated kurtosis far closer to 3 than the input's)."""
+    w3 = synth.WORKLOADS[3]
+    _, v = synth.kv_bits(w3, 0, shape=(1, 8, 128, 128))
+    x = bf16_bits_to_f32(v).astype(np.float64).reshape(-1, 128)
+    rms = np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    z = (x @ hadamard(128).T) / (math.sqrt(128) * rms)
+    assert np.mean((x / rms) ** 4) > 5
+    assert abs(np.mean(z ** 4) - 3) < 0.3
+    w2 = synth.WORKLOADS[2]
+    _, v = synth.kv_bits(w2, 0, shape=(1, 32, 64, 64))
+    x = bf16_bits_to_f32(v).astype(np.float64).reshape(-1, 64)
+    rms = np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    z = (x @ hadamard(64).T) / (8.0 * rms)
+    kx, kz = np.mean((x / rms) ** 4), np.mean(z ** 4)
+    assert kx > 10 and abs(kz - 3) < abs(kx - 3) / 5
