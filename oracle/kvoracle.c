@@ -141,15 +141,13 @@ static uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 /*   k_scale  f32[L]                                                   */
 /*   k_codes  i8[L][H][T][d]                                           */
 /*   v_scale  f16[L][H][T]                                             */
-/*   v_codes  blocks of 16 tokens, see below                           */
+/*   v_codes  u8[L][H][T][3][d/8]: 3 bit planes per vector            */
 /* Sections start on 256-byte boundaries; the total is a multiple of   */
 /* 256.                                                                */
 /*                                                                     */
-/* v_codes: for every (layer, head), tokens are taken in blocks of 16  */
-/* (the last block zero-padded). A block is 3 planes x (d/4) slots of  */
-/* one little-endian u64 word, slot-major within a plane. In word      */
-/* W[p][k], bit 4*v + m holds bit p of the 3-bit code of coordinate    */
-/* m*(d/4) + k of token 16*blk + v (v < 16, m < 4).                    */
+/* v_codes: plane p of a vector holds bit p of the 3-bit code of each  */
+/* coordinate, in coordinate order, least significant bit first: bit m */
+/* of byte j of plane p belongs to coordinate 8*j + m.                 */
 /* ------------------------------------------------------------------ */
 
 #define POOL_HEADER 64u
@@ -163,12 +161,11 @@ static int shape_ok(uint32_t L, uint32_t H, uint32_t T, uint32_t d) {
 int or_pool_layout(uint32_t L, uint32_t H, uint32_t T, uint32_t d, uint64_t off[5]) {
     if (!shape_ok(L, H, T, d)) return OR_E_ARG;
     uint64_t n_vec = (uint64_t)L * H * T;
-    uint64_t n_blk = (uint64_t)L * H * ((T + 15) / 16);
     off[0] = 256;
     off[1] = round_up(off[0] + 4ull * L, 256);
     off[2] = round_up(off[1] + n_vec * d, 256);
     off[3] = round_up(off[2] + 2ull * n_vec, 256);
-    off[4] = round_up(off[3] + n_blk * 6ull * d, 256);
+    off[4] = round_up(off[3] + n_vec * 3ull * (d / 8), 256);
     return OR_OK;
 }
 
@@ -267,35 +264,20 @@ static int8_t k_quantize(float x, float inv) {
     return (int8_t)rintf(u);
 }
 
-static void v_pack_block(const uint8_t* codes /* [16][d], rows beyond nv ignored */, uint32_t nv,
-                         uint32_t d, uint8_t* blk) {
-    uint32_t slots = d / 4;
-    memset(blk, 0, 6u * d);
-    for (uint32_t v = 0; v < nv; ++v)
-        for (uint32_t i = 0; i < d; ++i) {
-            uint32_t m = i / slots, k = i % slots;
-            uint32_t bit = 4 * v + m;
-            for (uint32_t p = 0; p < 3; ++p)
-                if ((codes[v * d + i] >> p) & 1u) {
-                    uint8_t* w = blk + 8u * (p * slots + k);
-                    w[bit / 8] |= (uint8_t)(1u << (bit % 8));
-                }
-        }
+/* codes[d] -> 3 planes of d/8 bytes (coordinate i: byte i/8, bit i%8). */
+static void v_pack_planes(const uint8_t* codes, uint32_t d, uint8_t* out) {
+    memset(out, 0, 3u * (d / 8));
+    for (uint32_t i = 0; i < d; ++i)
+        for (uint32_t p = 0; p < 3; ++p)
+            if ((codes[i] >> p) & 1u) out[p * (d / 8) + i / 8] |= (uint8_t)(1u << (i % 8));
 }
 
-static void v_unpack_block(const uint8_t* blk, uint32_t nv, uint32_t d, uint8_t* codes) {
-    uint32_t slots = d / 4;
-    for (uint32_t v = 0; v < nv; ++v)
-        for (uint32_t i = 0; i < d; ++i) {
-            uint32_t m = i / slots, k = i % slots;
-            uint32_t bit = 4 * v + m;
-            uint8_t c = 0;
-            for (uint32_t p = 0; p < 3; ++p) {
-                const uint8_t* w = blk + 8u * (p * slots + k);
-                c |= (uint8_t)(((w[bit / 8] >> (bit % 8)) & 1u) << p);
-            }
-            codes[v * d + i] = c;
-        }
+static void v_unpack_planes(const uint8_t* in, uint32_t d, uint8_t* codes) {
+    for (uint32_t i = 0; i < d; ++i) {
+        uint8_t c = 0;
+        for (uint32_t p = 0; p < 3; ++p) c |= (uint8_t)(((in[p * (d / 8) + i / 8] >> (i % 8)) & 1u) << p);
+        codes[i] = c;
+    }
 }
 
 /* Encode K and V (bf16 [L][H][T][d], raw bits) into a pool (PolyKV 2.A/2.B). */
@@ -326,22 +308,14 @@ int or_pool_encode(uint32_t L, uint32_t H, uint32_t T, uint32_t d,
             kc[i] = k_quantize(or_bf16_to_f32(kl[i]), inv);
     }
 
-    uint32_t nblk = (T + 15) / 16;
-    int64_t total_blocks = (int64_t)L * H * nblk;
+    int64_t n_vec = (int64_t)L * H * T;
     #pragma omp parallel for schedule(static)
-    for (int64_t b = 0; b < total_blocks; ++b) {
-        uint64_t lh = (uint64_t)b / nblk;
-        uint32_t blk = (uint32_t)((uint64_t)b % nblk);
-        uint32_t t0 = blk * 16;
-        uint32_t nv = (T - t0 < 16) ? T - t0 : 16;
-        uint8_t codes[16 * 128];
-        for (uint32_t j = 0; j < nv; ++j) {
-            uint64_t vec = lh * T + t0 + j;
-            uint16_t sh;
-            or_v_encode_vector(v + vec * d, d, thr, &sh, codes + j * d);
-            put_u16(pool + off[2] + 2 * vec, sh);
-        }
-        v_pack_block(codes, nv, d, pool + off[3] + (uint64_t)b * 6u * d);
+    for (int64_t vec = 0; vec < n_vec; ++vec) {
+        uint8_t codes[128];
+        uint16_t sh;
+        or_v_encode_vector(v + (uint64_t)vec * d, d, thr, &sh, codes);
+        put_u16(pool + off[2] + 2 * (uint64_t)vec, sh);
+        v_pack_planes(codes, d, pool + off[3] + (uint64_t)vec * 3u * (d / 8));
     }
     return OR_OK;
 }
@@ -377,23 +351,14 @@ int or_pool_decode(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uint8_t
         for (int64_t i = 0; i < (int64_t)per_layer; ++i)
             ko[i] = or_f64_to_bf16((double)kc[i] * scale);
     }
-    uint32_t nblk = (T + 15) / 16;
-    int64_t nb = (int64_t)(l1 - l0) * H * nblk;
+    int64_t nv = (int64_t)(l1 - l0) * H * T;
     #pragma omp parallel for schedule(static)
-    for (int64_t bb = 0; bb < nb; ++bb) {
-        uint64_t b = (uint64_t)l0 * H * nblk + (uint64_t)bb;
-        uint64_t lh = b / nblk;
-        uint32_t blk = (uint32_t)(b % nblk);
-        uint32_t t0 = blk * 16;
-        uint32_t nv = (T - t0 < 16) ? T - t0 : 16;
-        uint8_t codes[16 * 128];
-        v_unpack_block(pool + off[3] + b * 6u * d, nv, d, codes);
-        for (uint32_t j = 0; j < nv; ++j) {
-            uint64_t vec = lh * T + t0 + j;
-            uint16_t sh = get_u16(pool + off[2] + 2 * vec);
-            uint64_t out_vec = vec - (uint64_t)l0 * H * T;
-            or_v_decode_vector(codes + j * d, sh, d, levels, v_out + out_vec * d);
-        }
+    for (int64_t j = 0; j < nv; ++j) {
+        uint64_t vec = (uint64_t)l0 * H * T + (uint64_t)j;
+        uint8_t codes[128];
+        v_unpack_planes(pool + off[3] + vec * 3u * (d / 8), d, codes);
+        uint16_t sh = get_u16(pool + off[2] + 2 * vec);
+        or_v_decode_vector(codes, sh, d, levels, v_out + (uint64_t)j * d);
     }
     return OR_OK;
 }
@@ -403,14 +368,9 @@ int or_pool_v_codes(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uint8_
                     uint64_t pool_bytes, uint8_t* codes_out) {
     uint64_t off[5];
     if (!pool_header_ok(pool, pool_bytes, L, H, T, d, off)) return OR_E_FORMAT;
-    uint32_t nblk = (T + 15) / 16;
-    uint64_t nb = (uint64_t)L * H * nblk;
-    for (uint64_t b = 0; b < nb; ++b) {
-        uint64_t lh = b / nblk;
-        uint32_t t0 = (uint32_t)(b % nblk) * 16;
-        uint32_t nv = (T - t0 < 16) ? T - t0 : 16;
-        v_unpack_block(pool + off[3] + b * 6u * d, nv, d, codes_out + (lh * T + t0) * d);
-    }
+    uint64_t nv = (uint64_t)L * H * T;
+    for (uint64_t vec = 0; vec < nv; ++vec)
+        v_unpack_planes(pool + off[3] + vec * 3u * (d / 8), d, codes_out + vec * d);
     return OR_OK;
 }
 

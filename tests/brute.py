@@ -122,19 +122,13 @@ def v_decode_brute(codes, scale_bits, levels):
 
 def unpack_v_codes(section, L, H, T, d):
     """Unpack the v_codes section from the format definition with numpy:
-    blocks of 16 tokens per (layer, head); 3 planes x d/4 u64 words; bit
-    4v+m of word [p][k] = bit p of the code of coordinate m*(d/4)+k of
-    token v of the block."""
-    nblk = (T + 15) // 16
-    slots = d // 4
-    words = np.frombuffer(section.tobytes(), dtype="<u8")[: L * H * nblk * 3 * slots]
-    words = words.reshape(L, H, nblk, 3, slots)
-    bits = (words[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
-    bits = bits.reshape(L, H, nblk, 3, slots, 16, 4)          # [.., p, k, v, m]
-    codes = (bits[:, :, :, 0] | (bits[:, :, :, 1] << np.uint64(1)) | (bits[:, :, :, 2] << np.uint64(2)))
-    codes = codes.transpose(0, 1, 2, 4, 5, 3)                 # [L, H, blk, v, m, k]
-    codes = codes.reshape(L, H, nblk * 16, d)[:, :, :T].astype(np.uint8)
-    return codes
+    per vector 3 planes of d/8 bytes; numpy's little-endian bit order makes
+    bit m of byte j the coordinate 8j + m."""
+    n = L * H * T * 3 * (d // 8)
+    planes = np.frombuffer(section.tobytes()[:n], np.uint8).reshape(L, H, T, 3, d // 8)
+    bits = np.unpackbits(planes, axis=-1, bitorder="little")       # [L, H, T, 3, d]
+    codes = bits[..., 0, :] | (bits[..., 1, :] << 1) | (bits[..., 2, :] << 2)
+    return codes.astype(np.uint8)
 
 
 # ------------------------------------------------------------------ CacheCard

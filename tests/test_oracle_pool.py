@@ -50,7 +50,7 @@ def test_pool_size_closed_form(shape):
     off = oracle.pool_layout(*shape)
     n_vec = L * H * T
     payload_k = n_vec * d                       # int8
-    payload_v = 3 * L * H * (-(-T // 16)) * 16 * d // 8
+    payload_v = 3 * L * H * T * d // 8
     scales = 4 * L + 2 * n_vec
     total = oracle.pool_bytes(*shape)
     assert total == off[4]
@@ -226,13 +226,9 @@ def test_v_section_layout_against_numpy_unpacker():
         ref_codes, _, near = v_codes_brute(v, LEVELS, THRESH)
         codes = unpack_v_codes(v_sec, L, H, T, d)
         assert np.all(codes[~near] == ref_codes[~near])
-        # padding tokens of the last block carry zero bits
-        nblk = -(-T // 16)
-        words = v_sec[: L * H * nblk * 6 * d].view("<u8").reshape(L, H, nblk, 3, d // 4)
-        tail = T - (nblk - 1) * 16
-        if tail < 16:
-            mask = np.uint64(((1 << 64) - 1) ^ ((1 << (4 * tail)) - 1))
-            assert np.all(words[:, :, -1] & mask == 0)
+        np.testing.assert_array_equal(codes, oracle.pool_v_codes(pool, shape))
+        # the section ends in zero padding
+        assert np.all(v_sec[L * H * T * 3 * d // 8:] == 0)
 
 
 @pytest.mark.parametrize("d", [64, 128])
