@@ -1,0 +1,402 @@
+// card_kernels.hip - CacheCard pack / unpack for gfx950.
+//
+// QKVShare (gist.science/ko/paper/2605.03884), method items 1-3: every token
+// has a bit-width in {2, 4, 8, FP16}; the CacheCard carries the quantised KV
+// groups, the widths and metadata; the receiver rebuilds full-width
+// past_key_values. Groups here are 32 consecutive channels quantised with
+// min-max (asymmetric) steps; width 16 keeps the bf16 input.
+//
+// Offsets. Records are variable-sized, so token t's record starts at the sum
+// of the record sizes of tokens 0..t-1 (the same in every stream, since the
+// width is per token). A single-workgroup scan kernel computes these offsets
+// once into the workspace (and, for pack, writes the header and widths);
+// the pack / unpack kernels then place one record per (layer, K/V, head,
+// token).
+//
+// Work mapping: one lane per 32-channel group (d/32 lanes per token, so 16
+// tokens per wave at d = 128); a lane loads its 64 input bytes, finds the
+// group's min and max in registers, and writes its scale, minimum and codes.
+// All lanes of a token share its width, so a wave branches once per distinct
+// width it holds (widths come in runs).
+#include "kernels_common.h"
+#include "launch.h"
+#include "layout.h"
+
+namespace kvc {
+namespace {
+
+constexpr uint32_t kFlagBadHeader = 1, kFlagBadWidth = 2, kFlagCapacity = 4;
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 8;
+
+struct ScanParams {
+    const uint8_t* widths;     // pack: input widths; unpack: card + 256
+    uint8_t* card_out;         // pack: card to receive header and widths; unpack: null
+    const uint8_t* card_in;    // unpack: card whose header is checked; pack: null
+    uint64_t* info;            // ws: S, total, flags
+    uint64_t* off;             // ws: record offsets [T + 1]
+    uint64_t limit;            // pack: capacity; unpack: card bytes
+    uint64_t* dev_card_bytes;  // pack, nullable
+    int32_t* status;           // nullable
+    uint32_t L, H, T, d;
+    CardMetaDev meta;
+};
+
+struct CardParams {
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* k_out;
+    uint16_t* v_out;
+    const uint8_t* widths;  // device widths (pack input or card + 256)
+    uint8_t* card;          // pack: output card
+    const uint8_t* card_in; // unpack: input card
+    const uint64_t* info;
+    const uint64_t* off;
+    uint32_t L, H, T, nbk;  // nbk = token blocks per stream
+    uint64_t payload;
+    uint64_t n_waves;
+};
+
+__global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
+    __shared__ uint64_t sums[kScanThreads];
+    __shared__ uint32_t bad;
+    __shared__ uint32_t flags_sh;
+    const uint32_t tid = threadIdx.x;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < p.T; base += (uint64_t)kScanThreads * kScanItems) {
+        const uint64_t t0 = base + (uint64_t)tid * kScanItems;
+        uint32_t rs[kScanItems];
+        uint32_t local = 0;
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            uint32_t r = 0;
+            if (t0 + i < p.T) {
+                r = card_record_bytes(p.d, p.widths[t0 + i]);
+                if (r == 0) bad = 1;
+            }
+            rs[i] = r;
+            local += r;
+        }
+        sums[tid] = local;
+        __syncthreads();
+        // Hillis-Steele inclusive scan of the per-thread totals
+        for (int o = 1; o < kScanThreads; o <<= 1) {
+            const uint64_t add = tid >= (uint32_t)o ? sums[tid - o] : 0;
+            __syncthreads();
+            sums[tid] += add;
+            __syncthreads();
+        }
+        uint64_t run = carry + sums[tid] - local;  // exclusive prefix of this thread
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            if (t0 + i < p.T) p.off[t0 + i] = run;
+            run += rs[i];
+        }
+        carry += sums[kScanThreads - 1];
+        __syncthreads();
+    }
+    const uint64_t S = align_up(carry, 256);
+    const uint64_t payload = card_payload_offset(p.T);
+    const uint64_t total = payload + 2ull * p.L * p.H * S;
+    if (tid == 0) {
+        uint32_t flags = bad ? kFlagBadWidth : 0u;
+        p.off[p.T] = carry;
+        if (p.card_out) {
+            if (total > p.limit) flags |= kFlagCapacity;
+            if (p.dev_card_bytes) *p.dev_card_bytes = total;
+        } else {
+            const uint32_t* h = reinterpret_cast<const uint32_t*>(p.card_in);
+            const uint64_t* h64 = reinterpret_cast<const uint64_t*>(p.card_in);
+            const bool ok = h[0] == kCardMagic && h[1] == (1u | (2u << 16)) && h[2] == p.L && h[3] == p.H &&
+                            h[4] == p.T && h[5] == p.d && h[6] == kCardGroup && h64[5] == kCardHeaderBytes &&
+                            h64[6] == payload && h64[7] == S && h64[8] == total && total <= p.limit;
+            if (!ok) flags |= kFlagBadHeader;
+        }
+        p.info[0] = S;
+        p.info[1] = total;
+        p.info[2] = flags;
+        if (flags && p.status) atomicOr(p.status, (int)flags);
+        flags_sh = flags;
+    }
+    __syncthreads();
+    if (!p.card_out || flags_sh) return;
+    // header (256 B) + widths + zero padding up to the payload
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(p.card_out);
+    if (tid < 64) {
+        uint32_t val = 0;
+        switch (tid) {
+            case 0: val = kCardMagic; break;
+            case 1: val = 1u | (2u << 16); break;  // version 1, kind 2
+            case 2: val = p.L; break;
+            case 3: val = p.H; break;
+            case 4: val = p.T; break;
+            case 5: val = p.d; break;
+            case 6: val = kCardGroup; break;
+            case 8: val = (uint32_t)(uint64_t)p.meta.position_offset; break;
+            case 9: val = (uint32_t)((uint64_t)p.meta.position_offset >> 32); break;
+            case 10: val = kCardHeaderBytes; break;
+            case 12: val = (uint32_t)payload; break;
+            case 13: val = (uint32_t)(payload >> 32); break;
+            case 14: val = (uint32_t)S; break;
+            case 15: val = (uint32_t)(S >> 32); break;
+            case 16: val = (uint32_t)total; break;
+            case 17: val = (uint32_t)(total >> 32); break;
+            default:
+                if (tid >= 18 && tid < 34) {
+                    const int c = (int)(tid - 18) * 4;
+                    val = (uint32_t)(uint8_t)p.meta.model_id[c] | ((uint32_t)(uint8_t)p.meta.model_id[c + 1] << 8) |
+                          ((uint32_t)(uint8_t)p.meta.model_id[c + 2] << 16) |
+                          ((uint32_t)(uint8_t)p.meta.model_id[c + 3] << 24);
+                }
+        }
+        hdr[tid] = val;
+    }
+    for (uint64_t i = tid; i < payload - kCardHeaderBytes; i += kScanThreads)
+        p.card_out[kCardHeaderBytes + i] = i < p.T ? p.widths[i] : 0;
+}
+
+// One 32-channel group at width b (2, 4 or 8): returns the packed codes in
+// out[0 .. b-1] (b dwords = 32 codes of b bits, least significant first).
+template <int B>
+__device__ __forceinline__ void quant_group(const float (&x)[32], uint16_t& sbits, uint16_t& mbits,
+                                            uint32_t (&out)[8]) {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        mn = __builtin_fminf(mn, x[j]);
+        mx = __builtin_fmaxf(mx, x[j]);
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    constexpr float qmax = (float)((1 << B) - 1);
+    const float s = (mx - mn) / qmax;
+    const _Float16 s16 = (_Float16)__builtin_fminf(s, 65504.0f);
+    const float sf = (float)s16;
+    const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+    constexpr int PER = 32 / B;  // codes per dword
+#pragma unroll
+    for (int w = 0; w < B; ++w) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const float u = __builtin_rintf((x[w * PER + j] - mn) * inv);
+            const uint32_t q = (uint32_t)__builtin_fminf(u, qmax);
+            acc |= q << (B * j);
+        }
+        out[w] = acc;
+    }
+    sbits = __builtin_bit_cast(uint16_t, s16);
+    mbits = (uint16_t)(__float_as_uint(mn) >> 16);
+}
+
+template <int B>
+__device__ __forceinline__ void store_group(uint8_t* rec, uint32_t G, uint32_t g, uint16_t sb, uint16_t mb,
+                                            const uint32_t (&codes)[8]) {
+    reinterpret_cast<uint16_t*>(rec)[g] = sb;
+    reinterpret_cast<uint16_t*>(rec)[G + g] = mb;
+    // codes start 8-byte aligned (4*G is a multiple of 8, records 16-aligned)
+    uint2* dst = reinterpret_cast<uint2*>(rec + 4 * G + g * 4 * B);
+#pragma unroll
+    for (int i = 0; i < B / 2; ++i) dst[i] = make_uint2(codes[2 * i], codes[2 * i + 1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) {
+    constexpr uint32_t G = D / kCardGroup;  // lanes per token
+    constexpr uint32_t TPW = kWave / G;     // tokens per wave
+    const uint32_t lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    if (wave >= p.n_waves) return;
+    if (p.info[2] != 0) return;
+    const uint64_t S = p.info[0];
+    const uint64_t s = wave / p.nbk;
+    const uint32_t b = (uint32_t)(wave % p.nbk);
+    const uint32_t tok = b * TPW + lane / G;
+    const uint32_t g = lane % G;
+    if (tok >= p.T) return;
+    const uint32_t h = (uint32_t)(s % p.H);
+    const uint32_t kv = (uint32_t)((s / p.H) & 1);
+    const uint32_t l = (uint32_t)(s / (2ull * p.H));
+    const uint16_t* src = (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
+    const uint32_t width = p.widths[tok];
+    uint8_t* stream = p.card + p.payload + s * S;
+    uint8_t* rec = stream + p.off[tok];
+
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+    if (width == 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rec + 64 * g)[i] = raw[i];
+    } else {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+        float x[32];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            x[2 * j] = bf16_lo(w[j]);
+            x[2 * j + 1] = bf16_hi(w[j]);
+        }
+        uint16_t sb, mb;
+        uint32_t codes[8];
+        if (width == 2) {
+            quant_group<2>(x, sb, mb, codes);
+            store_group<2>(rec, G, g, sb, mb, codes);
+        } else if (width == 4) {
+            quant_group<4>(x, sb, mb, codes);
+            store_group<4>(rec, G, g, sb, mb, codes);
+        } else {
+            quant_group<8>(x, sb, mb, codes);
+            store_group<8>(rec, G, g, sb, mb, codes);
+        }
+        // zero the record's tail padding (present for d = 64)
+        const uint32_t used = 4 * G + D * width / 8;
+        const uint32_t R = card_record_bytes(D, width);
+        if (g == 0)
+            for (uint32_t i = used; i < R; i += 8) *reinterpret_cast<uint2*>(rec + i) = make_uint2(0, 0);
+    }
+    // zero the stream's tail padding after the last record
+    if (tok == p.T - 1 && g == 0)
+        for (uint64_t i = p.off[p.T]; i < S; i += 16) *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
+}
+
+template <int B>
+__device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t (&o)[16]) {
+    const float sf = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(rec)[g]);
+    const float mn = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rec)[G + g] << 16);
+    const uint2* src = reinterpret_cast<const uint2*>(rec + 4 * G + g * 4 * B);
+    uint32_t codes[B];
+#pragma unroll
+    for (int i = 0; i < B / 2; ++i) {
+        const uint2 c = src[i];
+        codes[2 * i] = c.x;
+        codes[2 * i + 1] = c.y;
+    }
+    constexpr int PER = 32 / B;
+    constexpr uint32_t MASK = (1u << B) - 1u;
+    float y[32];
+#pragma unroll
+    for (int w = 0; w < B; ++w)
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            y[w * PER + j] = __builtin_fmaf((float)((codes[w] >> (B * j)) & MASK), sf, mn);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[j] = pack_bf16x2(y[2 * j], y[2 * j + 1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p) {
+    constexpr uint32_t G = D / kCardGroup;
+    constexpr uint32_t TPW = kWave / G;
+    const uint32_t lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    if (wave >= p.n_waves) return;
+    if (p.info[2] != 0) return;
+    const uint64_t S = p.info[0];
+    const uint64_t s = wave / p.nbk;
+    const uint32_t b = (uint32_t)(wave % p.nbk);
+    const uint32_t tok = b * TPW + lane / G;
+    const uint32_t g = lane % G;
+    if (tok >= p.T) return;
+    const uint32_t h = (uint32_t)(s % p.H);
+    const uint32_t kv = (uint32_t)((s / p.H) & 1);
+    const uint32_t l = (uint32_t)(s / (2ull * p.H));
+    uint16_t* dst = (kv ? p.v_out : p.k_out) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
+    const uint32_t width = p.widths[tok];
+    const uint8_t* rec = p.card_in + p.payload + s * S + p.off[tok];
+    uint32_t o[16];
+    if (width == 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
+    } else if (width == 2) {
+        dequant_group<2>(rec, G, g, o);
+    } else if (width == 4) {
+        dequant_group<4>(rec, G, g, o);
+    } else {
+        dequant_group<8>(rec, G, g, o);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+}  // namespace
+
+static CardParams card_params(const Shape& s, const void* ws) {
+    CardParams p{};
+    constexpr uint32_t kTPW128 = kWave / (128 / kCardGroup), kTPW64 = kWave / (64 / kCardGroup);
+    const uint32_t tpw = s.d == 128 ? kTPW128 : kTPW64;
+    p.L = s.L;
+    p.H = s.H;
+    p.T = s.T;
+    p.nbk = (s.T + tpw - 1) / tpw;
+    p.payload = card_payload_offset(s.T);
+    p.n_waves = 2ull * s.L * s.H * p.nbk;
+    p.info = static_cast<const uint64_t*>(ws);
+    p.off = reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(ws) + kCardInfoBytes);
+    return p;
+}
+
+hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const uint8_t* widths,
+                            const CardMetaDev& meta, void* card, uint64_t capacity,
+                            uint64_t* dev_card_bytes, int32_t* dev_status, void* ws,
+                            hipStream_t stream) {
+    ScanParams sp{};
+    sp.widths = widths;
+    sp.card_out = static_cast<uint8_t*>(card);
+    sp.card_in = nullptr;
+    sp.info = static_cast<uint64_t*>(ws);
+    sp.off = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + kCardInfoBytes);
+    sp.limit = capacity;
+    sp.dev_card_bytes = dev_card_bytes;
+    sp.status = dev_status;
+    sp.L = s.L;
+    sp.H = s.H;
+    sp.T = s.T;
+    sp.d = s.d;
+    sp.meta = meta;
+    hipLaunchKernelGGL(card_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sp);
+    CardParams p = card_params(s, ws);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.widths = widths;
+    p.card = static_cast<uint8_t*>(card);
+    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    if (s.d == 64)
+        hipLaunchKernelGGL(card_pack_kernel<64>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(card_pack_kernel<128>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_bytes, void* k_out,
+                              void* v_out, int32_t* dev_status, void* ws, hipStream_t stream) {
+    ScanParams sp{};
+    sp.widths = static_cast<const uint8_t*>(card) + kCardHeaderBytes;
+    sp.card_out = nullptr;
+    sp.card_in = static_cast<const uint8_t*>(card);
+    sp.info = static_cast<uint64_t*>(ws);
+    sp.off = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + kCardInfoBytes);
+    sp.limit = card_bytes;
+    sp.dev_card_bytes = nullptr;
+    sp.status = dev_status;
+    sp.L = s.L;
+    sp.H = s.H;
+    sp.T = s.T;
+    sp.d = s.d;
+    hipLaunchKernelGGL(card_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sp);
+    CardParams p = card_params(s, ws);
+    p.k_out = static_cast<uint16_t*>(k_out);
+    p.v_out = static_cast<uint16_t*>(v_out);
+    p.widths = sp.widths;
+    p.card_in = static_cast<const uint8_t*>(card);
+    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    if (s.d == 64)
+        hipLaunchKernelGGL(card_unpack_kernel<64>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(card_unpack_kernel<128>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,76 @@
+// kernels_common.h - device helpers shared by the pool and CacheCard kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// Wave64: lanes 4t..4t+3 handle one head vector (token t of a 16-token
+// block); quad-local exchanges use DPP quad permutes.
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;  // 4 waves per workgroup
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// DPP quad_perm selectors: xor-1 = [1,0,3,2], xor-2 = [2,3,0,1]
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t dpp_xor1_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t dpp_xor2_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Per-lane select from a wave-uniform 64-bit lane mask: bit `lane` of mask
+// set -> b, clear -> a.
+__device__ __forceinline__ float select_by_mask(uint64_t mask, float a, float b) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+    return r;
+}
+// bit set -> +m, clear -> -m
+__device__ __forceinline__ float signed_by_mask(uint64_t mask, float m) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, -%1, %1, %2" : "=v"(r) : "v"(m), "s"(mask));
+    return r;
+}
+
+// acc * 2 + (bit `lane` of mask): appends one code bit per lane (the mask is
+// a wave-wide compare result) in a single add-with-carry.
+__device__ __forceinline__ uint32_t shift_in_bit(uint32_t acc, uint64_t mask) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(mask));
+    return r;
+}
+
+// w * 2, returning the lanes' former top bits as a wave mask (carry out).
+__device__ __forceinline__ uint64_t shift_out_bit(uint32_t& w) {
+    uint32_t r;
+    uint64_t mask;
+    asm("v_add_co_u32_e64 %0, %1, %2, %2" : "=v"(r), "=s"(mask) : "v"(w));
+    w = r;
+    return mask;
+}
+
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace kvc

@@ -1,0 +1,40 @@
+// launch.h - internal launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+struct Shape {
+    uint32_t L, H, T, d;
+};
+
+constexpr int kMaxAgents = 64;
+
+// Pool encode: ws holds L u32 per-layer absmax words (bf16 magnitude bits).
+hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
+                              hipStream_t stream);
+
+hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,
+                              void* const* k_out, void* const* v_out, uint32_t n_out,
+                              int32_t* dev_status, hipStream_t stream);
+
+// CacheCard workspace: 256-byte info block {u64 S, u64 total, u32 flags},
+// then u64 record offsets[T + 1].
+constexpr uint64_t kCardInfoBytes = 256;
+
+struct CardMetaDev {
+    char model_id[64];
+    int64_t position_offset;
+};
+
+hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const uint8_t* widths,
+                            const CardMetaDev& meta, void* card, uint64_t capacity,
+                            uint64_t* dev_card_bytes, int32_t* dev_status, void* ws,
+                            hipStream_t stream);
+
+hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_bytes, void* k_out,
+                              void* v_out, int32_t* dev_status, void* ws, hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,467 @@
+// pool_kernels.hip - shared-pool encode and decode for gfx950.
+//
+// PolyKV (gist.science/ko/paper/2604.24971) section 2.A: one compressed pool
+// is written once and read by every agent; section 2.B item 1: int8 keys with
+// one scale per tensor (per layer); section 2.B item 2: values rotated by the
+// fast Walsh-Hadamard transform and mapped to 3-bit Lloyd-Max levels of
+// N(0,1), decoded by level lookup and the inverse transform.
+//
+// Work mapping. One wave64 handles one 16-token block of one (layer, head):
+// lane 4t+m holds channels [m*d/4, (m+1)*d/4) of token t, i.e. 32 consecutive
+// bf16 (64 bytes) for d = 128 and 16 (32 bytes) for d = 64. So
+//  - HBM traffic is contiguous per wave (4 KiB of K and of V for d = 128);
+//  - the first log2(d/4) butterfly stages and the first levels of the
+//    pairwise sum of squares run inside a lane, the last two across the quad
+//    through DPP quad permutes (no LDS);
+//  - each code bit is one wave-wide compare; a lane appends its bit to a
+//    per-plane word with one add-with-carry, so a lane ends with the three
+//    bit planes of its d/4 coordinates, already in the pool's layout
+//    (plane p: bit i <-> coordinate i, least significant bit first).
+//
+// Numerics. Every float step follows the codec definition operation by
+// operation (binary32, round to nearest even, no contraction - the library is
+// built with -ffp-contract=off): the butterfly runs its stages in ascending
+// order, the sum of squares is the pairwise tree over natural index order,
+// and a cross-lane butterfly step computes fma(own, +-1, partner), which is
+// exactly partner + own or partner - own. Hence codes and scales are
+// bit-identical to a scalar implementation of the same definition. Decoding
+// runs the butterfly on the stored levels, which sit on a 2^-15 grid: every
+// partial sum is a multiple of 2^-15 below 2^9 and is exact in binary32, so
+// the only roundings are the final product with s/sqrt(d) and the bf16
+// conversion.
+#include "codebook.h"
+#include "kernels_common.h"
+#include "launch.h"
+#include "layout.h"
+
+#include <utility>
+
+namespace kvc {
+namespace {
+
+// 1/sqrt(d) rounded to binary32
+template <int D>
+__device__ constexpr float inv_sqrt_d() {
+    return D == 64 ? 0.125f : 0x1.6a09e6p-4f;
+}
+
+struct EncodeParams {
+    const uint16_t* k;
+    const uint16_t* v;
+    uint8_t* pool;
+    const uint32_t* absmax;  // per layer: max |K| as bf16 magnitude bits
+    uint32_t L, H, T, nb;    // nb = 16-token blocks per head
+    uint64_t n_waves;        // L * H * nb
+    PoolLayout lay;
+};
+
+struct DecodeParams {
+    const uint8_t* pool;
+    int32_t* status;
+    uint32_t L, H, T, nb;
+    uint32_t l0, n_out;
+    uint64_t n_waves;  // (l1 - l0) * H * nb
+    PoolLayout lay;
+    uint16_t* k_out[kMaxAgents];
+    uint16_t* v_out[kMaxAgents];
+};
+
+// ---------------------------------------------------------------- helpers
+
+// Unnormalised Walsh-Hadamard transform of d = 4*C values spread over the
+// quad (C per lane, lane m holds block m): stages h = 1 .. C/2 in the lane,
+// then h = C (partner lane m^1) and h = 2C (partner lane m^2).
+template <int C>
+__device__ __forceinline__ void fwht_quad(float (&y)[C], uint32_t m) {
+#pragma unroll
+    for (int h = 1; h < C; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < C; i += 2 * h) {
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                const float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+        }
+    }
+    // lower partner: own + partner; upper partner: partner - own
+    const float s1 = (m & 1u) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) y[j] = __builtin_fmaf(y[j], s1, dpp_xor1(y[j]));
+    const float s2 = (m & 2u) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) y[j] = __builtin_fmaf(y[j], s2, dpp_xor2(y[j]));
+}
+
+// Header (64 B) and every padding byte of the pool; run by workgroup 0.
+__device__ void pool_header_and_padding(const EncodeParams& p, uint32_t d, uint32_t tid) {
+    uint8_t* pool = p.pool;
+    const PoolLayout& lay = p.lay;
+    if (tid < 16) {
+        const uint64_t offs[5] = {lay.k_scale, lay.k_codes, lay.v_scale, lay.v_codes, lay.total};
+        uint32_t val;
+        switch (tid) {
+            case 0: val = kPoolMagic; break;
+            case 1: val = 1u | (1u << 16); break;  // version 1, kind 1
+            case 2: val = p.L; break;
+            case 3: val = p.H; break;
+            case 4: val = p.T; break;
+            case 5: val = d; break;
+            default: {
+                const uint64_t o = offs[(tid - 6) / 2];
+                val = (tid & 1) ? (uint32_t)(o >> 32) : (uint32_t)o;
+            }
+        }
+        reinterpret_cast<uint32_t*>(pool)[tid] = val;
+    }
+    const uint64_t vecs = (uint64_t)p.L * p.H * p.T;
+    const uint64_t ends[5] = {kPoolHeaderBytes, lay.k_scale + 4ull * p.L, lay.k_codes + vecs * d,
+                              lay.v_scale + 2ull * vecs,
+                              lay.v_codes + vecs * pool_code_bytes(d)};
+    const uint64_t starts[5] = {lay.k_scale, lay.k_codes, lay.v_scale, lay.v_codes, lay.total};
+#pragma unroll
+    for (int r = 0; r < 5; ++r)
+        for (uint64_t i = ends[r] + tid; i < starts[r]; i += kBlockThreads) pool[i] = 0;
+}
+
+// ---------------------------------------------------------------- kernels
+
+__global__ void fill_zero_kernel(uint32_t* p, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// Per-layer max |K| (PolyKV 2.B item 1: one linear scale per tensor). For
+// bf16, |x| ordering equals integer ordering of the bits with the sign
+// cleared, so the maximum is taken on 16-bit integers (packed max, two
+// values per instruction).
+__global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* __restrict__ k,
+                                                                  uint64_t per_layer_u4,
+                                                                  uint32_t* __restrict__ absmax) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const uint32_t l = blockIdx.y;
+    const uint4* src = k + (uint64_t)l * per_layer_u4;
+    us2 mx = {0, 0};
+    const uint64_t stride = (uint64_t)gridDim.x * kBlockThreads;
+    uint64_t i = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+    for (; i + 3 * stride < per_layer_u4; i += 4 * stride) {
+        uint4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].x & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].y & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].z & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].w & 0x7FFF7FFFu));
+        }
+    }
+    for (; i < per_layer_u4; i += stride) {
+        const uint4 w = src[i];
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.x & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.y & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.z & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.w & 0x7FFF7FFFu));
+    }
+    uint32_t r = mx.x > mx.y ? mx.x : mx.y;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
+        r = t > r ? t : r;
+    }
+    __shared__ uint32_t red[kBlockThreads / kWave];
+    if (lane_id() == 0) red[threadIdx.x / kWave] = r;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kBlockThreads / kWave; ++w) r = red[w] > r ? red[w] : r;
+        atomicMax(absmax + l, r);
+    }
+}
+
+// Coordinate I of the lane: code = number of thresholds <= z, found bit by
+// bit (binary search over the 7 sorted thresholds); each bit is appended to
+// its plane word. Slots run from the last coordinate down so that
+// coordinate i lands in bit i.
+template <int C, int I>
+__device__ __forceinline__ void code_slot(const float (&y)[C], float r, uint32_t (&pl)[3]) {
+    const float z = y[I] * r;
+    const bool b2 = z >= 0.0f;
+    const float t1 = b2 ? kTh6 : -kTh6;
+    const bool b1 = z >= t1;
+    const float a0 = (b1 == b2) ? kTh7 : kTh5;
+    const float t0 = b2 ? a0 : -a0;
+    pl[0] = shift_in_bit(pl[0], __builtin_amdgcn_ballot_w64(z >= t0));
+    pl[1] = shift_in_bit(pl[1], __builtin_amdgcn_ballot_w64(b1));
+    pl[2] = shift_in_bit(pl[2], __builtin_amdgcn_ballot_w64(b2));
+}
+
+template <int C, int... Is>
+__device__ __forceinline__ void code_all(const float (&y)[C], float r, uint32_t (&pl)[3],
+                                         std::integer_sequence<int, Is...>) {
+    (code_slot<C, C - 1 - Is>(y, r, pl), ...);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams p) {
+    constexpr int C = D / 4;  // channels per lane
+    const uint32_t lane = lane_id();
+    if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    if (wave >= p.n_waves) return;
+
+    const uint32_t blk = (uint32_t)(wave % p.nb);
+    const uint64_t lh = wave / p.nb;
+    const uint32_t l = (uint32_t)(lh / p.H);
+    const uint32_t h = (uint32_t)(lh % p.H);
+    const uint32_t tok = blk * kBlockTokens + (lane >> 2);
+    const uint32_t m = lane & 3u;
+    const bool valid = tok < p.T;
+    const uint64_t vec = lh * p.T + tok;
+    const uint64_t elem = vec * D + (uint64_t)m * C;
+
+    // ---- keys: q = rint(x * (127 / m_l)); |x * inv| <= 127 (1 + 2^-23) so
+    // the result never leaves [-127, 127]. Rounding uses x + 1.5*2^23, whose
+    // low byte is the two's-complement integer (ties to even).
+    const float mk = __uint_as_float(p.absmax[l] << 16);
+    const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
+    if (valid) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.k + elem);
+        uint4 raw[C / 8];
+#pragma unroll
+        for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+        uint32_t out[C / 4];
+#pragma unroll
+        for (int j = 0; j < C / 4; ++j) {
+            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+            const float q0 = bf16_lo(w0) * inv + 12582912.0f;
+            const float q1 = bf16_hi(w0) * inv + 12582912.0f;
+            const float q2 = bf16_lo(w1) * inv + 12582912.0f;
+            const float q3 = bf16_hi(w1) * inv + 12582912.0f;
+            const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
+            const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
+            out[j] = ab | cd;
+        }
+        uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + elem);
+#pragma unroll
+        for (int i = 0; i < C / 16; ++i)
+            dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    }
+    if (h == 0 && blk == 0 && lane == 0)
+        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
+
+    // ---- values
+    float y[C];
+    if (valid) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.v + elem);
+        uint4 raw[C / 8];
+#pragma unroll
+        for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+#pragma unroll
+        for (int j = 0; j < C / 2; ++j) {
+            y[2 * j] = bf16_lo(w[j]);
+            y[2 * j + 1] = bf16_hi(w[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < C; ++j) y[j] = 0.0f;
+    }
+    // sum of squares: pairwise tree, left to right, lanes in block order
+    float sq[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) sq[j] = y[j] * y[j];
+#pragma unroll
+    for (int w = C / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int j = 0; j < w; ++j) sq[j] = sq[2 * j] + sq[2 * j + 1];
+    float ss = sq[0];
+    ss = ss + dpp_xor1(ss);
+    ss = ss + dpp_xor2(ss);
+    const float rms = __builtin_sqrtf(ss * (1.0f / D));
+    const _Float16 sh = (_Float16)__builtin_fminf(rms, 65504.0f);
+    const float sc = (float)sh;
+    const float r = (sc == 0.0f) ? 0.0f : inv_sqrt_d<D>() / sc;
+    if (valid && m == 0)
+        reinterpret_cast<uint16_t*>(p.pool + p.lay.v_scale)[vec] = __builtin_bit_cast(uint16_t, sh);
+
+    fwht_quad<C>(y, m);
+
+    uint32_t pl[3] = {0, 0, 0};
+    code_all<C>(y, r, pl, std::make_integer_sequence<int, C>{});
+    uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
+    if (D == 128) {
+        // lane m owns bytes [4m, 4m+4) of each 16-byte plane
+        if (valid)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) reinterpret_cast<uint32_t*>(codes + 16 * q)[m] = pl[q];
+    } else {
+        // 16 bits per lane: lanes m and m+1 share one dword of each 8-byte plane
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const uint32_t word = pl[q] | (dpp_xor1_u(pl[q]) << 16);
+            if (valid && (m & 1u) == 0) reinterpret_cast<uint32_t*>(codes + 8 * q)[m >> 1] = word;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams p) {
+    constexpr int C = D / 4;
+    const uint32_t lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    if (wave >= p.n_waves) return;
+
+    const uint32_t* hd = reinterpret_cast<const uint32_t*>(p.pool);
+    const uint64_t total = (uint64_t)hd[14] | ((uint64_t)hd[15] << 32);
+    const bool ok = hd[0] == kPoolMagic && hd[1] == (1u | (1u << 16)) && hd[2] == p.L && hd[3] == p.H &&
+                    hd[4] == p.T && hd[5] == (uint32_t)D && total == p.lay.total;
+    if (!ok) {
+        if (lane == 0 && p.status) atomicOr(p.status, 1 /* KVC_DEV_BAD_HEADER */);
+        return;
+    }
+
+    const uint32_t blk = (uint32_t)(wave % p.nb);
+    const uint64_t lh_rel = wave / p.nb;
+    const uint64_t lh = (uint64_t)p.l0 * p.H + lh_rel;
+    const uint32_t l = (uint32_t)(lh / p.H);
+    const uint32_t tok = blk * kBlockTokens + (lane >> 2);
+    const uint32_t m = lane & 3u;
+    const bool valid = tok < p.T;
+    const uint64_t vec = lh * p.T + tok;
+    const uint64_t elem = vec * D + (uint64_t)m * C;
+    const uint64_t out_elem = (lh_rel * p.T + tok) * D + (uint64_t)m * C;
+
+    // ---- keys: bf16(q * scale)
+    const float ks = reinterpret_cast<const float*>(p.pool + p.lay.k_scale)[l];
+    if (valid) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.pool + p.lay.k_codes + elem);
+        uint4 raw[C / 16];
+#pragma unroll
+        for (int i = 0; i < C / 16; ++i) raw[i] = src[i];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+        uint32_t o[C / 2];
+#pragma unroll
+        for (int j = 0; j < C / 4; ++j) {
+            const uint32_t q = w[j];
+            const float f0 = (float)(int32_t)(int8_t)(q & 0xFF) * ks;
+            const float f1 = (float)(int32_t)(int8_t)((q >> 8) & 0xFF) * ks;
+            const float f2 = (float)(int32_t)(int8_t)((q >> 16) & 0xFF) * ks;
+            const float f3 = (float)(int32_t)(int8_t)(q >> 24) * ks;
+            o[2 * j] = pack_bf16x2(f0, f1);
+            o[2 * j + 1] = pack_bf16x2(f2, f3);
+        }
+        for (uint32_t a = 0; a < p.n_out; ++a) {
+            uint4* dst = reinterpret_cast<uint4*>(p.k_out[a] + out_elem);
+#pragma unroll
+            for (int i = 0; i < C / 8; ++i)
+                dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        }
+    }
+
+    // ---- values: level lookup by the code bits of this lane, then the
+    // butterfly, then * (s / sqrt(d)).
+    float c0 = kLv0, c1 = kLv1, c2 = kLv2, c3 = kLv3;
+    asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+    uint32_t pw[3] = {0, 0, 0};
+    if (valid) {
+        const uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
+        if (D == 128) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) pw[q] = reinterpret_cast<const uint32_t*>(codes + 16 * q)[m];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(codes + 8 * q)[m >> 1];
+                pw[q] = (m & 1u) ? (w & 0xFFFF0000u) : (w << 16);  // this lane's 16 bits on top
+            }
+        }
+    }
+    float y[C];
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const uint64_t w0 = shift_out_bit(pw[0]);
+        const uint64_t w1 = shift_out_bit(pw[1]);
+        const uint64_t w2 = shift_out_bit(pw[2]);
+        // level index within the half: (b1, b0) for b2 = 1, complemented for b2 = 0
+        const uint64_t m1 = ~(w1 ^ w2), m0 = ~(w0 ^ w2);
+        const float lo = select_by_mask(m0, c0, c1);
+        const float hi = select_by_mask(m0, c2, c3);
+        const float mag = select_by_mask(m1, lo, hi);
+        y[i] = signed_by_mask(w2, mag);
+    }
+    fwht_quad<C>(y, m);
+    if (valid) {
+        const uint16_t sbits = reinterpret_cast<const uint16_t*>(p.pool + p.lay.v_scale)[vec];
+        const float a = (float)__builtin_bit_cast(_Float16, sbits) * inv_sqrt_d<D>();
+        uint32_t o[C / 2];
+#pragma unroll
+        for (int j = 0; j < C / 2; ++j) o[j] = pack_bf16x2(y[2 * j] * a, y[2 * j + 1] * a);
+        for (uint32_t ag = 0; ag < p.n_out; ++ag) {
+            uint4* dst = reinterpret_cast<uint4*>(p.v_out[ag] + out_elem);
+#pragma unroll
+            for (int i = 0; i < C / 8; ++i)
+                dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
+                              hipStream_t stream) {
+    EncodeParams p;
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.pool = static_cast<uint8_t*>(pool);
+    p.absmax = ws;
+    p.L = s.L;
+    p.H = s.H;
+    p.T = s.T;
+    p.nb = pool_blocks_per_head(s.T);
+    p.n_waves = (uint64_t)s.L * s.H * p.nb;
+    p.lay = pool_layout(s.L, s.H, s.T, s.d);
+
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((s.L + 255) / 256), dim3(256), 0, stream, ws, s.L);
+    const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
+    uint64_t gx = (per_layer_u4 + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
+    if (gx > 1024) gx = 1024;
+    hipLaunchKernelGGL(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), 0, stream,
+                       static_cast<const uint4*>(k), per_layer_u4, ws);
+    const uint64_t nblocks = (p.n_waves + 3) / 4;
+    if (s.d == 64)
+        hipLaunchKernelGGL(pool_encode_kernel<64>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(pool_encode_kernel<128>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,
+                              void* const* k_out, void* const* v_out, uint32_t n_out,
+                              int32_t* dev_status, hipStream_t stream) {
+    DecodeParams p;
+    p.pool = static_cast<const uint8_t*>(pool);
+    p.status = dev_status;
+    p.L = s.L;
+    p.H = s.H;
+    p.T = s.T;
+    p.nb = pool_blocks_per_head(s.T);
+    p.l0 = l0;
+    p.n_out = n_out;
+    p.n_waves = (uint64_t)(l1 - l0) * s.H * p.nb;
+    p.lay = pool_layout(s.L, s.H, s.T, s.d);
+    for (uint32_t a = 0; a < (uint32_t)kMaxAgents; ++a) {
+        p.k_out[a] = a < n_out ? static_cast<uint16_t*>(k_out[a]) : nullptr;
+        p.v_out[a] = a < n_out ? static_cast<uint16_t*>(v_out[a]) : nullptr;
+    }
+    const uint64_t nblocks = (p.n_waves + 3) / 4;
+    if (s.d == 64)
+        hipLaunchKernelGGL(pool_decode_kernel<64>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(pool_decode_kernel<128>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

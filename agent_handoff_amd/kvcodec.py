@@ -1,0 +1,206 @@
+"""Python binding of libkvcodec (include/kvcodec.h): argument marshalling only.
+
+Every function has the C entry point's name. Device buffers are torch
+tensors on the GPU (contiguous; bf16 tensors for K/V, uint8 for pools and
+cards); the work is enqueued on `stream` (a torch.cuda.Stream, a raw
+hipStream_t integer, or None for torch's current stream). Errors from the
+library raise KvcError. If libkvcodec.so is missing the import fails: there
+is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvcodec.so")
+
+KVC_OK = 0
+KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN = -1, -2, -3, -4
+KVC_E_ALIAS, KVC_E_FORMAT, KVC_E_RANGE, KVC_E_HIP = -5, -6, -7, -8
+KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY = 1, 2, 4
+KVC_MAX_AGENTS = 64
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {kvc_strerror(code)} ({code})")
+        self.code = code
+
+
+class kvc_shape(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_uint32), ("num_kv_heads", ctypes.c_uint32),
+                ("num_tokens", ctypes.c_uint32), ("head_dim", ctypes.c_uint32)]
+
+
+class kvc_card_meta(ctypes.Structure):
+    _fields_ = [("model_id", ctypes.c_char * 64), ("position_offset", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    sz, i32, u32, p = ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p
+    sp = ctypes.POINTER(kvc_shape)
+    sig = {
+        "kvpool_bytes": (sz, [sp]),
+        "kvpool_workspace_bytes": (sz, [sp]),
+        "kvpool_encode": (i32, [sp, p, p, p, sz, p, sz, p]),
+        "kvpool_decode": (i32, [sp, p, sz, u32, u32, ctypes.POINTER(p), ctypes.POINTER(p), u32, p, p]),
+        "cachecard_record_bytes": (sz, [u32, u32]),
+        "cachecard_max_bytes": (sz, [sp]),
+        "cachecard_bytes_host": (sz, [sp, p]),
+        "cachecard_workspace_bytes": (sz, [sp]),
+        "cachecard_pack": (i32, [sp, p, p, p, ctypes.POINTER(kvc_card_meta), p, sz, p, p, p, sz, p]),
+        "cachecard_unpack": (i32, [sp, p, sz, p, p, p, p, sz, p]),
+        "kvc_parse_header": (i32, [p, sz, sp, ctypes.POINTER(u32)]),
+        "kvc_strerror": (ctypes.c_char_p, [i32]),
+        "kvc_codebook": (None, [p, p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_decode",
+            "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
+            "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack", "kvc_parse_header",
+            "kvc_strerror", "kvc_codebook")
+
+
+def library():
+    return _lib
+
+
+def _shape(shape):
+    if isinstance(shape, kvc_shape):
+        return shape
+    L, H, T, d = (int(x) for x in shape)
+    return kvc_shape(L, H, T, d)
+
+
+def _ptr(t):
+    """Device address of a torch tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc, what):
+    if rc != KVC_OK:
+        raise KvcError(rc, what)
+
+
+def kvc_strerror(code):
+    return _lib.kvc_strerror(int(code)).decode()
+
+
+# ------------------------------------------------------------------ pool mode
+
+def kvpool_bytes(shape):
+    return int(_lib.kvpool_bytes(ctypes.byref(_shape(shape))))
+
+
+def kvpool_workspace_bytes(shape):
+    return int(_lib.kvpool_workspace_bytes(ctypes.byref(_shape(shape))))
+
+
+def kvpool_encode(shape, k, v, pool, ws, stream=None):
+    """k, v: bf16 [L, H, T, d]; pool, ws: uint8 device buffers."""
+    _check(_lib.kvpool_encode(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(pool), _nbytes(pool),
+                              _ptr(ws), _nbytes(ws), _stream(stream)), "kvpool_encode")
+
+
+def kvpool_decode(shape, pool, layer_begin, layer_end, k_outs, v_outs, dev_status=None, stream=None):
+    """k_outs, v_outs: lists of bf16 [layer_end-layer_begin, H, T, d] tensors
+    (one pair per agent); dev_status: int32 device tensor of 1 element or None."""
+    n = len(k_outs)
+    if len(v_outs) != n:
+        raise ValueError("k_outs and v_outs must have the same length")
+    karr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_outs])
+    varr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_outs])
+    for t in list(k_outs) + list(v_outs):
+        _ptr(t)
+    _check(_lib.kvpool_decode(ctypes.byref(_shape(shape)), _ptr(pool), _nbytes(pool), int(layer_begin),
+                              int(layer_end), karr, varr, n, _ptr(dev_status), _stream(stream)),
+           "kvpool_decode")
+
+
+# ------------------------------------------------------------------ CacheCard mode
+
+def cachecard_record_bytes(head_dim, bits):
+    return int(_lib.cachecard_record_bytes(int(head_dim), int(bits)))
+
+
+def cachecard_max_bytes(shape):
+    return int(_lib.cachecard_max_bytes(ctypes.byref(_shape(shape))))
+
+
+def cachecard_bytes_host(shape, widths_host):
+    w = np.ascontiguousarray(widths_host, np.uint8)
+    return int(_lib.cachecard_bytes_host(ctypes.byref(_shape(shape)), w.ctypes.data_as(ctypes.c_void_p)))
+
+
+def cachecard_workspace_bytes(shape):
+    return int(_lib.cachecard_workspace_bytes(ctypes.byref(_shape(shape))))
+
+
+def cachecard_pack(shape, k, v, widths, card, ws, model_id=b"", position_offset=0,
+                   dev_card_bytes=None, dev_status=None, stream=None):
+    """widths: uint8 [T] device tensor; card, ws: uint8 device buffers;
+    dev_card_bytes: int64 device tensor of 1 element or None."""
+    meta = kvc_card_meta()
+    mid = model_id.encode() if isinstance(model_id, str) else bytes(model_id)
+    meta.model_id = mid[:63]
+    meta.position_offset = int(position_offset)
+    _check(_lib.cachecard_pack(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(widths), ctypes.byref(meta),
+                               _ptr(card), _nbytes(card), _ptr(dev_card_bytes), _ptr(dev_status), _ptr(ws),
+                               _nbytes(ws), _stream(stream)), "cachecard_pack")
+
+
+def cachecard_unpack(shape, card, k_out, v_out, ws, card_bytes=None, dev_status=None, stream=None):
+    n = _nbytes(card) if card_bytes is None else int(card_bytes)
+    _check(_lib.cachecard_unpack(ctypes.byref(_shape(shape)), _ptr(card), n, _ptr(k_out), _ptr(v_out),
+                                 _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_unpack")
+
+
+# ------------------------------------------------------------------ host utils
+
+def kvc_parse_header(host_bytes):
+    """bytes-like header -> ((L, H, T, d), kind) with kind 1 = pool, 2 = card."""
+    b = np.frombuffer(bytes(host_bytes), np.uint8)
+    s = kvc_shape()
+    kind = ctypes.c_uint32()
+    _check(_lib.kvc_parse_header(b.ctypes.data_as(ctypes.c_void_p), b.size, ctypes.byref(s), ctypes.byref(kind)),
+           "kvc_parse_header")
+    return (s.num_layers, s.num_kv_heads, s.num_tokens, s.head_dim), int(kind.value)
+
+
+def kvc_codebook():
+    lv = np.zeros(8, np.float32)
+    th = np.zeros(7, np.float32)
+    _lib.kvc_codebook(lv.ctypes.data_as(ctypes.c_void_p), th.ctypes.data_as(ctypes.c_void_p))
+    return lv, th

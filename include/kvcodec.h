@@ -1,0 +1,212 @@
+/*
+ * kvcodec.h - compressed KV-cache codec for multi-agent handoff, AMD Instinct
+ * MI355X (gfx950). C ABI; every entry point is extern "C".
+ *
+ * Two modes, both write-once / read-many:
+ *
+ *  Pool mode - PolyKV, "A Shared Asymmetrically-Compressed KV Cache Pool for
+ *  Multi-Agent LLM Inference" (gist.science/ko/paper/2604.24971):
+ *    section 2.A (SharedKVPool, PooledAgent): the whole KV state of a shared
+ *    document is compressed once into one object; every agent decompresses
+ *    it layer by layer into its own cache;
+ *    section 2.B item 1: keys become int8 with one linear scale per tensor
+ *    (here: per layer, over all heads, tokens and channels);
+ *    section 2.B item 2: values are rotated by the fast Walsh-Hadamard
+ *    transform, each coordinate is mapped to a 3-bit Lloyd-Max level for
+ *    N(0,1) (after division by a per-vector fp16 RMS scale), and decoding
+ *    looks the levels up and applies the inverse transform.
+ *
+ *  CacheCard mode - QKVShare, "Quantized KV-Cache Handoff for Multi-Agent
+ *  On-Device LLMs" (gist.science/ko/paper/2605.03884), method items 1-3: each
+ *  token carries a bit-width from {2, 4, 8, FP16}; the CacheCard holds the
+ *  quantised KV groups (here: 32 consecutive channels, min-max), the token
+ *  widths and metadata (sequence length, model ID, position offset); the
+ *  receiver rebuilds full-width past_key_values before its forward pass.
+ *
+ * Conventions for every call:
+ *  - Tensors are bf16 [L][H][T][d] (layer, kv-head, token, channel), dense,
+ *    row = one head vector; d is 64 or 128.
+ *  - Pointers are device memory unless marked "host". Device pointers must
+ *    be 16-byte aligned (pools and cards 256-byte aligned).
+ *  - The caller owns every buffer. The library allocates and frees nothing
+ *    and keeps no state between calls; size queries give every buffer size.
+ *  - Device work is enqueued on `stream` and is asynchronous: synchronise
+ *    before reading outputs, byte counts or status words on the host.
+ *  - Host-detectable errors return a negative KVC_E_* code before anything is
+ *    enqueued. Data errors found on the device (bad header, bad width, card
+ *    too large for its buffer) set bits of *dev_status (when not NULL); the
+ *    affected outputs are then unspecified.
+ *  - Outputs must not overlap inputs (checked on address ranges).
+ *  - Pools and cards are never written by decode/unpack, so any number of
+ *    decodes of one pool may run concurrently on any streams. Two encodes
+ *    sharing one workspace must not overlap.
+ */
+#ifndef KVCODEC_H
+#define KVCODEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvc_shape {
+    uint32_t num_layers;   /* L >= 1 */
+    uint32_t num_kv_heads; /* H >= 1 */
+    uint32_t num_tokens;   /* T >= 1 */
+    uint32_t head_dim;     /* d: 64 or 128 */
+} kvc_shape;
+
+/* CacheCard metadata besides the sequence length (QKVShare method item 2). */
+typedef struct kvc_card_meta {
+    char model_id[64];       /* NUL-terminated, at most 63 characters kept */
+    int64_t position_offset; /* position of token 0 in the sender's sequence */
+} kvc_card_meta;
+
+enum {
+    KVC_OK = 0,
+    KVC_E_NULL = -1,   /* a required pointer is NULL */
+    KVC_E_SHAPE = -2,  /* shape out of range (d not 64/128, zero sizes) */
+    KVC_E_SIZE = -3,   /* a buffer is smaller than required */
+    KVC_E_ALIGN = -4,  /* a pointer is not aligned as required */
+    KVC_E_ALIAS = -5,  /* an output overlaps an input or another output */
+    KVC_E_FORMAT = -6, /* malformed header bytes */
+    KVC_E_RANGE = -7,  /* bad layer range or agent count */
+    KVC_E_HIP = -8     /* a kernel launch failed */
+};
+
+/* Bits set in *dev_status by device-side checks. */
+enum {
+    KVC_DEV_BAD_HEADER = 1, /* pool/card header does not match the shape */
+    KVC_DEV_BAD_WIDTH = 2,  /* a token width is not 2, 4, 8 or 16 */
+    KVC_DEV_CAPACITY = 4    /* the card does not fit card_capacity */
+};
+
+#define KVC_MAX_AGENTS 64
+
+/* ---------------------------------------------------------------- pool mode */
+
+/* Exact size in bytes of the pool for `shape` (PolyKV 2.A: one object,
+ * independent of the number of agents); 0 if the shape is invalid.
+ * Layout (little-endian, sections on 256-byte boundaries):
+ *   header 64 B: "KVPL", u16 version 1, u16 kind 1, u32 L, H, T, d,
+ *                u64 offsets of k_scale, k_codes, v_scale, v_codes, u64 total
+ *   k_scale f32[L]           per-layer key step m_l / 127
+ *   k_codes i8[L][H][T][d]   round(x * 127 / m_l)
+ *   v_scale f16[L][H][T]     RMS of each value vector
+ *   v_codes u8[L][H][T][3][d/8]  3 bit planes per vector: bit m of byte j
+ *           of plane p is bit p of the 3-bit code of coordinate 8j+m
+ * Payload ratio against bf16 K+V: 16 / 5.5 (PolyKV 2.B, compression ratio). */
+size_t kvpool_bytes(const kvc_shape* shape);
+
+/* Workspace bytes needed by kvpool_encode (per-layer reductions). */
+size_t kvpool_workspace_bytes(const kvc_shape* shape);
+
+/* Compress bf16 K and V ([L][H][T][d]) into `pool` (PolyKV 2.B items 1-2).
+ *   k, v       device, bf16, 16-byte aligned, read only
+ *   pool       device, >= kvpool_bytes(shape), 256-byte aligned; fully written
+ *              (header, sections and zero padding)
+ *   ws         device workspace of >= kvpool_workspace_bytes(shape) bytes,
+ *              16-byte aligned; clobbered
+ * Keys: m_l = max |K[l]| over the layer; codes clamp(rint(x*(127/m_l))).
+ * Values: per vector, s = fp16(sqrt(sum x^2 / d)), y = H x (Sylvester
+ * order), z = y / (sqrt(d) s), code = number of Lloyd-Max thresholds <= z.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
+ * KVC_E_HIP. */
+int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool,
+                  size_t pool_bytes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decompress layers [layer_begin, layer_end) of `pool` into the caches of
+ * n_out agents (PolyKV 2.A, PooledAgent: layer-wise injection into each
+ * agent's own cache; 2.B item 2: level lookup, then inverse transform).
+ * The pool is read once; every agent receives the same bf16 values.
+ *   pool          device, as written by kvpool_encode, read only
+ *   k_out, v_out  host arrays of n_out (1..KVC_MAX_AGENTS) device pointers,
+ *                 each bf16 [layer_end-layer_begin][H][T][d], 16-byte aligned
+ *   dev_status    device int32 or NULL; KVC_DEV_BAD_HEADER if the pool's
+ *                 header does not match `shape`
+ * Calling it with (l, l+1) for l = 0..L-1 in order streams the cache layer
+ * by layer. An empty range enqueues nothing and returns KVC_OK.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
+ * KVC_E_RANGE, KVC_E_HIP. */
+int kvpool_decode(const kvc_shape* shape, const void* pool, size_t pool_bytes,
+                  uint32_t layer_begin, uint32_t layer_end, void* const* k_out,
+                  void* const* v_out, uint32_t n_out, int32_t* dev_status,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------ CacheCard mode */
+
+/* Record bytes of one head vector at width b (QKVShare item 1 widths):
+ * b in {2,4,8}: f16 scale[d/32], bf16 min[d/32], then d codes of b bits,
+ * least significant bit first, padded to 16 bytes; b = 16: the d bf16
+ * inputs unchanged. 0 for any other b. For d = 128: 48, 80, 144, 256. */
+size_t cachecard_record_bytes(uint32_t head_dim, uint32_t bits);
+
+/* Upper bound on the card size (every token at width 16). */
+size_t cachecard_max_bytes(const kvc_shape* shape);
+
+/* Exact card size for host-resident widths (u8[T]); 0 if a width or the
+ * shape is invalid. Layout (little-endian):
+ *   header 256 B: "QKVC", u16 version 1, u16 kind 2, u32 L, H, T, d,
+ *     u32 group size 32, u32 0, i64 position offset, u64 widths offset (256),
+ *     u64 payload offset, u64 stream bytes S, u64 total, char model_id[64]
+ *   widths u8[T] at 256, zero padding to a 256-byte boundary
+ *   payload: 2*L*H streams of S bytes; stream (l, kv, h) at index
+ *     (2*l + kv)*H + h (kv 0 = K, 1 = V); token t's record starts at the sum
+ *     of the record sizes of tokens 0..t-1; S rounds that sum up to 256. */
+size_t cachecard_bytes_host(const kvc_shape* shape, const uint8_t* widths_host);
+
+/* Workspace bytes needed by cachecard_pack / cachecard_unpack. */
+size_t cachecard_workspace_bytes(const kvc_shape* shape);
+
+/* Package K and V into a CacheCard (QKVShare item 2).
+ *   k, v            device bf16 [L][H][T][d]; d a multiple of 32 (64 or 128)
+ *   widths          device u8[T], each 2, 4, 8 or 16; one width per token,
+ *                   shared by every layer, head, K and V
+ *   meta            host; model_id and position_offset copied into the header
+ *   card            device, card_capacity bytes, 256-byte aligned
+ *   dev_card_bytes  device u64 or NULL; receives the card's exact size
+ *   dev_status      device int32 or NULL; KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY
+ *   ws              device workspace, >= cachecard_workspace_bytes(shape)
+ * Per group of 32 channels at width b < 16: mn, mx = group min and max,
+ * s = fp16((mx - mn) / (2^b - 1)), q = min(rint((x - mn) / s), 2^b - 1).
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
+ * KVC_E_HIP. */
+int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const uint8_t* widths,
+                   const kvc_card_meta* meta, void* card, size_t card_capacity,
+                   uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* Rebuild bf16 K and V from a CacheCard (QKVShare item 3: full-width
+ * past_key_values for the receiver): x = bf16(q * s + mn), width 16 copies.
+ *   card        device, card_bytes valid bytes, read only
+ *   k_out, v_out device bf16 [L][H][T][d]
+ *   dev_status  device int32 or NULL; KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
+ * KVC_E_HIP. */
+int cachecard_unpack(const kvc_shape* shape, const void* card, size_t card_bytes, void* k_out,
+                     void* v_out, int32_t* dev_status, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* --------------------------------------------------------------- host utils */
+
+/* Parse a pool or card header from host bytes; *kind = 1 (pool) or 2
+ * (card). KVC_E_FORMAT on bad magic, version, kind or field values,
+ * KVC_E_SIZE if n is shorter than the header. No device work. */
+int kvc_parse_header(const void* host_bytes, size_t n, kvc_shape* shape_out, uint32_t* kind_out);
+
+/* Static text for a KVC_E_* code. */
+const char* kvc_strerror(int code);
+
+/* The library's 3-bit level table (ascending, 8 values) and its 7 decision
+ * thresholds, as used by the kernels. Host only. */
+void kvc_codebook(float levels[8], float thresholds[7]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCODEC_H */

@@ -1,0 +1,83 @@
+"""Helpers for the GPU parity tests: moving bf16 bit patterns to and from the
+device, comparing against the oracle, reporting what differs."""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from agent_handoff_amd.synth import bf16_bits_to_f32
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits):
+    """numpy uint16 bf16 bits -> torch bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def to_host(t):
+    """torch bf16 tensor -> numpy uint16 bits."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_bytes(n, fill=None):
+    t = torch.empty(int(n), dtype=torch.uint8, device=DEV)
+    if fill is not None:
+        t.fill_(fill)
+    return t
+
+
+def ordered(bits):
+    """bf16 bits -> integers in value order (+0 and -0 both map to 0)."""
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def ulp_distance(a_bits, b_bits):
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def pool_section_diff(got, ref, shape):
+    """Names of pool sections whose bytes differ (empty list if identical)."""
+    off = oracle.pool_layout(*shape)
+    names = ["header+pad", "k_scale+pad", "k_codes+pad", "v_scale+pad", "v_codes+pad"]
+    bounds = [0] + off
+    bad = []
+    for i, n in enumerate(names):
+        a, b = bounds[i], bounds[i + 1]
+        if not np.array_equal(got[a:b], ref[a:b]):
+            idx = np.nonzero(got[a:b] != ref[a:b])[0]
+            bad.append(f"{n}: {idx.size} bytes differ, first at +{idx[0]} "
+                       f"(got {got[a + idx[0]]}, want {ref[a + idx[0]]})")
+    return bad
+
+
+def assert_pool_equal(got, ref, shape):
+    assert got.size == ref.size
+    diff = pool_section_diff(got, ref, shape)
+    assert not diff, "; ".join(diff)
+
+
+def assert_decode_close(got_bits, ref_bits, what=""):
+    """Decoded bf16 within 1 ulp of the oracle's decode (values compared
+    numerically, so +0 and -0 are equal). Returns the count at 1 ulp."""
+    d = ulp_distance(got_bits, ref_bits)
+    worst = int(d.max()) if d.size else 0
+    assert worst <= 1, f"{what}: {np.count_nonzero(d > 1)} values off by more than 1 ulp (max {worst})"
+    return int(np.count_nonzero(d == 1))
+
+
+def per_head_rel_mse(x_bits, y_bits):
+    """[L, H] relative MSE of reconstruction y against input x."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    y = bf16_bits_to_f32(y_bits).astype(np.float64)
+    num = np.sum((x - y) ** 2, axis=(2, 3))
+    den = np.sum(x * x, axis=(2, 3))
+    return num / np.maximum(den, 1e-300)
