@@ -356,18 +356,16 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
     sp.T = s.T;
     sp.d = s.d;
     sp.meta = meta;
-    hipLaunchKernelGGL(card_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sp);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sp);
+    if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
     p.widths = widths;
     p.card = static_cast<uint8_t*>(card);
     const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
-    if (s.d == 64)
-        hipLaunchKernelGGL(card_pack_kernel<64>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(card_pack_kernel<128>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(s.d == 64 ? card_pack_kernel<64> : card_pack_kernel<128>, dim3(nblocks),
+                         dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_bytes, void* k_out,
@@ -385,18 +383,16 @@ hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_by
     sp.H = s.H;
     sp.T = s.T;
     sp.d = s.d;
-    hipLaunchKernelGGL(card_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sp);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sp);
+    if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k_out = static_cast<uint16_t*>(k_out);
     p.v_out = static_cast<uint16_t*>(v_out);
     p.widths = sp.widths;
     p.card_in = static_cast<const uint8_t*>(card);
     const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
-    if (s.d == 64)
-        hipLaunchKernelGGL(card_unpack_kernel<64>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(card_unpack_kernel<128>, dim3(nblocks), dim3(kBlockThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(s.d == 64 ? card_unpack_kernel<64> : card_unpack_kernel<128>, dim3(nblocks),
+                         dim3(kBlockThreads), stream, p);
 }
 
 }  // namespace kvc

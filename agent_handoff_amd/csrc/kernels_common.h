@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace kvc {
 
@@ -69,6 +71,24 @@ __device__ __forceinline__ uint64_t shift_out_bit(uint32_t& w) {
     asm("v_add_co_u32_e64 %0, %1, %2, %2" : "=v"(r), "=s"(mask) : "v"(w));
     w = r;
     return mask;
+}
+
+// Launch and return this launch's own status (hipGetLastError would also
+// report errors left behind by unrelated earlier runtime calls).
+// With KVC_DEBUG set in the environment a failing launch prints the HIP
+// error text to stderr.
+inline hipError_t report_launch(hipError_t e, const char* what) {
+    if (e != hipSuccess && getenv("KVC_DEBUG"))
+        fprintf(stderr, "kvcodec: launch of %s failed: %s (%d)\n", what, hipGetErrorString(e), (int)e);
+    return e;
+}
+
+template <typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t stream,
+                                Args... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return report_launch(hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream),
+                         "kernel");
 }
 
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -424,18 +424,17 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.n_waves = (uint64_t)s.L * s.H * p.nb;
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((s.L + 255) / 256), dim3(256), 0, stream, ws, s.L);
+    hipError_t e = launch_kernel(fill_zero_kernel, dim3((s.L + 255) / 256), dim3(256), stream, ws, s.L);
+    if (e != hipSuccess) return e;
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
     uint64_t gx = (per_layer_u4 + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
     if (gx > 1024) gx = 1024;
-    hipLaunchKernelGGL(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), 0, stream,
-                       static_cast<const uint4*>(k), per_layer_u4, ws);
+    e = launch_kernel(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), stream,
+                      static_cast<const uint4*>(k), per_layer_u4, ws);
+    if (e != hipSuccess) return e;
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    if (s.d == 64)
-        hipLaunchKernelGGL(pool_encode_kernel<64>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(pool_encode_kernel<128>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>, dim3((uint32_t)nblocks),
+                         dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,
@@ -457,11 +456,8 @@ hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uin
         p.v_out[a] = a < n_out ? static_cast<uint16_t*>(v_out[a]) : nullptr;
     }
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    if (s.d == 64)
-        hipLaunchKernelGGL(pool_decode_kernel<64>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(pool_decode_kernel<128>, dim3((uint32_t)nblocks), dim3(kBlockThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(s.d == 64 ? pool_decode_kernel<64> : pool_decode_kernel<128>, dim3((uint32_t)nblocks),
+                         dim3(kBlockThreads), stream, p);
 }
 
 }  // namespace kvc

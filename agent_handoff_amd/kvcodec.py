@@ -12,6 +12,11 @@ import ctypes
 import os
 
 import numpy as np
+# torch first: it ships its own HIP runtime (SONAME libamdhip64.so.7) and
+# names it by file name, so if libkvcodec.so were loaded first the process
+# would hold two HIP runtimes and our launches would not see torch's memory
+# or streams. Loaded in this order, libkvcodec binds to torch's runtime.
+import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcodec.so")
