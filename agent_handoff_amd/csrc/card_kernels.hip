@@ -288,7 +288,7 @@ __device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, ui
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p) {
     constexpr uint32_t G = D / kCardGroup;
-    constexpr uint32_t TPW = kWave / G;
+    constexpr uint32_t TPW = kWave / G;  // the wave's tokens: 4 KiB of bf16 output
     const uint32_t lane = lane_id();
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
@@ -296,29 +296,44 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     const uint64_t S = p.info[0];
     const uint64_t s = wave / p.nbk;
     const uint32_t b = (uint32_t)(wave % p.nbk);
-    const uint32_t tok = b * TPW + lane / G;
+    const uint32_t t0 = b * TPW;
+    const uint32_t tok = t0 + lane / G;
     const uint32_t g = lane % G;
-    if (tok >= p.T) return;
+    const bool valid = tok < p.T;
+    const uint32_t nv = (p.T - t0 < TPW) ? p.T - t0 : TPW;
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
-    uint16_t* dst = (kv ? p.v_out : p.k_out) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
-    const uint32_t width = p.widths[tok];
-    const uint8_t* rec = p.card_in + p.payload + s * S + p.off[tok];
     uint32_t o[16];
-    if (width == 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
-    } else if (width == 2) {
-        dequant_group<2>(rec, G, g, o);
-    } else if (width == 4) {
-        dequant_group<4>(rec, G, g, o);
-    } else {
-        dequant_group<8>(rec, G, g, o);
+    for (int i = 0; i < 16; ++i) o[i] = 0;
+    if (valid) {
+        const uint32_t width = p.widths[tok];
+        const uint8_t* rec = p.card_in + p.payload + s * S + p.off[tok];
+        if (width == 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
+        } else if (width == 2) {
+            dequant_group<2>(rec, G, g, o);
+        } else if (width == 4) {
+            dequant_group<4>(rec, G, g, o);
+        } else {
+            dequant_group<8>(rec, G, g, o);
+        }
     }
+    // Stage the wave's contiguous output image in LDS, then store it with
+    // each instruction covering a contiguous span (lane-strided 64-byte
+    // stores run at about half the write bandwidth).
+    __shared__ uint4 stage[kBlockThreads / kWave][kWave * 4];
+    uint4* st = stage[threadIdx.x / kWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int c = 0; c < 4; ++c) st[lane * 4 + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    uint4* dst = reinterpret_cast<uint4*>((kv ? p.v_out : p.k_out) + (((uint64_t)l * p.H + h) * p.T + t0) * D);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 chunk = st[64 * j + lane];
+        if ((64 * j + lane) / (2 * D / 16) < nv) dst[64 * j + lane] = chunk;
+    }
 }
 
 }  // namespace

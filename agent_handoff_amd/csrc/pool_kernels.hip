@@ -332,15 +332,31 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     const bool valid = tok < p.T;
     const uint64_t vec = lh * p.T + tok;
     const uint64_t elem = vec * D + (uint64_t)m * C;
-    const uint64_t out_elem = (lh_rel * p.T + tok) * D + (uint64_t)m * C;
+
+    // Outputs are staged per wave in LDS (the lane-major 64-byte chunks form
+    // the wave's contiguous 16-token output image) and stored so that each
+    // store instruction covers one contiguous span across the wave: stores
+    // where every lane writes its own 64-byte piece run at about half the
+    // write bandwidth of coalesced ones.
+    constexpr int CH = C / 8;  // 16-byte chunks per lane
+    __shared__ uint4 stage[kBlockThreads / kWave][kWave * CH];
+    uint4* st = stage[threadIdx.x / kWave];
+    const uint32_t t0 = blk * kBlockTokens;
+    const uint32_t nv = (p.T - t0 < kBlockTokens) ? p.T - t0 : kBlockTokens;  // valid tokens of the block
+    const uint64_t out_base = (lh_rel * p.T + t0) * D / 8;  // in 16-byte chunks
 
     // ---- keys: bf16(q * scale)
     const float ks = reinterpret_cast<const float*>(p.pool + p.lay.k_scale)[l];
-    if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.pool + p.lay.k_codes + elem);
+    {
         uint4 raw[C / 16];
+        if (valid) {
+            const uint4* src = reinterpret_cast<const uint4*>(p.pool + p.lay.k_codes + elem);
 #pragma unroll
-        for (int i = 0; i < C / 16; ++i) raw[i] = src[i];
+            for (int i = 0; i < C / 16; ++i) raw[i] = src[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < C / 16; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+        }
         const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
         uint32_t o[C / 2];
 #pragma unroll
@@ -353,19 +369,19 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
             o[2 * j] = pack_bf16x2(f0, f1);
             o[2 * j + 1] = pack_bf16x2(f2, f3);
         }
-        for (uint32_t a = 0; a < p.n_out; ++a) {
-            uint4* dst = reinterpret_cast<uint4*>(p.k_out[a] + out_elem);
 #pragma unroll
-            for (int i = 0; i < C / 8; ++i)
-                dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-        }
+        for (int c = 0; c < CH; ++c) st[lane * CH + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     }
+    uint4 kc[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) kc[j] = st[64 * j + lane];
 
     // ---- values: level lookup by the code bits of this lane, then the
     // butterfly, then * (s / sqrt(d)).
     float c0 = kLv0, c1 = kLv1, c2 = kLv2, c3 = kLv3;
     asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
     uint32_t pw[3] = {0, 0, 0};
+    uint16_t sbits = 0;
     if (valid) {
         const uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
         if (D == 128) {
@@ -378,6 +394,7 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
                 pw[q] = (m & 1u) ? (w & 0xFFFF0000u) : (w << 16);  // this lane's 16 bits on top
             }
         }
+        sbits = reinterpret_cast<const uint16_t*>(p.pool + p.lay.v_scale)[vec];
     }
     float y[C];
 #pragma unroll
@@ -393,17 +410,28 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
         y[i] = signed_by_mask(w2, mag);
     }
     fwht_quad<C>(y, m);
-    if (valid) {
-        const uint16_t sbits = reinterpret_cast<const uint16_t*>(p.pool + p.lay.v_scale)[vec];
+    {
         const float a = (float)__builtin_bit_cast(_Float16, sbits) * inv_sqrt_d<D>();
         uint32_t o[C / 2];
 #pragma unroll
         for (int j = 0; j < C / 2; ++j) o[j] = pack_bf16x2(y[2 * j] * a, y[2 * j + 1] * a);
-        for (uint32_t ag = 0; ag < p.n_out; ++ag) {
-            uint4* dst = reinterpret_cast<uint4*>(p.v_out[ag] + out_elem);
 #pragma unroll
-            for (int i = 0; i < C / 8; ++i)
-                dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        for (int c = 0; c < CH; ++c) st[lane * CH + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    }
+    uint4 vc[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) vc[j] = st[64 * j + lane];
+
+    // chunk 64*j + lane of the image belongs to token (64*j + lane) / (4*CH)
+    for (uint32_t ag = 0; ag < p.n_out; ++ag) {
+        uint4* dk = reinterpret_cast<uint4*>(p.k_out[ag]) + out_base;
+        uint4* dv = reinterpret_cast<uint4*>(p.v_out[ag]) + out_base;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if ((64 * j + lane) / (4 * CH) < nv) {
+                dk[64 * j + lane] = kc[j];
+                dv[64 * j + lane] = vc[j];
+            }
         }
     }
 }

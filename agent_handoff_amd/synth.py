@@ -150,3 +150,57 @@ def card_widths(w, seed=0, T=None, mean_run=16.0):
         out[t:t + n] = g.choice(WIDTHS, p=WIDTH_PROBS)
         t += n
     return out
+
+
+# ------------------------------------------------------------------ on-device
+# The same recipes drawn on the GPU with torch's generator (Philox), for the
+# large workloads of the benchmark. Values differ from the numpy streams of
+# the same seed; whoever checks a result copies the inputs it needs back.
+
+def _torch_seed(seed, cfg, tensor, layer):
+    return int(np.random.SeedSequence([seed, cfg, tensor, layer]).generate_state(1, np.uint64)[0] >> np.uint64(1))
+
+
+def layer_values_torch(recipe, seed, cfg, tensor, layer, H, T, d, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(seed, cfg, tensor, layer))
+    gs = torch.Generator(device=device)
+    gs.manual_seed(_torch_seed(seed, cfg, STRUCT_TENSOR, 1000 * (tensor + 1) + layer))
+    if recipe == "normal":
+        return torch.randn((H, T, d), generator=g, device=device)
+    if recipe == "normal_two_channels_x8":
+        x = torch.randn((H, T, d), generator=g, device=device)
+        ch = torch.randperm(d, generator=gs, device=device)[:2]
+        x[:, :, ch] *= 8.0
+        return x
+    if recipe in ("normal_outliers_x20", "normal_outliers_x20_sink_x50"):
+        x = torch.randn((H, T, d), generator=g, device=device)
+        n_out = int(round(0.02 * H * d))
+        flat = torch.randperm(H * d, generator=gs, device=device)[:n_out]
+        x[flat // d, :, flat % d] *= 20.0
+        if recipe.endswith("sink_x50"):
+            x[:, 0, :] *= 50.0
+        return x
+    if recipe == "student_t5_lognormal_channels":
+        z = torch.randn((H, T, d), generator=g, device=device)
+        chi2 = torch.zeros((H, T, d), device=device)
+        for _ in range(5):
+            chi2 += torch.randn((H, T, d), generator=g, device=device) ** 2
+        x = z / torch.sqrt(chi2 / 5.0)
+        scale = torch.exp(0.5 * torch.randn((H, 1, d), generator=gs, device=device))
+        return x * scale
+    raise ValueError(f"unknown recipe {recipe}")
+
+
+def kv_tensors_torch(w, seed=0, device="cuda", shape=None):
+    """(K, V) as bf16 torch tensors [L, H, T, d] on `device`."""
+    import torch
+    L, H, T, d = shape if shape is not None else w.shape
+    out = []
+    for tensor in (K_TENSOR, V_TENSOR):
+        t = torch.empty((L, H, T, d), dtype=torch.bfloat16, device=device)
+        for l in range(L):
+            t[l] = layer_values_torch(w.recipe, seed, w.cfg, tensor, l, H, T, d, device).to(torch.bfloat16)
+        out.append(t)
+    return out[0], out[1]

@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed KV-cache codec on one MI355X.
+
+One step = one pass of the whole hot path over the Llama-3-8B-shaped 4K
+shared cache (32 layers x 8 kv-heads x 4096 tokens x head_dim 128, bf16 K/V,
+Student-t(5) values with log-normal channel scales):
+  kvpool_encode   K+V -> pool                        (PolyKV 2.B)
+  kvpool_decode   pool -> bf16 K/V of 15 agents       (PolyKV 2.A fan-out)
+  cachecard_pack  K+V -> CacheCard, per-token widths  (QKVShare item 2)
+  cachecard_unpack card -> bf16 K/V                   (QKVShare item 3)
+Inputs are generated on the GPU before timing. The JSON line reports
+whole-step throughput in algorithmic GB/s (bytes each op must read and write
+once), the per-op figures, the roofline of the dominant kernel (timed with
+HIP events on the stream it runs on) and the CPU oracle timed on a sample of
+the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "KV codec encode/decode GB/s and % of HBM peak, Llama-3-8B shape 4K tok"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--agents", type=int, default=15)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=32, help="layers of the workload in the CPU oracle sample")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per dispatch (from rocprofv3 counters)")
+    return ap.parse_args()
+
+
+def pool_payload_bytes(L, H, T, d):
+    """Bytes of the pool's sections without header or padding."""
+    vecs = L * H * T
+    return 4 * L + vecs * d + 2 * vecs + vecs * 3 * d // 8
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this codec is measured on "
+              "one GPU's share; the multi-GPU handoff is a design note, not a benchmark)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from agent_handoff_amd import kvcodec as kv
+    from agent_handoff_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[3]
+    L, H, T, d = shape = w.shape
+    A = args.agents
+    kv_bytes = L * H * T * d * 2
+
+    log(f"generating {w.name} inputs on the GPU")
+    k, v = synth.kv_tensors_torch(w, args.seed, dev)
+    widths_np = synth.card_widths(synth.WORKLOADS[4], args.seed, T=T)
+    widths = torch.from_numpy(widths_np).to(dev)
+
+    pool = torch.empty(kv.kvpool_bytes(shape), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kv.kvpool_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    k_out = [torch.empty_like(k) for _ in range(A)]
+    v_out = [torch.empty_like(v) for _ in range(A)]
+    card_n = kv.cachecard_bytes_host(shape, widths_np)
+    card = torch.empty(card_n, dtype=torch.uint8, device=dev)
+    cws = torch.empty(kv.cachecard_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    k_rt = torch.empty_like(k)
+    v_rt = torch.empty_like(v)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    stream = torch.cuda.Stream()
+    ops = ["encode", "decode", "pack", "unpack"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kv.kvpool_encode(shape, k, v, pool, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kv.kvpool_decode(shape, pool, 0, L, k_out, v_out, status, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        kv.cachecard_pack(shape, k, v, widths, card, cws, b"llama-3-8b", 0, None, status, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        kv.cachecard_unpack(shape, card, k_rt, v_rt, cws, card_n, status, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set"
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {o: [] for o in ops}
+    for ev in events:
+        for j, o in enumerate(ops):
+            per_op[o].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    step_s = [sum(per_op[o][i] for o in ops) for i in range(args.steps)]
+    ms_per_step = wall / args.steps * 1e3
+
+    pool_b = pool_payload_bytes(*shape)
+    alg = {
+        "encode": 2 * kv_bytes + pool_b,
+        "decode": pool_b + A * 2 * kv_bytes,
+        "pack": 2 * kv_bytes + card_n,
+        "unpack": card_n + 2 * kv_bytes,
+    }
+    total_bytes = sum(alg.values())
+    value = total_bytes / (wall / args.steps) / 1e9
+
+    def med(x):
+        return float(np.median(np.asarray(x)))
+
+    ops_out = {}
+    for o in ops:
+        t = med(per_op[o])
+        gbs = alg[o] / t / 1e9
+        ops_out[o] = {"us": round(t * 1e6, 2), "bytes": alg[o], "GB/s": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # dominant kernel: the one with the most time per step
+    dom = max(ops, key=lambda o: med(per_op[o]))
+    kernel_names = {"encode": "pool_encode_kernel", "decode": "pool_decode_kernel",
+                    "pack": "card_pack_kernel", "unpack": "card_unpack_kernel"}
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        entry = tr.get(kernel_names[dom])
+        if entry and entry.get("library_sha") == _lib_sha(kv.LIB_PATH):
+            traffic = entry.get("bytes_per_dispatch")
+    ach = alg[dom] / med(per_op[dom]) / 1e9
+    roofline = {"bound": "hbm", "kernel": kernel_names[dom], "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(k, v, widths_np, shape, args.cpu_layers, A)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "kv_heads": H, "tokens": T, "head_dim": d, "agents": A,
+                   "values": "student-t(5) x log-normal channel scales",
+                   "card_widths": "runs of geometric length, mean 16, widths 2/4/8/16 at .4/.3/.2/.1"},
+        "ops": ops_out,
+        "step_ms_events": round(med(step_s) * 1e3, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _lib_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _oracle_pass(kb, vb, widths_np, sub, agents):
+    """encode, decode (+ copies to the other agents' buffers), card pack and
+    unpack with the CPU oracle; returns (seconds per op, card bytes)."""
+    import numpy as np
+
+    import oracle
+    t0 = time.perf_counter()
+    pool = oracle.pool_encode(kb, vb)
+    t1 = time.perf_counter()
+    dk, dv = oracle.pool_decode(pool, sub)
+    # one decode serves every agent; the other agents' buffers are filled by copies
+    ck, cv = np.empty_like(dk), np.empty_like(dv)
+    for _ in range(agents - 1):
+        np.copyto(ck, dk)
+        np.copyto(cv, dv)
+    t2 = time.perf_counter()
+    card = oracle.card_pack(kb, vb, widths_np)
+    t3 = time.perf_counter()
+    oracle.card_unpack(card, sub)
+    t4 = time.perf_counter()
+    return {"encode": t1 - t0, "decode": t2 - t1, "pack": t3 - t2, "unpack": t4 - t3}, card.size
+
+
+def cpu_baseline(k, v, widths_np, shape, layers, agents):
+    """The CPU oracle on the first `layers` layers of the same workload with
+    every host thread, and on one layer with a single thread; the same
+    algorithmic byte accounting as the GPU step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    L, H, T, d = shape
+
+    def bits(t, n):
+        return t[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def gbs(n, secs, card_bytes):
+        kv_bytes = n * H * T * d * 2
+        pool_b = pool_payload_bytes(n, H, T, d)
+        nbytes = (2 * kv_bytes + pool_b) + (pool_b + agents * 2 * kv_bytes) + 2 * (2 * kv_bytes + card_bytes)
+        return nbytes / secs / 1e9
+
+    oracle.lib()
+    threads = oracle.max_threads()
+    kb, vb = bits(k, layers), bits(v, layers)
+    secs, card_bytes = _oracle_pass(kb, vb, widths_np, (layers, H, T, d), agents)
+    total = sum(secs.values())
+    oracle.set_threads(1)
+    try:
+        s1, c1 = _oracle_pass(kb[:1].copy(), vb[:1].copy(), widths_np, (1, H, T, d), agents)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(gbs(layers, total, card_bytes), 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layers 0..{layers - 1} of {L} of the same workload: encode, decode + copies to "
+                      f"{agents} agents, card pack, unpack ({total:.1f} s)",
+            "seconds": {o: round(t, 3) for o, t in secs.items()},
+            "single_thread": {"value": round(gbs(1, sum(s1.values()), c1), 3), "unit": "GB/s", "cores": 1,
+                              "sample": f"layer 0 ({sum(s1.values()):.1f} s)"}}
+
+
+if __name__ == "__main__":
+    main()

@@ -69,6 +69,10 @@ def lib():
         L.or_card_pack.argtypes = [u32] * 4 + [p, p, p, ctypes.c_char_p, i64, p]
         L.or_card_unpack.restype = ctypes.c_int
         L.or_card_unpack.argtypes = [u32] * 4 + [p, u64, p, p]
+        L.or_set_threads.restype = None
+        L.or_set_threads.argtypes = [ctypes.c_int]
+        L.or_max_threads.restype = ctypes.c_int
+        L.or_max_threads.argtypes = []
         L.or_f64_to_bf16.restype = ctypes.c_uint16
         L.or_f64_to_bf16.argtypes = [ctypes.c_double]
         L.or_f32_to_f16.restype = ctypes.c_uint16
@@ -77,6 +81,14 @@ def lib():
         L.or_f16_to_f32.argtypes = [ctypes.c_uint16]
         _lib = L
     return _lib
+
+
+def set_threads(n):
+    lib().or_set_threads(int(n))
+
+
+def max_threads():
+    return int(lib().or_max_threads())
 
 
 def _ptr(a):

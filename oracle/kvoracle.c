@@ -39,9 +39,14 @@
  * rounded once to bf16.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Thread count of the OpenMP loops below (timing only). */
+void or_set_threads(int n) { omp_set_num_threads(n); }
+int or_max_threads(void) { return omp_get_max_threads(); }
 
 #define OR_OK 0
 #define OR_E_ARG (-1)
