@@ -49,11 +49,26 @@ struct EncodeParams {
     const uint16_t* k;
     const uint16_t* v;
     uint8_t* pool;
-    const uint32_t* absmax;  // per layer: max |K| as bf16 magnitude bits
-    uint32_t L, H, T, nb;    // nb = 16-token blocks per head
-    uint64_t n_waves;        // L * H * nb
+    uint32_t* ws;           // workspace, see the slot helpers below
+    uint32_t L, H, T, nb;   // nb = 16-token blocks per head
+    uint32_t blocks_per_layer;  // H * nb
+    uint32_t wg_per_layer;      // workgroups per layer (4 blocks each)
+    uint64_t n_waves;           // L * H * nb
     PoolLayout lay;
 };
+
+// Encode workspace (u32 words): [0] workgroup ticket, [1] timeout flag, then
+//  - single pass: one word per workgroup, L x wg_per_layer, holding
+//    0x80000000 | the workgroup's key max once published;
+//  - two passes: per layer kSlots partial maxima, each on its own 128-byte
+//    line so that concurrent atomics spread over addresses.
+constexpr uint32_t kSlots = 16;
+constexpr uint32_t kSlotStride = 32;  // words
+constexpr uint32_t kWsHead = 64;      // words
+
+__device__ __forceinline__ uint32_t* absmax_slot(uint32_t* ws, uint32_t l, uint32_t s) {
+    return ws + kWsHead + (l * kSlots + s) * kSlotStride;
+}
 
 struct DecodeParams {
     const uint8_t* pool;
@@ -138,7 +153,7 @@ __global__ void fill_zero_kernel(uint32_t* p, uint32_t n) {
 // values per instruction).
 __global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* __restrict__ k,
                                                                   uint64_t per_layer_u4,
-                                                                  uint32_t* __restrict__ absmax) {
+                                                                  uint32_t* __restrict__ ws) {
     typedef unsigned short us2 __attribute__((ext_vector_type(2)));
     const uint32_t l = blockIdx.y;
     const uint4* src = k + (uint64_t)l * per_layer_u4;
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* 
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kBlockThreads / kWave; ++w) r = red[w] > r ? red[w] : r;
-        atomicMax(absmax + l, r);
+        atomicMax(absmax_slot(ws, l, blockIdx.x % kSlots), r);
     }
 }
 
@@ -203,54 +218,113 @@ __device__ __forceinline__ void code_all(const float (&y)[C], float r, uint32_t 
     (code_slot<C, C - 1 - Is>(y, r, pl), ...);
 }
 
+// Per-wave LDS staging for the encode outputs: the wave's K codes (16
+// tokens x d bytes) and V code planes (16 tokens x 3d/8 bytes), written to
+// HBM with every store instruction covering one contiguous span.
 template <int D>
+struct EncodeStage {
+    uint4 k[kBlockTokens * D / 16];
+    uint32_t v[kBlockTokens * 3 * D / 32];
+};
+
+// Largest bf16 magnitude (as bits) of a lane's packed words.
+template <int N>
+__device__ __forceinline__ uint32_t lane_absmax_bits(const uint32_t* w) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mx = {0, 0};
+#pragma unroll
+    for (int j = 0; j < N; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j] & 0x7FFF7FFFu));
+    return mx.x > mx.y ? mx.x : mx.y;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
+        r = t > r ? t : r;
+    }
+    return r;
+}
+
+// Spin limit of the fused encode's per-layer wait, in ticks of the 100 MHz
+// constant clock: 0.5 s, far beyond any legitimate wait.
+constexpr uint64_t kWaitTicks = 50000000ull;
+
+// FUSED: one pass over K. Workgroups take tickets in start order, so every
+// workgroup of layer l has started before any of layer l+1; the host uses
+// this path only when one layer's workgroups fit on the GPU twice over, so
+// the per-layer wait always completes. Each workgroup keeps its K chunk in
+// registers, publishes its partial max, encodes its V chunk while the other
+// workgroups of the layer arrive, then quantises K from registers. The wait
+// is bounded: after 0.5 s (never expected) the pool is marked invalid
+// instead of hanging.
+// !FUSED: the per-layer maxima were reduced by key_absmax_kernel.
+template <int D, bool FUSED>
 __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams p) {
     constexpr int C = D / 4;  // channels per lane
+    constexpr int WPB = kBlockThreads / kWave;
+    __shared__ uint32_t sh[8];
+    __shared__ EncodeStage<D> stage_all[WPB];
     const uint32_t lane = lane_id();
-    if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
-    if (wave >= p.n_waves) return;
+    const uint32_t wib = wave_uniform(threadIdx.x / kWave);
+    EncodeStage<D>& stg = stage_all[wib];
 
-    const uint32_t blk = (uint32_t)(wave % p.nb);
-    const uint64_t lh = wave / p.nb;
-    const uint32_t l = (uint32_t)(lh / p.H);
-    const uint32_t h = (uint32_t)(lh % p.H);
-    const uint32_t tok = blk * kBlockTokens + (lane >> 2);
+    uint32_t l, bidx, chunk;
+    bool wave_active;
+    if (FUSED) {
+        if (threadIdx.x == 0) sh[0] = atomicAdd(p.ws, 1u);
+        __syncthreads();
+        const uint32_t ticket = sh[0];
+        if (ticket == 0) pool_header_and_padding(p, D, threadIdx.x);
+        l = ticket / p.wg_per_layer;
+        chunk = ticket % p.wg_per_layer;
+        bidx = chunk * WPB + wib;
+        wave_active = bidx < p.blocks_per_layer;
+    } else {
+        if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
+        const uint64_t wave = (uint64_t)blockIdx.x * WPB + wib;
+        if (wave >= p.n_waves) return;
+        l = (uint32_t)(wave / p.blocks_per_layer);
+        bidx = (uint32_t)(wave % p.blocks_per_layer);
+        chunk = 0;
+        wave_active = true;
+    }
+    const uint32_t h = bidx / p.nb;
+    const uint32_t blk = bidx % p.nb;
+    const uint32_t t0 = blk * kBlockTokens;
+    const uint32_t tok = t0 + (lane >> 2);
     const uint32_t m = lane & 3u;
-    const bool valid = tok < p.T;
-    const uint64_t vec = lh * p.T + tok;
+    const bool valid = wave_active && tok < p.T;
+    const uint32_t nv = wave_active ? ((p.T - t0 < kBlockTokens) ? p.T - t0 : kBlockTokens) : 0;
+    const uint64_t lh = (uint64_t)l * p.H + h;
+    const uint64_t vec0 = lh * p.T + t0;  // first token of the wave
+    const uint64_t vec = vec0 + (lane >> 2);
     const uint64_t elem = vec * D + (uint64_t)m * C;
 
-    // ---- keys: q = rint(x * (127 / m_l)); |x * inv| <= 127 (1 + 2^-23) so
-    // the result never leaves [-127, 127]. Rounding uses x + 1.5*2^23, whose
-    // low byte is the two's-complement integer (ties to even).
-    const float mk = __uint_as_float(p.absmax[l] << 16);
-    const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
+    // ---- keys, first half: load (and in the fused pass, publish the max)
+    uint4 kraw[C / 8];
     if (valid) {
         const uint4* src = reinterpret_cast<const uint4*>(p.k + elem);
-        uint4 raw[C / 8];
 #pragma unroll
-        for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
-        uint32_t out[C / 4];
+        for (int i = 0; i < C / 8; ++i) kraw[i] = src[i];
+    } else {
 #pragma unroll
-        for (int j = 0; j < C / 4; ++j) {
-            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
-            const float q0 = bf16_lo(w0) * inv + 12582912.0f;
-            const float q1 = bf16_hi(w0) * inv + 12582912.0f;
-            const float q2 = bf16_lo(w1) * inv + 12582912.0f;
-            const float q3 = bf16_hi(w1) * inv + 12582912.0f;
-            const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
-            const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
-            out[j] = ab | cd;
-        }
-        uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + elem);
-#pragma unroll
-        for (int i = 0; i < C / 16; ++i)
-            dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+        for (int i = 0; i < C / 8; ++i) kraw[i] = make_uint4(0, 0, 0, 0);
     }
-    if (h == 0 && blk == 0 && lane == 0)
-        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
+    if (FUSED) {
+        const uint32_t r = wave_max_u32(lane_absmax_bits<C / 2>(reinterpret_cast<const uint32_t*>(kraw)));
+        if (lane == 0) sh[1 + wib] = r;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t mx = sh[1];
+#pragma unroll
+            for (int w = 1; w < WPB; ++w) mx = sh[1 + w] > mx ? sh[1 + w] : mx;
+            // flag and value in one word: a single device-coherent store, no
+            // read-modify-write, no ordering to enforce
+            __hip_atomic_store(p.ws + kWsHead + l * p.wg_per_layer + chunk, 0x80000000u | mx, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     // ---- values
     float y[C];
@@ -281,30 +355,119 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
     ss = ss + dpp_xor1(ss);
     ss = ss + dpp_xor2(ss);
     const float rms = __builtin_sqrtf(ss * (1.0f / D));
-    const _Float16 sh = (_Float16)__builtin_fminf(rms, 65504.0f);
-    const float sc = (float)sh;
+    const _Float16 sh16 = (_Float16)__builtin_fminf(rms, 65504.0f);
+    const float sc = (float)sh16;
     const float r = (sc == 0.0f) ? 0.0f : inv_sqrt_d<D>() / sc;
     if (valid && m == 0)
-        reinterpret_cast<uint16_t*>(p.pool + p.lay.v_scale)[vec] = __builtin_bit_cast(uint16_t, sh);
+        reinterpret_cast<uint16_t*>(p.pool + p.lay.v_scale)[vec] = __builtin_bit_cast(uint16_t, sh16);
 
     fwht_quad<C>(y, m);
 
     uint32_t pl[3] = {0, 0, 0};
     code_all<C>(y, r, pl, std::make_integer_sequence<int, C>{});
-    uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
-    if (D == 128) {
-        // lane m owns bytes [4m, 4m+4) of each 16-byte plane
-        if (valid)
+    {
+        // stage the wave's code planes (token t: 3 planes of d/8 bytes)
+        const uint32_t t = lane >> 2;
+        if (D == 128) {
 #pragma unroll
-            for (int q = 0; q < 3; ++q) reinterpret_cast<uint32_t*>(codes + 16 * q)[m] = pl[q];
-    } else {
-        // 16 bits per lane: lanes m and m+1 share one dword of each 8-byte plane
+            for (int q = 0; q < 3; ++q) stg.v[t * 12 + 4 * q + m] = pl[q];
+        } else {
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const uint32_t word = pl[q] | (dpp_xor1_u(pl[q]) << 16);
-            if (valid && (m & 1u) == 0) reinterpret_cast<uint32_t*>(codes + 8 * q)[m >> 1] = word;
+            for (int q = 0; q < 3; ++q) {
+                const uint32_t word = pl[q] | (dpp_xor1_u(pl[q]) << 16);
+                if ((m & 1u) == 0) stg.v[t * 6 + 2 * q + (m >> 1)] = word;
+            }
+        }
+        constexpr int VW = 3 * D / 8 / 4;  // code dwords per token
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.pool + p.lay.v_codes + vec0 * pool_code_bytes(D));
+#pragma unroll
+        for (int j = 0; j < (kBlockTokens * VW + 63) / 64; ++j) {
+            const uint32_t idx = 64 * j + lane;
+            if (idx < kBlockTokens * VW) {
+                const uint32_t wv = stg.v[idx];
+                if (idx / VW < nv) dst[idx] = wv;
+            }
         }
     }
+
+    // ---- keys, second half: the layer's max -> codes
+    uint32_t mbits;
+    if (FUSED) {
+        if (wib == 0) {
+            // wave 0 polls the layer's published words until all are set
+            const uint32_t* res = p.ws + kWsHead + l * p.wg_per_layer;
+            const uint64_t start = wall_clock64();
+            uint32_t mx = 0, timed_out = 0;
+            for (;;) {
+                bool all = true;
+                uint32_t lm = 0;
+                for (uint32_t i = lane; i < p.wg_per_layer; i += kWave) {
+                    const uint32_t v = __hip_atomic_load(res + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && (v & 0x80000000u) != 0;
+                    lm = (v & 0x7FFFu) > lm ? (v & 0x7FFFu) : lm;
+                }
+                if (__builtin_amdgcn_ballot_w64(!all) == 0) {
+                    mx = wave_max_u32(lm);
+                    break;
+                }
+                if (wall_clock64() - start > kWaitTicks) {
+                    timed_out = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            if (lane == 0) {
+                sh[5] = mx;
+                sh[6] = timed_out;
+            }
+        }
+        __syncthreads();
+        mbits = sh[5];
+        if (threadIdx.x == 0 && sh[6]) {
+            // never expected: mark the pool invalid (decode reports a bad header)
+            atomicOr(p.ws + 1, 1u);
+            reinterpret_cast<uint32_t*>(p.pool)[0] = 0;
+        }
+    } else {
+        mbits = 0;
+#pragma unroll
+        for (uint32_t s = 0; s < kSlots; ++s) {
+            const uint32_t v = *absmax_slot(p.ws, l, s);
+            mbits = v > mbits ? v : mbits;
+        }
+    }
+    // q = rint(x * (127 / m_l)); |x * inv| <= 127 (1 + 2^-23), so the result
+    // never leaves [-127, 127]. Rounding adds 1.5*2^23: the low byte of the
+    // sum is the two's-complement integer (ties to even).
+    const float mk = __uint_as_float(mbits << 16);
+    const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
+    {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
+        uint32_t out[C / 4];
+#pragma unroll
+        for (int j = 0; j < C / 4; ++j) {
+            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+            const float q0 = bf16_lo(w0) * inv + 12582912.0f;
+            const float q1 = bf16_hi(w0) * inv + 12582912.0f;
+            const float q2 = bf16_lo(w1) * inv + 12582912.0f;
+            const float q3 = bf16_hi(w1) * inv + 12582912.0f;
+            const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
+            const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
+            out[j] = ab | cd;
+        }
+        constexpr int KC = C / 16;  // 16-byte chunks of codes per lane
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            stg.k[lane * KC + c] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
+        uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + vec0 * D);
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const uint4 chunk16 = stg.k[64 * j + lane];
+            if ((64 * j + lane) / (D / 16) < nv) dst[64 * j + lane] = chunk16;
+        }
+    }
+    if (wave_active && bidx == 0 && lane == 0)
+        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
 }
 
 template <int D>
@@ -423,14 +586,13 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     for (int j = 0; j < CH; ++j) vc[j] = st[64 * j + lane];
 
     // chunk 64*j + lane of the image belongs to token (64*j + lane) / (4*CH)
-    for (uint32_t ag = 0; ag < p.n_out; ++ag) {
-        uint4* dk = reinterpret_cast<uint4*>(p.k_out[ag]) + out_base;
-        uint4* dv = reinterpret_cast<uint4*>(p.v_out[ag]) + out_base;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            if ((64 * j + lane) / (4 * CH) < nv) {
-                dk[64 * j + lane] = kc[j];
-                dv[64 * j + lane] = vc[j];
+    for (int j = 0; j < CH; ++j) {
+        if ((64 * j + lane) / (4 * CH) < nv) {
+            const uint4 kj = kc[j], vj = vc[j];
+            for (uint32_t ag = 0; ag < p.n_out; ++ag) {
+                (reinterpret_cast<uint4*>(p.k_out[ag]) + out_base)[64 * j + lane] = kj;
+                (reinterpret_cast<uint4*>(p.v_out[ag]) + out_base)[64 * j + lane] = vj;
             }
         }
     }
@@ -444,25 +606,48 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
     p.pool = static_cast<uint8_t*>(pool);
-    p.absmax = ws;
+    p.ws = ws;
     p.L = s.L;
     p.H = s.H;
     p.T = s.T;
     p.nb = pool_blocks_per_head(s.T);
-    p.n_waves = (uint64_t)s.L * s.H * p.nb;
+    p.blocks_per_layer = s.H * p.nb;
+    p.wg_per_layer = encode_workgroups_per_layer(s.H, s.T);
+    p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
-    hipError_t e = launch_kernel(fill_zero_kernel, dim3((s.L + 255) / 256), dim3(256), stream, ws, s.L);
+    // Two passes (key max reduction, then the fused encode). The single-pass
+    // kernel is kept behind KVC_ENCODE_SINGLE_PASS: with ordinary dispatch
+    // its per-layer wait can starve (each XCD only dispatches its own share
+    // of the grid), which its timeout turns into an invalid pool.
+    auto fused_kernel = s.d == 64 ? pool_encode_kernel<64, true> : pool_encode_kernel<128, true>;
+    bool fused = getenv("KVC_ENCODE_SINGLE_PASS") != nullptr;
+    if (fused) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fused_kernel),
+                                                         kBlockThreads, 0) != hipSuccess)
+            fused = false;
+        else
+            fused = 2ull * p.wg_per_layer <= (uint64_t)cus * (uint64_t)per_cu;
+    }
+
+    const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L, s.H, s.T);
+    hipError_t e = launch_kernel(fill_zero_kernel, dim3((ws_words + 255) / 256), dim3(256), stream, ws, ws_words);
     if (e != hipSuccess) return e;
+    if (fused)
+        return launch_kernel(fused_kernel, dim3(p.wg_per_layer * s.L), dim3(kBlockThreads), stream, p);
+
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
-    uint64_t gx = (per_layer_u4 + 4 * kBlockThreads - 1) / (4 * kBlockThreads);
-    if (gx > 1024) gx = 1024;
+    uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
+    if (gx > 64) gx = 64;
     e = launch_kernel(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), stream,
                       static_cast<const uint4*>(k), per_layer_u4, ws);
     if (e != hipSuccess) return e;
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>, dim3((uint32_t)nblocks),
-                         dim3(kBlockThreads), stream, p);
+    return launch_kernel(s.d == 64 ? pool_encode_kernel<64, false> : pool_encode_kernel<128, false>,
+                         dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,

@@ -87,6 +87,7 @@ def main():
     v_rt = torch.empty_like(v)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    torch.cuda.synchronize()  # inputs and buffers ready before the codec stream starts
     stream = torch.cuda.Stream()
     ops = ["encode", "decode", "pack", "unpack"]
 

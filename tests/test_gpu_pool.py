@@ -161,3 +161,34 @@ def test_full_size_workload_bit_exact(cfg):
     rk, rv = oracle.pool_decode(ref_pool, w.shape)
     n1 = assert_decode_close(to_host(ko[0]), rk, "K") + assert_decode_close(to_host(vo[0]), rv, "V")
     say("  values at 1 ulp:", n1, "of", 2 * k.size)
+
+
+@pytest.mark.parametrize("shape,cfg", [((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2), ((5, 2, 77, 128), 5)])
+def test_single_pass_and_two_pass_encodes_agree(shape, cfg, monkeypatch):
+    """The single-pass encode (keys held in registers across a per-layer
+    wait) and the two-pass encode (separate max reduction) write the same
+    bytes, equal to the oracle's."""
+    k, v = _inputs(shape, cfg, 4)
+    ref = oracle.pool_encode(k, v)
+    two = gpu_encode(shape, k, v).cpu().numpy()
+    monkeypatch.setenv("KVC_ENCODE_SINGLE_PASS", "1")
+    one = gpu_encode(shape, k, v).cpu().numpy()
+    assert_pool_equal(one, ref, shape)
+    assert_pool_equal(two, ref, shape)
+
+
+def test_two_concurrent_encodes():
+    shape = (4, 8, 1024, 128)
+    k, v = _inputs(shape, 3, 5)
+    ref = oracle.pool_encode(k, v)
+    kd, vd = to_dev(k), to_dev(v)
+    outs = []
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for s in streams:
+        pool = dev_bytes(kv.kvpool_bytes(shape), fill=0)
+        ws = dev_bytes(kv.kvpool_workspace_bytes(shape))
+        kv.kvpool_encode(shape, kd, vd, pool, ws, stream=s)
+        outs.append(pool)
+    torch.cuda.synchronize()
+    for pool in outs:
+        assert_pool_equal(pool.cpu().numpy(), ref, shape)
