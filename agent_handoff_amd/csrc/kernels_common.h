@@ -73,6 +73,32 @@ __device__ __forceinline__ uint64_t shift_out_bit(uint32_t& w) {
     return mask;
 }
 
+// Cross-lane butterfly step on 8 registers in one instruction each:
+// y[i] <- partner(y[i]) * s + y[i] with the partner read through DPP
+// (v_fmac_f32 with a DPP source). With s = -1 this yields own - partner,
+// the negation of the butterfly's partner - own; callers track that sign
+// per lane. The leading s_nop covers the DPP read-after-VALU-write hazard
+// for registers written just before the block; within the block no
+// register is read through DPP within two instructions of its write.
+#define KVC_FMAC_DPP8(NAME, PERM)                                                                     \
+    __device__ __forceinline__ void NAME(float* y, float s) {                                         \
+        asm("s_nop 1\n"                                                                               \
+            "v_fmac_f32_dpp %0, %0, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %1, %1, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %2, %2, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %3, %3, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %4, %4, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %5, %5, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %6, %6, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n"               \
+            "v_fmac_f32_dpp %7, %7, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf"                  \
+            : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]),   \
+              "+v"(y[7])                                                                              \
+            : "v"(s));                                                                                \
+    }
+KVC_FMAC_DPP8(fmac_dpp8_xor1, "[1,0,3,2]")
+KVC_FMAC_DPP8(fmac_dpp8_xor2, "[2,3,0,1]")
+#undef KVC_FMAC_DPP8
+
 // Launch and return this launch's own status (hipGetLastError would also
 // report errors left behind by unrelated earlier runtime calls).
 // With KVC_DEBUG set in the environment a failing launch prints the HIP

@@ -59,7 +59,7 @@ size_t kvpool_bytes(const kvc_shape* shape) {
 size_t kvpool_workspace_bytes(const kvc_shape* shape) {
     if (!pool_shape(shape)) return 0;
     return (size_t)align_up(
-        4ull * kvc::encode_workspace_words(shape->num_layers, shape->num_kv_heads, shape->num_tokens), 256);
+        4ull * kvc::encode_workspace_words(shape->num_layers), 256);
 }
 
 int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool, size_t pool_bytes,

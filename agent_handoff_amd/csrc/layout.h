@@ -47,16 +47,9 @@ KVC_HD PoolLayout pool_layout(uint32_t L, uint32_t H, uint32_t T, uint32_t d) {
     return p;
 }
 
-// kvpool_encode workspace: 64 control words, then the larger of one word per
-// encode workgroup (4 blocks of 16 tokens each) and 16 partial-max slots of
-// 32 words per layer.
-KVC_HD uint32_t encode_workgroups_per_layer(uint32_t H, uint32_t T) {
-    return (H * ((T + kBlockTokens - 1) / kBlockTokens) + 3u) / 4u;
-}
-KVC_HD uint64_t encode_workspace_words(uint32_t L, uint32_t H, uint32_t T) {
-    const uint64_t a = (uint64_t)L * encode_workgroups_per_layer(H, T), b = (uint64_t)L * 16u * 32u;
-    return 64u + (a > b ? a : b);
-}
+// kvpool_encode workspace: 64 reserved words, then per layer 16 partial-max
+// slots, 32 words apart.
+KVC_HD uint64_t encode_workspace_words(uint32_t L) { return 64u + (uint64_t)L * 16u * 32u; }
 
 KVC_HD bool card_shape_ok(uint32_t L, uint32_t H, uint32_t T, uint32_t d) {
     return L >= 1 && H >= 1 && T >= 1 && (d == 64 || d == 128) && L <= (1u << 16) &&

@@ -52,16 +52,13 @@ struct EncodeParams {
     uint32_t* ws;           // workspace, see the slot helpers below
     uint32_t L, H, T, nb;   // nb = 16-token blocks per head
     uint32_t blocks_per_layer;  // H * nb
-    uint32_t wg_per_layer;      // workgroups per layer (4 blocks each)
     uint64_t n_waves;           // L * H * nb
     PoolLayout lay;
 };
 
-// Encode workspace (u32 words): [0] workgroup ticket, [1] timeout flag, then
-//  - single pass: one word per workgroup, L x wg_per_layer, holding
-//    0x80000000 | the workgroup's key max once published;
-//  - two passes: per layer kSlots partial maxima, each on its own 128-byte
-//    line so that concurrent atomics spread over addresses.
+// Encode workspace (u32 words): 64 reserved words, then per layer kSlots
+// partial key maxima, each on its own 128-byte line so that concurrent
+// atomics spread over addresses.
 constexpr uint32_t kSlots = 16;
 constexpr uint32_t kSlotStride = 32;  // words
 constexpr uint32_t kWsHead = 64;      // words
@@ -85,7 +82,13 @@ struct DecodeParams {
 
 // Unnormalised Walsh-Hadamard transform of d = 4*C values spread over the
 // quad (C per lane, lane m holds block m): stages h = 1 .. C/2 in the lane,
-// then h = C (partner lane m^1) and h = 2C (partner lane m^2).
+// then h = C (partner lane m^1) and h = 2C (partner lane m^2), each
+// cross-lane step one v_fmac with a DPP source: stored = own + s * partner.
+// Lanes whose butterfly output is partner - own get own - partner instead,
+// so after both steps lane m holds sign_m * (the transform) with
+// sign_m = (-1)^popcount(m); the caller folds sign_m into its scale. Every
+// non-zero value is exactly +-(the ascending-order binary32 butterfly's
+// value) since rounding to nearest is symmetric; zeros may differ in sign.
 template <int C>
 __device__ __forceinline__ void fwht_quad(float (&y)[C], uint32_t m) {
 #pragma unroll
@@ -100,13 +103,20 @@ __device__ __forceinline__ void fwht_quad(float (&y)[C], uint32_t m) {
             }
         }
     }
-    // lower partner: own + partner; upper partner: partner - own
     const float s1 = (m & 1u) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int j = 0; j < C; ++j) y[j] = __builtin_fmaf(y[j], s1, dpp_xor1(y[j]));
+    for (int j = 0; j < C; j += 8) fmac_dpp8_xor1(y + j, s1);
+    // after the first step lane m carries sign (-1)^(m&1); the second step's
+    // multiplier sign_own * sign_partner (lower half) or its negation (upper
+    // half) works out to -1 exactly on the upper half
     const float s2 = (m & 2u) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int j = 0; j < C; ++j) y[j] = __builtin_fmaf(y[j], s2, dpp_xor2(y[j]));
+    for (int j = 0; j < C; j += 8) fmac_dpp8_xor2(y + j, s2);
+}
+
+// Sign (+1 / -1) that fwht_quad leaves on lane m's outputs.
+__device__ __forceinline__ float fwht_quad_sign(uint32_t m) {
+    return (__builtin_popcount(m & 3u) & 1) ? -1.0f : 1.0f;
 }
 
 // Header (64 B) and every padding byte of the pool; run by workgroup 0.
@@ -158,26 +168,26 @@ __global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* 
     const uint32_t l = blockIdx.y;
     const uint4* src = k + (uint64_t)l * per_layer_u4;
     us2 mx = {0, 0};
+    // kUnroll independent 16-byte loads in flight per thread
+    constexpr uint32_t kUnroll = 8;
     const uint64_t stride = (uint64_t)gridDim.x * kBlockThreads;
-    uint64_t i = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-    for (; i + 3 * stride < per_layer_u4; i += 4 * stride) {
-        uint4 w[4];
+    for (uint64_t i0 = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x; i0 < per_layer_u4;
+         i0 += kUnroll * stride) {
+        // past the end, re-load the last element: max is idempotent, and the
+        // loads stay unconditional (no branch between them)
+        uint4 w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].x & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].y & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].z & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[u].w & 0x7FFF7FFFu));
+        for (uint32_t j = 0; j < kUnroll; ++j) {
+            const uint64_t i = i0 + j * stride;
+            w[j] = src[i < per_layer_u4 ? i : per_layer_u4 - 1];
         }
-    }
-    for (; i < per_layer_u4; i += stride) {
-        const uint4 w = src[i];
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.x & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.y & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.z & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w.w & 0x7FFF7FFFu));
+#pragma unroll
+        for (uint32_t j = 0; j < kUnroll; ++j) {
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].x & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].y & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].z & 0x7FFF7FFFu));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].w & 0x7FFF7FFFu));
+        }
     }
     uint32_t r = mx.x > mx.y ? mx.x : mx.y;
 #pragma unroll
@@ -227,121 +237,53 @@ struct EncodeStage {
     uint32_t v[kBlockTokens * 3 * D / 32];
 };
 
-// Largest bf16 magnitude (as bits) of a lane's packed words.
-template <int N>
-__device__ __forceinline__ uint32_t lane_absmax_bits(const uint32_t* w) {
-    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-    us2 mx = {0, 0};
-#pragma unroll
-    for (int j = 0; j < N; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j] & 0x7FFF7FFFu));
-    return mx.x > mx.y ? mx.x : mx.y;
+// Geometry of one wave's block: 16 tokens of one (layer, head).
+struct BlockPos {
+    uint32_t l, bidx, m, nv;  // layer, block within the layer, lane's quarter, valid tokens
+    uint64_t vec0, vec;       // first token of the block, this lane's token
+    uint64_t elem;            // element offset this lane loads from
+    bool valid;               // this lane's token exists
+};
+
+template <int D>
+__device__ __forceinline__ BlockPos block_pos(const EncodeParams& p, uint32_t l, uint32_t bidx, uint32_t lane) {
+    BlockPos b;
+    b.l = l;
+    b.bidx = bidx;
+    b.m = lane & 3u;
+    const uint32_t h = bidx / p.nb, t0 = (bidx % p.nb) * kBlockTokens;
+    b.nv = (p.T - t0 < kBlockTokens) ? p.T - t0 : kBlockTokens;
+    b.vec0 = ((uint64_t)l * p.H + h) * p.T + t0;
+    b.vec = b.vec0 + (lane >> 2);
+    b.valid = t0 + (lane >> 2) < p.T;
+    // lanes past the end of the tokens load the block's first vector and are
+    // masked at the key max and at every store
+    b.elem = (b.valid ? b.vec : b.vec0) * D + (uint64_t)b.m * (D / 4);
+    return b;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
+template <int D>
+__device__ __forceinline__ void load_lane(const uint16_t* base, uint64_t elem, uint4 (&raw)[D / 32]) {
+    const uint4* src = reinterpret_cast<const uint4*>(base + elem);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
-        r = t > r ? t : r;
-    }
-    return r;
+    for (int i = 0; i < D / 32; ++i) raw[i] = src[i];
 }
 
-// Spin limit of the fused encode's per-layer wait, in ticks of the 100 MHz
-// constant clock: 0.5 s, far beyond any legitimate wait.
-constexpr uint64_t kWaitTicks = 50000000ull;
-
-// FUSED: one pass over K. Workgroups take tickets in start order, so every
-// workgroup of layer l has started before any of layer l+1; the host uses
-// this path only when one layer's workgroups fit on the GPU twice over, so
-// the per-layer wait always completes. Each workgroup keeps its K chunk in
-// registers, publishes its partial max, encodes its V chunk while the other
-// workgroups of the layer arrive, then quantises K from registers. The wait
-// is bounded: after 0.5 s (never expected) the pool is marked invalid
-// instead of hanging.
-// !FUSED: the per-layer maxima were reduced by key_absmax_kernel.
-template <int D, bool FUSED>
-__global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams p) {
+// Values of one block: RMS scale, rotation, 3-bit codes; writes the scales
+// and the code planes (PolyKV 2.B item 2).
+template <int D>
+__device__ __forceinline__ void encode_values(const EncodeParams& p, const BlockPos& b, const uint4 (&vraw)[D / 32],
+                                              EncodeStage<D>& stg, uint32_t lane) {
     constexpr int C = D / 4;  // channels per lane
-    constexpr int WPB = kBlockThreads / kWave;
-    __shared__ uint32_t sh[8];
-    __shared__ EncodeStage<D> stage_all[WPB];
-    const uint32_t lane = lane_id();
-    const uint32_t wib = wave_uniform(threadIdx.x / kWave);
-    EncodeStage<D>& stg = stage_all[wib];
-
-    uint32_t l, bidx, chunk;
-    bool wave_active;
-    if (FUSED) {
-        if (threadIdx.x == 0) sh[0] = atomicAdd(p.ws, 1u);
-        __syncthreads();
-        const uint32_t ticket = sh[0];
-        if (ticket == 0) pool_header_and_padding(p, D, threadIdx.x);
-        l = ticket / p.wg_per_layer;
-        chunk = ticket % p.wg_per_layer;
-        bidx = chunk * WPB + wib;
-        wave_active = bidx < p.blocks_per_layer;
-    } else {
-        if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
-        const uint64_t wave = (uint64_t)blockIdx.x * WPB + wib;
-        if (wave >= p.n_waves) return;
-        l = (uint32_t)(wave / p.blocks_per_layer);
-        bidx = (uint32_t)(wave % p.blocks_per_layer);
-        chunk = 0;
-        wave_active = true;
-    }
-    const uint32_t h = bidx / p.nb;
-    const uint32_t blk = bidx % p.nb;
-    const uint32_t t0 = blk * kBlockTokens;
-    const uint32_t tok = t0 + (lane >> 2);
-    const uint32_t m = lane & 3u;
-    const bool valid = wave_active && tok < p.T;
-    const uint32_t nv = wave_active ? ((p.T - t0 < kBlockTokens) ? p.T - t0 : kBlockTokens) : 0;
-    const uint64_t lh = (uint64_t)l * p.H + h;
-    const uint64_t vec0 = lh * p.T + t0;  // first token of the wave
-    const uint64_t vec = vec0 + (lane >> 2);
-    const uint64_t elem = vec * D + (uint64_t)m * C;
-
-    // ---- keys, first half: load (and in the fused pass, publish the max)
-    uint4 kraw[C / 8];
-    if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.k + elem);
-#pragma unroll
-        for (int i = 0; i < C / 8; ++i) kraw[i] = src[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < C / 8; ++i) kraw[i] = make_uint4(0, 0, 0, 0);
-    }
-    if (FUSED) {
-        const uint32_t r = wave_max_u32(lane_absmax_bits<C / 2>(reinterpret_cast<const uint32_t*>(kraw)));
-        if (lane == 0) sh[1 + wib] = r;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t mx = sh[1];
-#pragma unroll
-            for (int w = 1; w < WPB; ++w) mx = sh[1 + w] > mx ? sh[1 + w] : mx;
-            // flag and value in one word: a single device-coherent store, no
-            // read-modify-write, no ordering to enforce
-            __hip_atomic_store(p.ws + kWsHead + l * p.wg_per_layer + chunk, 0x80000000u | mx, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
-    // ---- values
+    const uint32_t m = b.m;
     float y[C];
-    if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.v + elem);
-        uint4 raw[C / 8];
-#pragma unroll
-        for (int i = 0; i < C / 8; ++i) raw[i] = src[i];
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+    {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(vraw);
 #pragma unroll
         for (int j = 0; j < C / 2; ++j) {
             y[2 * j] = bf16_lo(w[j]);
             y[2 * j + 1] = bf16_hi(w[j]);
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < C; ++j) y[j] = 0.0f;
     }
     // sum of squares: pairwise tree, left to right, lanes in block order
     float sq[C];
@@ -357,117 +299,101 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
     const float rms = __builtin_sqrtf(ss * (1.0f / D));
     const _Float16 sh16 = (_Float16)__builtin_fminf(rms, 65504.0f);
     const float sc = (float)sh16;
-    const float r = (sc == 0.0f) ? 0.0f : inv_sqrt_d<D>() / sc;
-    if (valid && m == 0)
-        reinterpret_cast<uint16_t*>(p.pool + p.lay.v_scale)[vec] = __builtin_bit_cast(uint16_t, sh16);
+    // scale, with the sign fwht_quad leaves on this lane folded in
+    const float r = ((sc == 0.0f) ? 0.0f : inv_sqrt_d<D>() / sc) * fwht_quad_sign(m);
+    if (b.valid && m == 0)
+        reinterpret_cast<uint16_t*>(p.pool + p.lay.v_scale)[b.vec] = __builtin_bit_cast(uint16_t, sh16);
 
     fwht_quad<C>(y, m);
 
     uint32_t pl[3] = {0, 0, 0};
     code_all<C>(y, r, pl, std::make_integer_sequence<int, C>{});
-    {
-        // stage the wave's code planes (token t: 3 planes of d/8 bytes)
-        const uint32_t t = lane >> 2;
-        if (D == 128) {
+    // stage the wave's code planes (token t: 3 planes of d/8 bytes), then
+    // store them with each instruction covering a contiguous span
+    const uint32_t t = lane >> 2;
+    if (D == 128) {
 #pragma unroll
-            for (int q = 0; q < 3; ++q) stg.v[t * 12 + 4 * q + m] = pl[q];
-        } else {
-#pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const uint32_t word = pl[q] | (dpp_xor1_u(pl[q]) << 16);
-                if ((m & 1u) == 0) stg.v[t * 6 + 2 * q + (m >> 1)] = word;
-            }
-        }
-        constexpr int VW = 3 * D / 8 / 4;  // code dwords per token
-        uint32_t* dst = reinterpret_cast<uint32_t*>(p.pool + p.lay.v_codes + vec0 * pool_code_bytes(D));
-#pragma unroll
-        for (int j = 0; j < (kBlockTokens * VW + 63) / 64; ++j) {
-            const uint32_t idx = 64 * j + lane;
-            if (idx < kBlockTokens * VW) {
-                const uint32_t wv = stg.v[idx];
-                if (idx / VW < nv) dst[idx] = wv;
-            }
-        }
-    }
-
-    // ---- keys, second half: the layer's max -> codes
-    uint32_t mbits;
-    if (FUSED) {
-        if (wib == 0) {
-            // wave 0 polls the layer's published words until all are set
-            const uint32_t* res = p.ws + kWsHead + l * p.wg_per_layer;
-            const uint64_t start = wall_clock64();
-            uint32_t mx = 0, timed_out = 0;
-            for (;;) {
-                bool all = true;
-                uint32_t lm = 0;
-                for (uint32_t i = lane; i < p.wg_per_layer; i += kWave) {
-                    const uint32_t v = __hip_atomic_load(res + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    all = all && (v & 0x80000000u) != 0;
-                    lm = (v & 0x7FFFu) > lm ? (v & 0x7FFFu) : lm;
-                }
-                if (__builtin_amdgcn_ballot_w64(!all) == 0) {
-                    mx = wave_max_u32(lm);
-                    break;
-                }
-                if (wall_clock64() - start > kWaitTicks) {
-                    timed_out = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
-            }
-            if (lane == 0) {
-                sh[5] = mx;
-                sh[6] = timed_out;
-            }
-        }
-        __syncthreads();
-        mbits = sh[5];
-        if (threadIdx.x == 0 && sh[6]) {
-            // never expected: mark the pool invalid (decode reports a bad header)
-            atomicOr(p.ws + 1, 1u);
-            reinterpret_cast<uint32_t*>(p.pool)[0] = 0;
-        }
+        for (int q = 0; q < 3; ++q) stg.v[t * 12 + 4 * q + m] = pl[q];
     } else {
-        mbits = 0;
 #pragma unroll
-        for (uint32_t s = 0; s < kSlots; ++s) {
-            const uint32_t v = *absmax_slot(p.ws, l, s);
-            mbits = v > mbits ? v : mbits;
+        for (int q = 0; q < 3; ++q) {
+            const uint32_t word = pl[q] | (dpp_xor1_u(pl[q]) << 16);
+            if ((m & 1u) == 0) stg.v[t * 6 + 2 * q + (m >> 1)] = word;
         }
     }
-    // q = rint(x * (127 / m_l)); |x * inv| <= 127 (1 + 2^-23), so the result
-    // never leaves [-127, 127]. Rounding adds 1.5*2^23: the low byte of the
-    // sum is the two's-complement integer (ties to even).
+    constexpr int VW = 3 * D / 8 / 4;  // code dwords per token
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.pool + p.lay.v_codes + b.vec0 * pool_code_bytes(D));
+#pragma unroll
+    for (int j = 0; j < (kBlockTokens * VW + 63) / 64; ++j) {
+        const uint32_t idx = 64 * j + lane;
+        if (idx < kBlockTokens * VW) {
+            const uint32_t wv = stg.v[idx];
+            if (idx / VW < b.nv) dst[idx] = wv;
+        }
+    }
+}
+
+// Keys of one block given the layer's max m (as bf16 magnitude bits)
+// (PolyKV 2.B item 1): q = rint(x * (127 / m)). |x * inv| <= 127 (1 + 2^-23),
+// so q never leaves [-127, 127]. Rounding adds 1.5*2^23: the low byte of the
+// sum is the two's-complement integer (ties to even).
+template <int D>
+__device__ __forceinline__ void quantize_keys(const EncodeParams& p, const BlockPos& b, const uint4 (&kraw)[D / 32],
+                                              uint32_t mbits, EncodeStage<D>& stg, uint32_t lane) {
+    constexpr int C = D / 4;
     const float mk = __uint_as_float(mbits << 16);
     const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
-    {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
-        uint32_t out[C / 4];
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
+    uint32_t out[C / 4];
 #pragma unroll
-        for (int j = 0; j < C / 4; ++j) {
-            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
-            const float q0 = bf16_lo(w0) * inv + 12582912.0f;
-            const float q1 = bf16_hi(w0) * inv + 12582912.0f;
-            const float q2 = bf16_lo(w1) * inv + 12582912.0f;
-            const float q3 = bf16_hi(w1) * inv + 12582912.0f;
-            const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
-            const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
-            out[j] = ab | cd;
-        }
-        constexpr int KC = C / 16;  // 16-byte chunks of codes per lane
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            stg.k[lane * KC + c] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
-        uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + vec0 * D);
-#pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            const uint4 chunk16 = stg.k[64 * j + lane];
-            if ((64 * j + lane) / (D / 16) < nv) dst[64 * j + lane] = chunk16;
-        }
+    for (int j = 0; j < C / 4; ++j) {
+        const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+        const float q0 = bf16_lo(w0) * inv + 12582912.0f;
+        const float q1 = bf16_hi(w0) * inv + 12582912.0f;
+        const float q2 = bf16_lo(w1) * inv + 12582912.0f;
+        const float q3 = bf16_hi(w1) * inv + 12582912.0f;
+        const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
+        const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
+        out[j] = ab | cd;
     }
-    if (wave_active && bidx == 0 && lane == 0)
-        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
+    constexpr int KC = C / 16;  // 16-byte chunks of codes per lane
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+        stg.k[lane * KC + c] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
+    uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + b.vec0 * D);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+        const uint4 chunk16 = stg.k[64 * j + lane];
+        if ((64 * j + lane) / (D / 16) < b.nv) dst[64 * j + lane] = chunk16;
+    }
+    if (b.bidx == 0 && lane == 0)
+        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[b.l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
+}
+
+// Two passes: the per-layer key maxima were reduced by key_absmax_kernel;
+// one wave per 16-token block.
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams p) {
+    constexpr int WPB = kBlockThreads / kWave;
+    __shared__ EncodeStage<D> stage_all[WPB];
+    const uint32_t lane = lane_id();
+    const uint32_t wib = wave_uniform(threadIdx.x / kWave);
+    if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
+    const uint64_t wave = (uint64_t)blockIdx.x * WPB + wib;
+    if (wave >= p.n_waves) return;
+    const BlockPos b = block_pos<D>(p, (uint32_t)(wave / p.blocks_per_layer), (uint32_t)(wave % p.blocks_per_layer),
+                                    lane);
+    uint4 kraw[D / 32], vraw[D / 32];
+    load_lane<D>(p.k, b.elem, kraw);
+    load_lane<D>(p.v, b.elem, vraw);
+    encode_values<D>(p, b, vraw, stage_all[wib], lane);
+    uint32_t mbits = 0;
+#pragma unroll
+    for (uint32_t s = 0; s < kSlots; ++s) {
+        const uint32_t v = *absmax_slot(p.ws, b.l, s);
+        mbits = v > mbits ? v : mbits;
+    }
+    quantize_keys<D>(p, b, kraw, mbits, stage_all[wib], lane);
 }
 
 template <int D>
@@ -574,7 +500,7 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     }
     fwht_quad<C>(y, m);
     {
-        const float a = (float)__builtin_bit_cast(_Float16, sbits) * inv_sqrt_d<D>();
+        const float a = (float)__builtin_bit_cast(_Float16, sbits) * inv_sqrt_d<D>() * fwht_quad_sign(m);
         uint32_t o[C / 2];
 #pragma unroll
         for (int j = 0; j < C / 2; ++j) o[j] = pack_bf16x2(y[2 * j] * a, y[2 * j + 1] * a);
@@ -585,7 +511,9 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
 #pragma unroll
     for (int j = 0; j < CH; ++j) vc[j] = st[64 * j + lane];
 
-    // chunk 64*j + lane of the image belongs to token (64*j + lane) / (4*CH)
+    // chunk 64*j + lane of the image belongs to token (64*j + lane) / (4*CH).
+    // (Writing each agent's spans back to back instead of interleaving the
+    // agents per chunk measured about 1% slower.)
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         if ((64 * j + lane) / (4 * CH) < nv) {
@@ -612,33 +540,14 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.T = s.T;
     p.nb = pool_blocks_per_head(s.T);
     p.blocks_per_layer = s.H * p.nb;
-    p.wg_per_layer = encode_workgroups_per_layer(s.H, s.T);
     p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
-    // Two passes (key max reduction, then the fused encode). The single-pass
-    // kernel is kept behind KVC_ENCODE_SINGLE_PASS: with ordinary dispatch
-    // its per-layer wait can starve (each XCD only dispatches its own share
-    // of the grid), which its timeout turns into an invalid pool.
-    auto fused_kernel = s.d == 64 ? pool_encode_kernel<64, true> : pool_encode_kernel<128, true>;
-    bool fused = getenv("KVC_ENCODE_SINGLE_PASS") != nullptr;
-    if (fused) {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fused_kernel),
-                                                         kBlockThreads, 0) != hipSuccess)
-            fused = false;
-        else
-            fused = 2ull * p.wg_per_layer <= (uint64_t)cus * (uint64_t)per_cu;
-    }
-
-    const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L, s.H, s.T);
+    // Two passes: the per-layer key maxima, then the encode proper (the
+    // first needs every key of a layer before any key code can be written).
+    const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L);
     hipError_t e = launch_kernel(fill_zero_kernel, dim3((ws_words + 255) / 256), dim3(256), stream, ws, ws_words);
     if (e != hipSuccess) return e;
-    if (fused)
-        return launch_kernel(fused_kernel, dim3(p.wg_per_layer * s.L), dim3(kBlockThreads), stream, p);
-
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
     uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
     if (gx > 64) gx = 64;
@@ -646,7 +555,7 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
                       static_cast<const uint4*>(k), per_layer_u4, ws);
     if (e != hipSuccess) return e;
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    return launch_kernel(s.d == 64 ? pool_encode_kernel<64, false> : pool_encode_kernel<128, false>,
+    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>,
                          dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
 }
 
