@@ -15,9 +15,10 @@
 //
 // Work mapping: one lane per 32-channel group (d/32 lanes per token, so 16
 // tokens per wave at d = 128); a lane loads its 64 input bytes, finds the
-// group's min and max in registers, and writes its scale, minimum and codes.
-// All lanes of a token share its width, so a wave branches once per distinct
-// width it holds (widths come in runs).
+// group's min and max in registers, and places its scale, minimum and codes
+// in the wave's LDS image of its records, which the wave then stores as one
+// contiguous span. All lanes of a token share its width, so a wave branches
+// once per distinct width it holds (widths come in runs).
 #include "kernels_common.h"
 #include "launch.h"
 #include "layout.h"
@@ -202,62 +203,83 @@ __device__ __forceinline__ void store_group(uint8_t* rec, uint32_t G, uint32_t g
     for (int i = 0; i < B / 2; ++i) dst[i] = make_uint2(codes[2 * i], codes[2 * i + 1]);
 }
 
+// Per-wave LDS image of the wave's records: its tokens are consecutive, so
+// their records form one contiguous span of the stream (at most TPW records
+// of at most 2d bytes: 4 KiB), 16-byte aligned at both ends.
+constexpr uint32_t kSpanChunks = 256;  // 16-byte chunks
+
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) {
     constexpr uint32_t G = D / kCardGroup;  // lanes per token
     constexpr uint32_t TPW = kWave / G;     // tokens per wave
+    static_assert(TPW * 2 * D <= 16 * kSpanChunks, "span exceeds the stage");
     const uint32_t lane = lane_id();
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
     if (p.info[2] != 0) return;
     const uint64_t S = p.info[0];
     const uint64_t s = wave / p.nbk;
-    const uint32_t b = (uint32_t)(wave % p.nbk);
-    const uint32_t tok = b * TPW + lane / G;
+    const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
+    const uint32_t tok = t0 + lane / G;
     const uint32_t g = lane % G;
-    if (tok >= p.T) return;
+    const bool valid = tok < p.T;
+    const uint32_t nv = (p.T - t0 < TPW) ? p.T - t0 : TPW;
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
-    const uint16_t* src = (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
-    const uint32_t width = p.widths[tok];
     uint8_t* stream = p.card + p.payload + s * S;
-    uint8_t* rec = stream + p.off[tok];
+    const uint64_t span0 = p.off[t0], span1 = p.off[t0 + nv];
 
-    uint4 raw[4];
+    __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
+    uint8_t* st = reinterpret_cast<uint8_t*>(stage[threadIdx.x / kWave]);
+    if (valid) {
+        const uint16_t* src = (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
+        const uint32_t width = p.widths[tok];
+        uint8_t* rec = st + (uint32_t)(p.off[tok] - span0);
+        uint4 raw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
-    if (width == 16) {
+        for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+        if (width == 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rec + 64 * g)[i] = raw[i];
-    } else {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
-        float x[32];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            x[2 * j] = bf16_lo(w[j]);
-            x[2 * j + 1] = bf16_hi(w[j]);
-        }
-        uint16_t sb, mb;
-        uint32_t codes[8];
-        if (width == 2) {
-            quant_group<2>(x, sb, mb, codes);
-            store_group<2>(rec, G, g, sb, mb, codes);
-        } else if (width == 4) {
-            quant_group<4>(x, sb, mb, codes);
-            store_group<4>(rec, G, g, sb, mb, codes);
+            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rec + 64 * g)[i] = raw[i];
         } else {
-            quant_group<8>(x, sb, mb, codes);
-            store_group<8>(rec, G, g, sb, mb, codes);
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+            float x[32];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                x[2 * j] = bf16_lo(w[j]);
+                x[2 * j + 1] = bf16_hi(w[j]);
+            }
+            uint16_t sb, mb;
+            uint32_t codes[8];
+            if (width == 2) {
+                quant_group<2>(x, sb, mb, codes);
+                store_group<2>(rec, G, g, sb, mb, codes);
+            } else if (width == 4) {
+                quant_group<4>(x, sb, mb, codes);
+                store_group<4>(rec, G, g, sb, mb, codes);
+            } else {
+                quant_group<8>(x, sb, mb, codes);
+                store_group<8>(rec, G, g, sb, mb, codes);
+            }
+            // zero the record's tail padding (present for d = 64)
+            const uint32_t used = 4 * G + D * width / 8;
+            const uint32_t R = card_record_bytes(D, width);
+            if (g == 0)
+                for (uint32_t i = used; i < R; i += 8) *reinterpret_cast<uint2*>(rec + i) = make_uint2(0, 0);
         }
-        // zero the record's tail padding (present for d = 64)
-        const uint32_t used = 4 * G + D * width / 8;
-        const uint32_t R = card_record_bytes(D, width);
-        if (g == 0)
-            for (uint32_t i = used; i < R; i += 8) *reinterpret_cast<uint2*>(rec + i) = make_uint2(0, 0);
+    }
+    // the span, 16 bytes per lane per store
+    const uint32_t n16 = (uint32_t)((span1 - span0) / 16);
+    uint4* dst = reinterpret_cast<uint4*>(stream + span0);
+    const uint4* img = stage[threadIdx.x / kWave];
+#pragma unroll
+    for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
+        const uint32_t idx = kWave * j + lane;
+        if (idx < n16) dst[idx] = img[idx];
     }
     // zero the stream's tail padding after the last record
-    if (tok == p.T - 1 && g == 0)
+    if (t0 + nv == p.T && lane == 0)
         for (uint64_t i = p.off[p.T]; i < S; i += 16) *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
 }
 
@@ -304,12 +326,29 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
+    // The wave's records are one contiguous span of the stream: load it with
+    // 16-byte coalesced loads into LDS, then decode each group from there.
+    __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
+    uint4* st = stage[threadIdx.x / kWave];
+    {
+        const uint64_t span0 = p.off[t0];
+        const uint32_t n16 = (uint32_t)((p.off[t0 + nv] - span0) / 16);
+        const uint4* src = reinterpret_cast<const uint4*>(p.card_in + p.payload + s * S + span0);
+        uint4 c[kSpanChunks / kWave];
+#pragma unroll
+        for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
+            const uint32_t idx = kWave * j + lane;
+            c[j] = idx < n16 ? src[idx] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) st[kWave * j + lane] = c[j];
+    }
     uint32_t o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = 0;
     if (valid) {
         const uint32_t width = p.widths[tok];
-        const uint8_t* rec = p.card_in + p.payload + s * S + p.off[tok];
+        const uint8_t* rec = reinterpret_cast<const uint8_t*>(st) + (uint32_t)(p.off[tok] - p.off[t0]);
         if (width == 16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
@@ -321,11 +360,11 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
             dequant_group<8>(rec, G, g, o);
         }
     }
-    // Stage the wave's contiguous output image in LDS, then store it with
-    // each instruction covering a contiguous span (lane-strided 64-byte
-    // stores run at about half the write bandwidth).
-    __shared__ uint4 stage[kBlockThreads / kWave][kWave * 4];
-    uint4* st = stage[threadIdx.x / kWave];
+    // Stage the wave's contiguous output image in LDS (over the records,
+    // which every lane has read by now), then store it with each instruction
+    // covering a contiguous span (lane-strided 64-byte stores run at about
+    // half the write bandwidth).
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int c = 0; c < 4; ++c) st[lane * 4 + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     uint4* dst = reinterpret_cast<uint4*>((kv ? p.v_out : p.k_out) + (((uint64_t)l * p.H + h) * p.T + t0) * D);
