@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=32, help="layers of the workload in the CPU oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per dispatch (from rocprofv3 counters)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy a 1 GiB device buffer 3 times (the reference dispatches "
+                         "that scale the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="only parse two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calibrate-copy run, write --traffic and print a summary table")
     return ap.parse_args()
 
 
@@ -54,6 +60,9 @@ def pool_payload_bytes(L, H, T, d):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this codec is measured on "
               "one GPU's share; the multi-GPU handoff is a design note, not a benchmark)", file=sys.stderr)
@@ -162,6 +171,15 @@ def main():
     roofline = {"bound": "hbm", "kernel": kernel_names[dom], "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
+    if args.calibrate_copy:
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(k, v, widths_np, shape, args.cpu_layers, A)
@@ -179,6 +197,71 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+CALIBRATION_BYTES = 1 << 30
+CODEC_KERNELS = ["pool_decode_kernel", "pool_encode_kernel", "key_absmax_kernel", "card_pack_kernel",
+                 "card_unpack_kernel", "card_scan_kernel"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, value) per dispatch, in dispatch order, from the
+    counter_collection.csv rocprofv3 wrote under folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {folder}, found {files}")
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(n, v) for _, n, v in rows]
+
+
+def traffic_from_counters(fetch_dir, write_dir, out_path):
+    """HBM bytes per dispatch of each codec kernel: the FETCH_SIZE and
+    WRITE_SIZE counters (KiB per dispatch, separate runs), each scaled by
+    known bytes / counter reading of the last three calibration copies."""
+    import numpy as np
+
+    from agent_handoff_amd import kvcodec as kv
+    res = {}
+    factors = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(folder, counter)
+        copies = [v for n, v in rows if n.startswith(COPY_KERNEL)][-3:]
+        if len(copies) != 3:
+            raise SystemExit(f"{counter}: calibration copies not found")
+        kib = float(np.median(copies))
+        factors[counter] = CALIBRATION_BYTES / (kib * 1024.0)
+        for k in CODEC_KERNELS:
+            vals = [v for n, v in rows if k + "<" in n or k + "(" in n]
+            if vals:
+                res.setdefault(k, {})[counter] = {"kib_per_dispatch": float(np.median(vals)), "dispatches": len(vals)}
+    sha = _lib_sha(kv.LIB_PATH)
+    out = {"_calibration": {"copy_bytes": CALIBRATION_BYTES, "copy_kernel": COPY_KERNEL,
+                            "factor": {c: round(f, 5) for c, f in factors.items()}}}
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes / dispatch |",
+             "|---|---|---|---|---|"]
+    for k, e in res.items():
+        if "FETCH_SIZE" not in e or "WRITE_SIZE" not in e:
+            continue
+        fb = e["FETCH_SIZE"]["kib_per_dispatch"] * 1024.0 * factors["FETCH_SIZE"]
+        wb = e["WRITE_SIZE"]["kib_per_dispatch"] * 1024.0 * factors["WRITE_SIZE"]
+        out[k] = {"library_sha": sha, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                  "bytes_per_dispatch": round(fb + wb),
+                  "fetch_kib_raw": e["FETCH_SIZE"]["kib_per_dispatch"],
+                  "write_kib_raw": e["WRITE_SIZE"]["kib_per_dispatch"]}
+        lines.append(f"| {k} | {e['FETCH_SIZE']['dispatches']} | {e['FETCH_SIZE']['kib_per_dispatch']:.0f} | "
+                     f"{e['WRITE_SIZE']['kib_per_dispatch']:.0f} | {fb + wb:.4g} |")
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print("\n".join(lines))
+    print(f"copy factors: {factors}; library sha {sha}")
 
 
 def _lib_sha(path):
