@@ -163,6 +163,37 @@ def test_full_size_workload_bit_exact(cfg):
     say("  values at 1 ulp:", n1, "of", 2 * k.size)
 
 
+def test_long_context_32k_pool_layer_streamed():
+    """Llama-3-8B at 32K tokens (4.3 GB of bf16 K/V, inputs generated on the
+    GPU): the whole pool bit-exact against the oracle; then decode streamed
+    one layer per call, as a receiver injects a long pool layer by layer,
+    with three layers checked element by element within 1 ulp."""
+    w = synth.WORKLOADS[5]
+    L = w.shape[0]
+    say("32K pool:", w.name, "generating inputs on the GPU")
+    kd, vd = synth.kv_tensors_torch(w, 0, DEV)
+    pool = dev_bytes(kv.kvpool_bytes(w.shape), fill=0xA5)
+    ws = dev_bytes(kv.kvpool_workspace_bytes(w.shape), fill=0x5A)
+    say("  GPU encode")
+    kv.kvpool_encode(w.shape, kd, vd, pool, ws)
+    torch.cuda.synchronize()
+    k, v = to_host(kd), to_host(vd)
+    del kd, vd
+    say("  oracle encode")
+    ref = oracle.pool_encode(k, v)
+    assert_pool_equal(pool.cpu().numpy(), ref, w.shape)
+    del k, v
+    say("  layer-streamed decode")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for l in range(L):
+        ko, vo = gpu_decode(w.shape, pool, l, l + 1, status=status)
+        if l in (0, 13, L - 1):
+            rk, rv = oracle.pool_decode(ref, w.shape, l, l + 1)
+            assert_decode_close(to_host(ko[0]), rk, f"K layer {l}")
+            assert_decode_close(to_host(vo[0]), rv, f"V layer {l}")
+    assert int(status.item()) == 0
+
+
 @pytest.mark.parametrize("shape,cfg", [((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2), ((5, 2, 77, 128), 5)])
 def test_encode_many_blocks_per_layer(shape, cfg):
     """Layers of hundreds of 16-token blocks: the key max is reduced over
