@@ -396,6 +396,16 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
     quantize_keys<D>(p, b, kraw, mbits, stage_all[wib], lane);
 }
 
+// The pool's header as kvpool_encode writes it (magic, version 1 kind 1,
+// shape, total bytes).
+__device__ __forceinline__ bool pool_header_valid(const uint8_t* pool, uint32_t L, uint32_t H, uint32_t T, uint32_t D,
+                                                  uint64_t total) {
+    const uint32_t* hd = reinterpret_cast<const uint32_t*>(pool);
+    const uint64_t t = (uint64_t)hd[14] | ((uint64_t)hd[15] << 32);
+    return hd[0] == kPoolMagic && hd[1] == (1u | (1u << 16)) && hd[2] == L && hd[3] == H && hd[4] == T &&
+           hd[5] == D && t == total;
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams p) {
     constexpr int C = D / 4;
@@ -403,11 +413,7 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
 
-    const uint32_t* hd = reinterpret_cast<const uint32_t*>(p.pool);
-    const uint64_t total = (uint64_t)hd[14] | ((uint64_t)hd[15] << 32);
-    const bool ok = hd[0] == kPoolMagic && hd[1] == (1u | (1u << 16)) && hd[2] == p.L && hd[3] == p.H &&
-                    hd[4] == p.T && hd[5] == (uint32_t)D && total == p.lay.total;
-    if (!ok) {
+    if (!pool_header_valid(p.pool, p.L, p.H, p.T, D, p.lay.total)) {
         if (lane == 0 && p.status) atomicOr(p.status, 1 /* KVC_DEV_BAD_HEADER */);
         return;
     }
@@ -526,6 +532,46 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     }
 }
 
+// Fan-out (PolyKV 2.A: every agent injects the same decoded layers into its
+// own cache). With many agents, the decode writes agent 0 only and this
+// kernel copies agent 0's K and V to agents 1..n-1. Writing 2n streams from
+// one wave measured 5.4-5.8 TB/s, while workgroups that each write one
+// 4 KiB chunk of one stream, the streams taken in turn, reach 6-7 TB/s. So
+// here a workgroup copies one 4 KiB chunk (one 16-byte load and store per
+// thread) of one destination stream, and the grid is ordered so that each
+// XCD (workgroups are dealt to the 8 XCDs round-robin) walks its share of
+// the chunks in windows of kFanoutWindow chunks, every stream in turn per
+// window: the window's source chunks come from HBM once and from that XCD's
+// L2 for the other streams. (The mapping is only a performance assumption;
+// any placement copies the same bytes.)
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kFanoutWindow = 128;    // 4 KiB chunks per XCD window
+constexpr uint32_t kFanoutMinAgents = 8;  // below this the decode writes every agent itself (measured: fused wins at 4, fan-out at 8 and 15)
+
+struct FanoutParams {
+    const uint8_t* pool;  // header re-checked: nothing is copied after a refused decode
+    uint32_t L, H, T, D;
+    uint64_t total;
+    const uint4* src[2];                // agent 0's K and V
+    uint4* dst[2 * (kMaxAgents - 1)];   // stream 2 (a - 1) + kv for agent a
+    uint64_t n16;                       // 16-byte units per stream
+    uint64_t per_xcd;                   // chunks per XCD share
+    uint32_t streams, window;
+};
+
+__global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams p) {
+    if (!pool_header_valid(p.pool, p.L, p.H, p.T, p.D, p.total)) return;
+    const uint32_t xcd = blockIdx.x % kXcds;
+    const uint32_t i = blockIdx.x / kXcds;  // the grid has fewer than 2^31 workgroups
+    const uint32_t ci = i % p.window, t = i / p.window;
+    const uint32_t s = t % p.streams;
+    const uint64_t local = (uint64_t)(t / p.streams) * p.window + ci;
+    if (local >= p.per_xcd) return;
+    const uint64_t e = ((uint64_t)xcd * p.per_xcd + local) * kBlockThreads + threadIdx.x;
+    if (e >= p.n16) return;
+    p.dst[s][e] = p.src[s & 1u][e];
+}
+
 }  // namespace
 
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
@@ -570,16 +616,42 @@ hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uin
     p.T = s.T;
     p.nb = pool_blocks_per_head(s.T);
     p.l0 = l0;
-    p.n_out = n_out;
     p.n_waves = (uint64_t)(l1 - l0) * s.H * p.nb;
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
+
+    // fan-out copy plan (see fanout_copy_kernel)
+    FanoutParams f{};
+    f.n16 = (uint64_t)(l1 - l0) * s.H * s.T * s.d * 2 / 16;
+    const uint64_t chunks = (f.n16 + kBlockThreads - 1) / kBlockThreads;
+    f.per_xcd = (chunks + kXcds - 1) / kXcds;
+    f.window = (uint32_t)(f.per_xcd < kFanoutWindow ? f.per_xcd : kFanoutWindow);
+    f.streams = 2 * (n_out - 1);
+    const uint64_t fgrid = (uint64_t)kXcds * ((f.per_xcd + f.window - 1) / f.window) * f.streams * f.window;
+    const bool fanout = n_out >= kFanoutMinAgents && fgrid <= 0x7FFFFFFFull;
+
+    p.n_out = fanout ? 1 : n_out;
     for (uint32_t a = 0; a < (uint32_t)kMaxAgents; ++a) {
-        p.k_out[a] = a < n_out ? static_cast<uint16_t*>(k_out[a]) : nullptr;
-        p.v_out[a] = a < n_out ? static_cast<uint16_t*>(v_out[a]) : nullptr;
+        p.k_out[a] = a < p.n_out ? static_cast<uint16_t*>(k_out[a]) : nullptr;
+        p.v_out[a] = a < p.n_out ? static_cast<uint16_t*>(v_out[a]) : nullptr;
     }
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    return launch_kernel(s.d == 64 ? pool_decode_kernel<64> : pool_decode_kernel<128>, dim3((uint32_t)nblocks),
-                         dim3(kBlockThreads), stream, p);
+    hipError_t e = launch_kernel(s.d == 64 ? pool_decode_kernel<64> : pool_decode_kernel<128>,
+                                 dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
+    if (e != hipSuccess || !fanout) return e;
+
+    f.pool = p.pool;
+    f.L = s.L;
+    f.H = s.H;
+    f.T = s.T;
+    f.D = s.d;
+    f.total = p.lay.total;
+    f.src[0] = static_cast<const uint4*>(k_out[0]);
+    f.src[1] = static_cast<const uint4*>(v_out[0]);
+    for (uint32_t a = 1; a < n_out; ++a) {
+        f.dst[2 * (a - 1)] = static_cast<uint4*>(k_out[a]);
+        f.dst[2 * (a - 1) + 1] = static_cast<uint4*>(v_out[a]);
+    }
+    return launch_kernel(fanout_copy_kernel, dim3((uint32_t)fgrid), dim3(kBlockThreads), stream, f);
 }
 
 }  // namespace kvc

@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FANOUT_MIN_AGENTS = 8  # the library decodes into this many agents or more as decode + fan-out copy
 METRIC = "KV codec encode/decode GB/s and % of HBM peak, Llama-3-8B shape 4K tok"
 
 
@@ -61,7 +62,7 @@ def pool_payload_bytes(L, H, T, d):
 def main():
     args = parse()
     if args.traffic_from:
-        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.traffic)
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.traffic, args.agents)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this codec is measured on "
@@ -181,20 +182,26 @@ def main():
     copy_ceiling = {"bytes": 2 * half, "us": round(tc * 1e6, 2), "GB/s": round(2 * half / tc / 1e9, 1),
                     "decode_frac_of_copy": round(alg["decode"] / med(per_op["decode"]) / (2 * half / tc), 4)}
 
-    # dominant kernel: the one with the most time per step
+    # dominant op: the one with the most time per step. Its kernels (the
+    # decode into many agents is the decode kernel for agent 0, then the
+    # fan-out copy kernel) are timed together by the op's events.
     dom = max(ops, key=lambda o: med(per_op[o]))
-    kernel_names = {"encode": "pool_encode_kernel", "decode": "pool_decode_kernel",
-                    "pack": "card_pack_kernel", "unpack": "card_unpack_kernel"}
+    kernel_names = {"encode": ["fill_zero_kernel", "key_absmax_kernel", "pool_encode_kernel"],
+                    "decode": ["pool_decode_kernel", "fanout_copy_kernel"] if A >= FANOUT_MIN_AGENTS
+                    else ["pool_decode_kernel"],
+                    "pack": ["card_scan_kernel", "card_pack_kernel"],
+                    "unpack": ["card_scan_kernel", "card_unpack_kernel"]}
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
             tr = json.load(f)
-        entry = tr.get(kernel_names[dom])
-        if entry and entry.get("library_sha") == _lib_sha(kv.LIB_PATH):
-            traffic = entry.get("bytes_per_dispatch")
+        entries = [tr.get(k) for k in kernel_names[dom]]
+        sha = _lib_sha(kv.LIB_PATH)
+        if all(e and e.get("library_sha") == sha and e.get("agents") == A for e in entries):
+            traffic = sum(e["bytes_per_dispatch"] for e in entries)
     ach = alg[dom] / med(per_op[dom]) / 1e9
-    roofline = {"bound": "hbm", "kernel": kernel_names[dom], "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roofline = {"bound": "hbm", "kernel": " + ".join(kernel_names[dom]), "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
     if args.calibrate_copy:
         src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -226,8 +233,8 @@ def main():
 
 
 CALIBRATION_BYTES = 1 << 30
-CODEC_KERNELS = ["pool_decode_kernel", "pool_encode_kernel", "key_absmax_kernel", "card_pack_kernel",
-                 "card_unpack_kernel", "card_scan_kernel"]
+CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_kernel", "key_absmax_kernel",
+                 "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -248,7 +255,7 @@ def _counter_rows(folder, counter):
     return [(n, v) for _, n, v in rows]
 
 
-def traffic_from_counters(fetch_dir, write_dir, out_path):
+def traffic_from_counters(fetch_dir, write_dir, out_path, agents):
     """HBM bytes per dispatch of each codec kernel: the FETCH_SIZE and
     WRITE_SIZE counters (KiB per dispatch, separate runs), each scaled by
     known bytes / counter reading of the last three calibration copies."""
@@ -278,7 +285,7 @@ def traffic_from_counters(fetch_dir, write_dir, out_path):
             continue
         fb = e["FETCH_SIZE"]["kib_per_dispatch"] * 1024.0 * factors["FETCH_SIZE"]
         wb = e["WRITE_SIZE"]["kib_per_dispatch"] * 1024.0 * factors["WRITE_SIZE"]
-        out[k] = {"library_sha": sha, "fetch_bytes": round(fb), "write_bytes": round(wb),
+        out[k] = {"library_sha": sha, "agents": agents, "fetch_bytes": round(fb), "write_bytes": round(wb),
                   "bytes_per_dispatch": round(fb + wb),
                   "fetch_kib_raw": e["FETCH_SIZE"]["kib_per_dispatch"],
                   "write_kib_raw": e["WRITE_SIZE"]["kib_per_dispatch"]}

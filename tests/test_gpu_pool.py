@@ -107,7 +107,8 @@ def test_decode_fanout_and_layer_ranges():
     assert torch.equal(vm[0].view(torch.int16), vo[0][1:3].view(torch.int16))
 
 
-def test_decode_bad_header_sets_status_and_writes_nothing():
+@pytest.mark.parametrize("agents", [1, 5, 9])
+def test_decode_bad_header_sets_status_and_writes_nothing(agents):
     shape = (2, 2, 32, 64)
     k, v = _inputs(shape, 1, 0)
     ref_pool = oracle.pool_encode(k, v)
@@ -116,9 +117,28 @@ def test_decode_bad_header_sets_status_and_writes_nothing():
         bad[pos] = val
         pool = torch.from_numpy(bad).to(DEV)
         status = torch.zeros(1, dtype=torch.int32, device=DEV)
-        ko, vo = gpu_decode(shape, pool, status=status)
+        ko, vo = gpu_decode(shape, pool, status=status, agents=agents)
         assert int(status.item()) == kv.KVC_DEV_BAD_HEADER
-        assert torch.isnan(ko[0].float()).all() and torch.isnan(vo[0].float()).all()
+        for a in range(agents):
+            assert torch.isnan(ko[a].float()).all() and torch.isnan(vo[a].float()).all()
+
+
+@pytest.mark.parametrize("agents", [2, 7, 8, 9, 64])
+def test_decode_fanout_equals_one_agent_decode(agents):
+    """From a few agents on, the decode writes agent 0 and a second kernel
+    copies it to the others in 4 KiB chunks of one stream per workgroup;
+    every agent must equal a one-agent decode, also for ragged sizes (a
+    partial last chunk) and layer sub-ranges."""
+    for shape, cfg in [((2, 3, 37, 128), 3), ((1, 2, 5, 64), 2), ((3, 8, 512, 128), 3), ((2, 1, 17, 64), 1)]:
+        say("fan-out", shape, "agents", agents)
+        k, v = _inputs(shape, cfg, 6)
+        pool = torch.from_numpy(oracle.pool_encode(k, v)).to(DEV)
+        rk, rv = gpu_decode(shape, pool, agents=1)
+        for l0, l1 in [(0, shape[0]), (shape[0] - 1, shape[0])]:
+            ko, vo = gpu_decode(shape, pool, l0, l1, agents=agents)
+            for a in range(agents):
+                assert torch.equal(ko[a].view(torch.int16), rk[0][l0:l1].view(torch.int16)), (a, l0, l1)
+                assert torch.equal(vo[a].view(torch.int16), rv[0][l0:l1].view(torch.int16)), (a, l0, l1)
 
 
 def test_concurrent_decodes_on_streams():
