@@ -52,16 +52,19 @@ struct EncodeParams {
     uint32_t* ws;           // workspace, see the slot helpers below
     uint32_t L, H, T, nb;   // nb = 16-token blocks per head
     uint32_t blocks_per_layer;  // H * nb
+    uint32_t layers_per_round;  // single-pass encode: whole layers per round
     uint64_t n_waves;           // L * H * nb
     PoolLayout lay;
 };
 
-// Encode workspace (u32 words): 64 reserved words, then per layer kSlots
-// partial key maxima, each on its own 128-byte line so that concurrent
-// atomics spread over addresses.
+// Encode workspace (u32 words): [2] the single-pass encode's timeout flag,
+// up to 64 reserved words; then per layer kSlots partial key maxima of the
+// two-pass encode, each on its own 128-byte line so that concurrent atomics
+// spread over addresses; then the single-pass encode's flag words.
 constexpr uint32_t kSlots = 16;
 constexpr uint32_t kSlotStride = 32;  // words
 constexpr uint32_t kWsHead = 64;      // words
+constexpr uint32_t kWsTimeout = 2;
 
 __device__ __forceinline__ uint32_t* absmax_slot(uint32_t* ws, uint32_t l, uint32_t s) {
     return ws + kWsHead + (l * kSlots + s) * kSlotStride;
@@ -396,6 +399,303 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
     quantize_keys<D>(p, b, kraw, mbits, stage_all[wib], lane);
 }
 
+// ---------------------------------------------------------------- single-pass encode
+//
+// The key scale of a layer needs every key of the layer, so the two-pass
+// encode reads K twice. Here K is read once and parked in LDS: a
+// cooperative persistent grid (all workgroups co-resident, one per CU at
+// this LDS size) walks the layers in rounds of whole layers; each of a
+// workgroup's 8 worker waves takes 4 KiB of keys per round.
+//
+// Worker wave, iteration r:
+//   a. issue the loads of its round-r block(s);
+//   b. wait (in LDS) until its workgroup's coordinator has the maxima of
+//      round r-2, then quantise the keys it parked in round r-2;
+//   c. encode round r's values, park its keys in LDS, fold its key maxima
+//      into the workgroup's (LDS atomics) and count itself done.
+// Coordinator wave (a ninth wave), round r: when the workers are done with
+// r, publish the workgroup's maxima of r as flag|max words (one per layer
+// and workgroup; one plain device-scope store each, no returning atomic),
+// then read every workgroup's words of round r-1 until all are flagged,
+// reduce them to the layer maxima and hand those to the workers in LDS.
+// Only the coordinator waits on device-scope memory, so the workers' load
+// counters never wait for a poll, and a round of work separates each
+// publication from the wait for it.
+constexpr int kFusedWorkers = 8;
+constexpr int kFusedThreads = (kFusedWorkers + 1) * kWave;
+constexpr int kHoldRounds = 3;
+constexpr uint32_t kMaxRoundLayers = 32;
+constexpr uint32_t kMaxFusedGrid = 1024;  // workgroups; sizes the flag words of the workspace
+constexpr uint32_t kFlag = 0x80000000u;
+// Spin limit of every wait, in ticks of the 100 MHz constant clock: 0.5 s,
+// far beyond any legitimate wait.
+constexpr uint64_t kWaitTicks = 50000000ull;
+
+__device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t L, uint32_t l) {
+    return ws + kWsHead + L * kSlots * kSlotStride + l * kMaxFusedGrid;
+}
+
+template <int D>
+struct FusedLds {
+    static constexpr int kBpw = 128 / D;  // blocks per worker wave per round: 4 KiB of keys
+    uint4 hold[kHoldRounds][kFusedWorkers][kBpw][D / 32][kWave];  // [round % 3][wave][block][chunk][lane]
+    EncodeStage<D> stage[kFusedWorkers];
+    // By round % 3: a worker reaches round r only after its wait in round
+    // r-1 saw the maxima of round r-3 ready, i.e. after the coordinator has
+    // consumed and cleared the round-(r-3) entries that round r reuses.
+    uint32_t wg_max[kHoldRounds][kMaxRoundLayers];     // this workgroup's key maxima
+    uint32_t layer_max[kHoldRounds][kMaxRoundLayers];  // every workgroup's, per layer
+    uint32_t done[kHoldRounds];                        // workers done with the round
+    uint32_t ready;                                    // rounds whose maxima are in layer_max
+};
+
+// Largest bf16 magnitude (as bits) among a lane's raw words.
+template <int N>
+__device__ __forceinline__ uint32_t lane_absmax_bits(const uint4 (&raw)[N]) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, raw[i].x & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, raw[i].y & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, raw[i].z & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, raw[i].w & 0x7FFF7FFFu));
+    }
+    return mx.x > mx.y ? mx.x : mx.y;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
+        r = t > r ? t : r;
+    }
+    return r;
+}
+
+struct Round {
+    uint32_t l0, nl, nblk;  // first layer, layers, blocks
+};
+
+__device__ __forceinline__ Round round_of(const EncodeParams& p, uint32_t r) {
+    Round q;
+    q.l0 = r * p.layers_per_round;
+    q.nl = (p.L - q.l0 < p.layers_per_round) ? p.L - q.l0 : p.layers_per_round;
+    q.nblk = q.nl * p.blocks_per_layer;
+    return q;
+}
+
+__device__ __forceinline__ uint32_t lds_load(const uint32_t* a) {
+    return __hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Record that a wait gave up (never expected). The wait for all of the
+// wave's memory operations makes the flag performed before the wave's later
+// work, so workgroup 0 sees it before it writes the header. (Waiting here,
+// inside the rare branch, rather than on a returned value keeps the common
+// path free of a full wait that would drain the prefetched loads.)
+__device__ __forceinline__ void note_timeout(const EncodeParams& p) {
+    __hip_atomic_fetch_or(p.ws + kWsTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+template <int D>
+struct FusedRaw {
+    uint4 k[FusedLds<D>::kBpw][D / 32];
+    uint4 v[FusedLds<D>::kBpw][D / 32];
+};
+
+// Loads of a worker wave's round-r block(s). Always issued, the same number
+// every time (a block past the round's end, or a round past the last, loads
+// block 0 of layer 0 and is never used): the waits for a round's data then
+// count exactly the loads issued after it, and never drain the prefetch.
+template <int D>
+__device__ __forceinline__ void fused_load(const EncodeParams& p, uint32_t r, uint32_t nrounds, uint32_t gw,
+                                           uint32_t NW, uint32_t lane, FusedRaw<D>& raw) {
+    const bool live_round = r < nrounds;
+    const Round q = round_of(p, live_round ? r : 0);
+#pragma unroll
+    for (int j = 0; j < FusedLds<D>::kBpw; ++j) {
+        const uint32_t bi = gw + (uint32_t)j * NW;
+        const bool live = live_round && bi < q.nblk;
+        const BlockPos b = block_pos<D>(p, live ? q.l0 + bi / p.blocks_per_layer : 0u,
+                                        live ? bi % p.blocks_per_layer : 0u, lane);
+        load_lane<D>(p.k, b.elem, raw.k[j]);
+        load_lane<D>(p.v, b.elem, raw.v[j]);
+    }
+}
+
+// Worker iteration r: round r+1's loads go out first (into `fill`), then
+// round r (in `cur`, loaded one iteration earlier) is encoded, then round
+// r-2's keys are quantised: a round of work separates the workers' count
+// for a round from their wait for that round's maxima.
+template <int D>
+__device__ __forceinline__ void fused_worker_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t w, uint32_t lane,
+                                                   uint32_t r, uint32_t nrounds, FusedRaw<D>& cur,
+                                                   FusedRaw<D>& fill) {
+    constexpr int BPW = FusedLds<D>::kBpw;
+    const uint32_t NW = gridDim.x * kFusedWorkers;  // worker waves in the grid
+    const uint32_t gw = blockIdx.x * kFusedWorkers + w;
+    fused_load<D>(p, r + 1, nrounds, gw, NW, lane, fill);
+    // round r's values and keys
+    if (r < nrounds) {
+        const Round q = round_of(p, r);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const uint32_t bi = gw + (uint32_t)j * NW;
+            if (bi < q.nblk) {
+                const uint32_t lr = bi / p.blocks_per_layer;
+                const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                encode_values<D>(p, b, cur.v[j], sm.stage[w], lane);
+                const uint32_t m = wave_max_u32(b.valid ? lane_absmax_bits<D / 32>(cur.k[j]) : 0u);
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) sm.hold[r % kHoldRounds][w][j][i][lane] = cur.k[j][i];
+                if (lane == 0)
+                    __hip_atomic_fetch_max(&sm.wg_max[r % kHoldRounds][lr], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        // LDS operations of a wave complete in order: the maxima above land
+        // before the count
+        if (lane == 0) __hip_atomic_fetch_add(&sm.done[r % kHoldRounds], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // round r-2's keys
+    if (r >= 2) {
+        const uint32_t rq = r - 2;
+        const uint64_t start = wall_clock64();
+        while (lds_load(&sm.ready) < rq + 1) {
+            if (wall_clock64() - start > kWaitTicks) {
+                note_timeout(p);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const Round q = round_of(p, rq);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const uint32_t bi = gw + (uint32_t)j * NW;
+            if (bi < q.nblk) {
+                const uint32_t lr = bi / p.blocks_per_layer;
+                const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                uint4 kr[D / 32];
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) kr[i] = sm.hold[rq % kHoldRounds][w][j][i][lane];
+                quantize_keys<D>(p, b, kr, lds_load(&sm.layer_max[rq % kHoldRounds][lr]), sm.stage[w], lane);
+            }
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void fused_worker(const EncodeParams& p, FusedLds<D>& sm, uint32_t w, uint32_t lane,
+                                             uint32_t nrounds) {
+    // two register sets, alternating, one round of loads in flight (the loop
+    // is unrolled by two so that both stay in registers)
+    FusedRaw<D> a, b;
+    const uint32_t gw = blockIdx.x * kFusedWorkers + w, NW = gridDim.x * kFusedWorkers;
+    fused_load<D>(p, 0, nrounds, gw, NW, lane, a);
+    for (uint32_t r = 0; r < nrounds + 2; r += 2) {
+        fused_worker_round<D>(p, sm, w, lane, r, nrounds, a, b);
+        if (r + 1 < nrounds + 2) fused_worker_round<D>(p, sm, w, lane, r + 1, nrounds, b, a);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLds<D>& sm, uint32_t lane,
+                                                  uint32_t nrounds) {
+    const uint32_t G = gridDim.x;
+    for (uint32_t r = 0; r <= nrounds; ++r) {
+        if (r < nrounds) {
+            // the workers' round r, then this workgroup's maxima of it, published
+            const Round q = round_of(p, r);
+            const uint64_t start = wall_clock64();
+            while (lds_load(&sm.done[r % kHoldRounds]) < (uint32_t)kFusedWorkers) {
+                if (wall_clock64() - start > kWaitTicks) {
+                    note_timeout(p);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            uint32_t m = 0;
+            if (lane < q.nl) m = lds_load(&sm.wg_max[r % kHoldRounds][lane]);
+            if (lane < kMaxRoundLayers) sm.wg_max[r % kHoldRounds][lane] = 0;  // reused in round r + 3
+            if (lane == 0) sm.done[r % kHoldRounds] = 0;
+            if (lane < q.nl)
+                __hip_atomic_store(round_flags(p.ws, p.L, q.l0 + lane) + blockIdx.x, kFlag | m, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (r >= 1) {
+            // every workgroup's maxima of round r-1, reduced per layer
+            const uint32_t rq = r - 1;
+            const Round q = round_of(p, rq);
+            for (uint32_t lr = 0; lr < q.nl; ++lr) {
+                const uint32_t* f = round_flags(p.ws, p.L, q.l0 + lr);
+                // all of the layer's words at once (lane + 64 i), then again
+                // for those not yet flagged
+                constexpr int kPer = kMaxFusedGrid / kWave;
+                uint32_t v[kPer];
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const uint32_t g = lane + (uint32_t)i * kWave;
+                    v[i] = g < G ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlag;
+                }
+                const uint64_t start = wall_clock64();
+                for (;;) {
+                    bool all = true;
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) all = all && (v[i] & kFlag);
+                    if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
+                    if (wall_clock64() - start > kWaitTicks) {
+                        note_timeout(p);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const uint32_t g = lane + (uint32_t)i * kWave;
+                        if (!(v[i] & kFlag)) v[i] = __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                uint32_t mx = 0;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const uint32_t x = v[i] & ~kFlag;
+                    mx = x > mx ? x : mx;
+                }
+                mx = wave_max_u32(mx);
+                if (lane == 0) sm.layer_max[rq % kHoldRounds][lr] = mx;
+            }
+            if (lane == 0)
+                __hip_atomic_store(&sm.ready, rq + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kFusedThreads) void pool_encode_fused_kernel(EncodeParams p) {
+    __shared__ FusedLds<D> sm;
+    const uint32_t lane = lane_id();
+    const uint32_t w = wave_uniform(threadIdx.x / kWave);
+    const uint32_t nrounds = (p.L + p.layers_per_round - 1) / p.layers_per_round;
+    if (threadIdx.x < kHoldRounds * kMaxRoundLayers) (&sm.wg_max[0][0])[threadIdx.x] = 0;
+    if (threadIdx.x < kHoldRounds) sm.done[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sm.ready = 0;
+    __syncthreads();
+    if (w < (uint32_t)kFusedWorkers)
+        fused_worker<D>(p, sm, w, lane, nrounds);
+    else
+        fused_coordinator<D>(p, sm, lane, nrounds);
+    // Header and padding last, by workgroup 0: its coordinator saw every
+    // workgroup's last publication, so any timeout flag is visible by now,
+    // and no wait can time out after it.
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < kBlockThreads) pool_header_and_padding(p, D, threadIdx.x);
+        if (threadIdx.x == 0 &&
+            __hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            reinterpret_cast<uint32_t*>(p.pool)[0] = 0;
+    }
+}
+
 // The pool's header as kvpool_encode writes it (magic, version 1 kind 1,
 // shape, total bytes).
 __device__ __forceinline__ bool pool_header_valid(const uint8_t* pool, uint32_t L, uint32_t H, uint32_t T, uint32_t D,
@@ -586,14 +886,38 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.T = s.T;
     p.nb = pool_blocks_per_head(s.T);
     p.blocks_per_layer = s.H * p.nb;
+    p.layers_per_round = 0;
     p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
-    // Two passes: the per-layer key maxima, then the encode proper (the
-    // first needs every key of a layer before any key code can be written).
     const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L);
     hipError_t e = launch_kernel(fill_zero_kernel, dim3((ws_words + 255) / 256), dim3(256), stream, ws, ws_words);
     if (e != hipSuccess) return e;
+
+    // Single pass when one workgroup per CU can be co-resident and a round of
+    // whole layers fits the grid's LDS; otherwise two passes (the per-layer
+    // key maxima, then the encode proper).
+    const void* fused = s.d == 64 ? reinterpret_cast<const void*>(pool_encode_fused_kernel<64>)
+                                  : reinterpret_cast<const void*>(pool_encode_fused_kernel<128>);
+    int dev = 0, cus = 0, per_cu = 0, coop = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, kFusedThreads, 0) == hipSuccess && per_cu > 0 &&
+        (uint64_t)cus * (uint64_t)per_cu <= kMaxFusedGrid) {
+        const uint64_t grid = (uint64_t)cus * (uint64_t)per_cu;
+        const uint64_t per_round = grid * kFusedWorkers * (128u / s.d);  // blocks a round can hold
+        uint64_t lpr = per_round / p.blocks_per_layer;
+        if (lpr > kMaxRoundLayers) lpr = kMaxRoundLayers;
+        if (lpr > s.L) lpr = s.L;
+        if (lpr >= 1) {
+            p.layers_per_round = (uint32_t)lpr;
+            void* argv[] = {&p};
+            return report_launch(hipLaunchCooperativeKernel(fused, dim3((uint32_t)grid), dim3(kFusedThreads), argv, 0,
+                                                            stream),
+                                 "pool_encode_fused_kernel");
+        }
+    }
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
     uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
     if (gx > 64) gx = 64;

@@ -214,10 +214,14 @@ def test_long_context_32k_pool_layer_streamed():
     assert int(status.item()) == 0
 
 
-@pytest.mark.parametrize("shape,cfg", [((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2), ((5, 2, 77, 128), 5)])
+@pytest.mark.parametrize("shape,cfg", [((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2), ((5, 2, 77, 128), 5),
+                                       ((2, 8, 4112, 128), 3), ((1, 32, 2064, 64), 2), ((40, 1, 16, 64), 1)])
 def test_encode_many_blocks_per_layer(shape, cfg):
     """Layers of hundreds of 16-token blocks: the key max is reduced over
-    many workgroups and slots before any key is coded."""
+    many workgroups before any key is coded. On a 256-CU GPU a single-pass
+    round holds 2048 blocks at d = 128 and 4096 at d = 64, so the 4112- and
+    2064-token shapes (2056 and 4128 blocks per layer) take the two-pass
+    encode; 40 one-block layers take more than one round of 32 layers."""
     say("encode", shape)
     k, v = _inputs(shape, cfg, 4)
     assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
