@@ -216,8 +216,6 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
     const uint32_t lane = lane_id();
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
-    if (p.info[2] != 0) return;
-    const uint64_t S = p.info[0];
     const uint64_t s = wave / p.nbk;
     const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
     const uint32_t tok = t0 + lane / G;
@@ -227,18 +225,27 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
-    uint8_t* stream = p.card + p.payload + s * S;
+    // The input loads go out first: they depend on nothing the scan wrote
+    // (lanes past the last token load the wave's first token), so their
+    // latency overlaps that of the scan's results below.
+    uint4 raw[4];
+    {
+        const uint16_t* src =
+            (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + (valid ? tok : t0)) * D + g * kCardGroup;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+    }
+    const uint64_t flags = p.info[2], S = p.info[0];
     const uint64_t span0 = p.off[t0], span1 = p.off[t0 + nv];
+    const uint64_t my_off = p.off[valid ? tok : t0];
+    const uint32_t width = p.widths[valid ? tok : t0];
+    if (flags != 0) return;
+    uint8_t* stream = p.card + p.payload + s * S;
 
     __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
     uint8_t* st = reinterpret_cast<uint8_t*>(stage[threadIdx.x / kWave]);
     if (valid) {
-        const uint16_t* src = (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + tok) * D + g * kCardGroup;
-        const uint32_t width = p.widths[tok];
-        uint8_t* rec = st + (uint32_t)(p.off[tok] - span0);
-        uint4 raw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+        uint8_t* rec = st + (uint32_t)(my_off - span0);
         if (width == 16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rec + 64 * g)[i] = raw[i];

@@ -713,20 +713,46 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
 
-    if (!pool_header_valid(p.pool, p.L, p.H, p.T, D, p.lay.total)) {
-        if (lane == 0 && p.status) atomicOr(p.status, 1 /* KVC_DEV_BAD_HEADER */);
-        return;
-    }
-
     const uint32_t blk = (uint32_t)(wave % p.nb);
     const uint64_t lh_rel = wave / p.nb;
     const uint64_t lh = (uint64_t)p.l0 * p.H + lh_rel;
     const uint32_t l = (uint32_t)(lh / p.H);
-    const uint32_t tok = blk * kBlockTokens + (lane >> 2);
+    const uint32_t t0 = blk * kBlockTokens;
     const uint32_t m = lane & 3u;
-    const bool valid = tok < p.T;
-    const uint64_t vec = lh * p.T + tok;
-    const uint64_t elem = vec * D + (uint64_t)m * C;
+    // lanes past the head's last token read the block's first vector (their
+    // outputs are never stored)
+    const bool valid = t0 + (lane >> 2) < p.T;
+    const uint64_t vec = lh * p.T + (valid ? t0 + (lane >> 2) : t0);
+
+    // The pool loads go out first; the header is checked while they are in
+    // flight (nothing is written before it has passed).
+    uint4 kraw[C / 16];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(p.pool + p.lay.k_codes + vec * D + (uint64_t)m * C);
+#pragma unroll
+        for (int i = 0; i < C / 16; ++i) kraw[i] = src[i];
+    }
+    uint32_t pw[3];
+    {
+        const uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
+        if (D == 128) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) pw[q] = reinterpret_cast<const uint32_t*>(codes + 16 * q)[m];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(codes + 8 * q)[m >> 1];
+                pw[q] = (m & 1u) ? (w & 0xFFFF0000u) : (w << 16);  // this lane's 16 bits on top
+            }
+        }
+    }
+    const uint16_t sbits = reinterpret_cast<const uint16_t*>(p.pool + p.lay.v_scale)[vec];
+    const float ks = reinterpret_cast<const float*>(p.pool + p.lay.k_scale)[l];
+
+    if (!pool_header_valid(p.pool, p.L, p.H, p.T, D, p.lay.total)) {
+        if (lane == 0 && p.status) atomicOr(p.status, 1 /* KVC_DEV_BAD_HEADER */);
+        return;
+    }
 
     // Outputs are staged per wave in LDS (the lane-major 64-byte chunks form
     // the wave's contiguous 16-token output image) and stored so that each
@@ -736,23 +762,12 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     constexpr int CH = C / 8;  // 16-byte chunks per lane
     __shared__ uint4 stage[kBlockThreads / kWave][kWave * CH];
     uint4* st = stage[threadIdx.x / kWave];
-    const uint32_t t0 = blk * kBlockTokens;
     const uint32_t nv = (p.T - t0 < kBlockTokens) ? p.T - t0 : kBlockTokens;  // valid tokens of the block
     const uint64_t out_base = (lh_rel * p.T + t0) * D / 8;  // in 16-byte chunks
 
     // ---- keys: bf16(q * scale)
-    const float ks = reinterpret_cast<const float*>(p.pool + p.lay.k_scale)[l];
     {
-        uint4 raw[C / 16];
-        if (valid) {
-            const uint4* src = reinterpret_cast<const uint4*>(p.pool + p.lay.k_codes + elem);
-#pragma unroll
-            for (int i = 0; i < C / 16; ++i) raw[i] = src[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < C / 16; ++i) raw[i] = make_uint4(0, 0, 0, 0);
-        }
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
         uint32_t o[C / 2];
 #pragma unroll
         for (int j = 0; j < C / 4; ++j) {
@@ -775,22 +790,6 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     // butterfly, then * (s / sqrt(d)).
     float c0 = kLv0, c1 = kLv1, c2 = kLv2, c3 = kLv3;
     asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
-    uint32_t pw[3] = {0, 0, 0};
-    uint16_t sbits = 0;
-    if (valid) {
-        const uint8_t* codes = p.pool + p.lay.v_codes + vec * pool_code_bytes(D);
-        if (D == 128) {
-#pragma unroll
-            for (int q = 0; q < 3; ++q) pw[q] = reinterpret_cast<const uint32_t*>(codes + 16 * q)[m];
-        } else {
-#pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const uint32_t w = reinterpret_cast<const uint32_t*>(codes + 8 * q)[m >> 1];
-                pw[q] = (m & 1u) ? (w & 0xFFFF0000u) : (w << 16);  // this lane's 16 bits on top
-            }
-        }
-        sbits = reinterpret_cast<const uint16_t*>(p.pool + p.lay.v_scale)[vec];
-    }
     float y[C];
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
@@ -860,7 +859,6 @@ struct FanoutParams {
 };
 
 __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams p) {
-    if (!pool_header_valid(p.pool, p.L, p.H, p.T, p.D, p.total)) return;
     const uint32_t xcd = blockIdx.x % kXcds;
     const uint32_t i = blockIdx.x / kXcds;  // the grid has fewer than 2^31 workgroups
     const uint32_t ci = i % p.window, t = i / p.window;
@@ -869,7 +867,10 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
     if (local >= p.per_xcd) return;
     const uint64_t e = ((uint64_t)xcd * p.per_xcd + local) * kBlockThreads + threadIdx.x;
     if (e >= p.n16) return;
-    p.dst[s][e] = p.src[s & 1u][e];
+    // load first, check the header while the load is in flight
+    const uint4 x = p.src[s & 1u][e];
+    if (!pool_header_valid(p.pool, p.L, p.H, p.T, p.D, p.total)) return;
+    p.dst[s][e] = x;
 }
 
 }  // namespace
