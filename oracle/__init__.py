@@ -230,6 +230,25 @@ def card_unpack(card, shape):
     return ko, vo
 
 
+def card_meta(card):
+    """(model ID bytes, position offset) from a card's header."""
+    card = np.ascontiguousarray(card, np.uint8)
+    model_id = bytes(card[72:136]).split(b"\0", 1)[0]
+    position_offset = int.from_bytes(bytes(card[32:40]), "little", signed=True)
+    return model_id, position_offset
+
+
+def card_transcode(card, shape, new_widths):
+    """One hop of a handoff chain (QKVShare, problem statement and method:
+    each agent passes the cache on as a card at its own per-token widths):
+    the card rebuilt to full width, then packed again at new_widths, with
+    the model ID and position offset carried over. This is the definition
+    itself, written as the composition of unpack and pack."""
+    k, v = card_unpack(card, shape)
+    model_id, position_offset = card_meta(card)
+    return card_pack(k, v, new_widths, model_id, position_offset)
+
+
 # ---------------------------------------------------------------- scalar formats
 
 def f64_to_bf16(x):

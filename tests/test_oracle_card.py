@@ -167,3 +167,54 @@ def test_width_16_is_passthrough_and_widths_shared_across_streams():
     np.testing.assert_array_equal(ko[:, :, :8], k[:, :, :8])
     np.testing.assert_array_equal(vo[:, :, :8], v[:, :, :8])
     assert not np.array_equal(ko[:, :, 8:], k[:, :, 8:])
+
+
+# ---------------------------------------------------------------- hop transcode
+
+def _widths(T, seed):
+    return synth.card_widths(synth.WORKLOADS[4], seed, T=T)
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 40, 128), (1, 3, 33, 64)])
+def test_transcode_from_full_width_card_equals_pack_of_the_data(shape):
+    """A card at width 16 everywhere holds the bf16 inputs verbatim, so one
+    hop from it to widths w must equal packing the original data at w."""
+    k, v = _kv(shape, 11)
+    T = shape[2]
+    full = oracle.card_pack(k, v, np.full(T, 16, np.uint8), b"llama-3.1-8b", -17)
+    for seed in (0, 1):
+        w = _widths(T, seed)
+        got = oracle.card_transcode(full, shape, w)
+        assert np.array_equal(got, oracle.card_pack(k, v, w, b"llama-3.1-8b", -17))
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 40, 128), (1, 3, 33, 64)])
+def test_transcode_to_full_width_is_lossless(shape):
+    """Width 16 keeps bf16 verbatim: a hop to all-16 reconstructs exactly
+    what the source card reconstructs, and stores those values as they are."""
+    k, v = _kv(shape, 12)
+    T, d = shape[2], shape[3]
+    card = oracle.card_pack(k, v, _widths(T, 3), b"m", 5)
+    full = oracle.card_transcode(card, shape, np.full(T, 16, np.uint8))
+    rk, rv = oracle.card_unpack(card, shape)
+    fk, fv = oracle.card_unpack(full, shape)
+    assert np.array_equal(fk, rk) and np.array_equal(fv, rv)
+    h, widths = _parse(full, shape)
+    rec = _record(full, h, widths, 0, T - 1, d)   # stream 0 = (l 0, K, h 0)
+    assert np.array_equal(rec.view("<u2"), rk[0, 0, T - 1])
+
+
+def test_transcode_carries_metadata_and_replaces_widths():
+    shape = (2, 2, 40, 128)
+    k, v = _kv(shape, 13)
+    T = shape[2]
+    w0, w1 = _widths(T, 4), _widths(T, 5)
+    card = oracle.card_pack(k, v, w0, b"qwen-7b-instruct", 123456789)
+    out = oracle.card_transcode(card, shape, w1)
+    h, widths = _parse(out, shape)
+    assert h["model"] == b"qwen-7b-instruct" and h["pos"] == 123456789
+    assert np.array_equal(widths, w1)
+    sizes = sum(card_record_size(shape[3], int(b)) for b in w1)
+    S = -(-sizes // 256) * 256
+    payload = 256 + (-(-T // 256) * 256)
+    assert h["S"] == S and h["payload"] == payload and h["total"] == payload + 2 * 2 * 2 * S == out.size
