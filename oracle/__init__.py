@@ -69,6 +69,8 @@ def lib():
         L.or_card_pack.argtypes = [u32] * 4 + [p, p, p, ctypes.c_char_p, i64, p]
         L.or_card_unpack.restype = ctypes.c_int
         L.or_card_unpack.argtypes = [u32] * 4 + [p, u64, p, p]
+        L.or_card_dequant.restype = ctypes.c_uint16
+        L.or_card_dequant.argtypes = [u32, ctypes.c_uint16, ctypes.c_uint16]
         L.or_set_threads.restype = None
         L.or_set_threads.argtypes = [ctypes.c_int]
         L.or_max_threads.restype = ctypes.c_int
@@ -228,6 +230,11 @@ def card_unpack(card, shape):
     if rc:
         raise ValueError(f"or_card_unpack failed: {rc}")
     return ko, vo
+
+
+def card_dequant(q, scale_f16_bits, min_bf16_bits):
+    """One dequantised card value: bf16 bits of q * s + mn rounded once."""
+    return int(lib().or_card_dequant(int(q), int(scale_f16_bits), int(min_bf16_bits)))
 
 
 def card_meta(card):

@@ -490,6 +490,35 @@ static void card_pack_record(const uint16_t* x, uint32_t d, uint32_t b, uint8_t*
 }
 
 /* out = bf16(q * s + mn) in binary64; width 16 copies the stored bf16. */
+/* Whether x lies exactly halfway between two neighbouring bf16 values. */
+static int bf16_halfway(double x) {
+    double ax = fabs(x);
+    if (ax == 0.0 || !isfinite(ax)) return 0;
+    int e;
+    frexp(ax, &e);
+    int lead = e - 1;
+    if (lead < -126) lead = -126;
+    double t = ax / ldexp(1.0, lead - 7); /* exact: division by a power of two */
+    return t - floor(t) == 0.5;
+}
+
+/* One dequantised card value (QKVShare method item 3, the receiver
+ * rebuilding full-width values from a group's scale and minimum): the real
+ * number q*s + mn rounded once to bf16, ties to even. q*s is exact in
+ * binary64 (at most 8 + 11 significant bits). The sum is formed together
+ * with its rounding error (two-sum); the error can only matter when the
+ * rounded sum lies exactly halfway between two bf16 values, and then its
+ * sign decides the direction. */
+uint16_t or_card_dequant(uint32_t q, uint16_t scale_f16, uint16_t min_bf16) {
+    double p = (double)q * (double)or_f16_to_f32(scale_f16);
+    double mn = (double)or_bf16_to_f32(min_bf16);
+    double r = p + mn;
+    double bb = r - p;
+    double err = (p - (r - bb)) + (mn - bb);
+    if (err != 0.0 && bf16_halfway(r)) r = nextafter(r, err > 0.0 ? INFINITY : -INFINITY);
+    return or_f64_to_bf16(r);
+}
+
 static void card_unpack_record(const uint8_t* rec, uint32_t d, uint32_t b, uint16_t* out) {
     if (b == 16) {
         for (uint32_t i = 0; i < d; ++i) out[i] = get_u16(rec + 2 * i);
@@ -498,14 +527,14 @@ static void card_unpack_record(const uint8_t* rec, uint32_t d, uint32_t b, uint1
     uint32_t G = d / CARD_GROUP;
     const uint8_t* codes = rec + 4 * G;
     for (uint32_t g = 0; g < G; ++g) {
-        double s = (double)or_f16_to_f32(get_u16(rec + 2 * g));
-        double mn = (double)or_bf16_to_f32(get_u16(rec + 2 * G + 2 * g));
+        uint16_t s = get_u16(rec + 2 * g);
+        uint16_t mn = get_u16(rec + 2 * G + 2 * g);
         for (uint32_t j = 0; j < CARD_GROUP; ++j) {
             uint64_t bitpos = (uint64_t)(g * CARD_GROUP + j) * b;
             uint32_t q = 0;
             for (uint32_t u = 0; u < b; ++u)
                 q |= (uint32_t)((codes[(bitpos + u) / 8] >> ((bitpos + u) % 8)) & 1u) << u;
-            out[g * CARD_GROUP + j] = or_f64_to_bf16((double)q * s + mn);
+            out[g * CARD_GROUP + j] = or_card_dequant(q, s, mn);
         }
     }
 }
