@@ -490,33 +490,13 @@ static void card_pack_record(const uint16_t* x, uint32_t d, uint32_t b, uint8_t*
 }
 
 /* out = bf16(q * s + mn) in binary64; width 16 copies the stored bf16. */
-/* Whether x lies exactly halfway between two neighbouring bf16 values. */
-static int bf16_halfway(double x) {
-    double ax = fabs(x);
-    if (ax == 0.0 || !isfinite(ax)) return 0;
-    int e;
-    frexp(ax, &e);
-    int lead = e - 1;
-    if (lead < -126) lead = -126;
-    double t = ax / ldexp(1.0, lead - 7); /* exact: division by a power of two */
-    return t - floor(t) == 0.5;
-}
-
 /* One dequantised card value (QKVShare method item 3, the receiver
- * rebuilding full-width values from a group's scale and minimum): the real
- * number q*s + mn rounded once to bf16, ties to even. q*s is exact in
- * binary64 (at most 8 + 11 significant bits). The sum is formed together
- * with its rounding error (two-sum); the error can only matter when the
- * rounded sum lies exactly halfway between two bf16 values, and then its
- * sign decides the direction. */
+ * rebuilding full-width values from a group's scale and minimum): q*s + mn
+ * computed in binary32 with one rounding (fmaf; q*s alone is exact, at most
+ * 8 + 11 significant bits), then stored as bf16, round to nearest even. */
 uint16_t or_card_dequant(uint32_t q, uint16_t scale_f16, uint16_t min_bf16) {
-    double p = (double)q * (double)or_f16_to_f32(scale_f16);
-    double mn = (double)or_bf16_to_f32(min_bf16);
-    double r = p + mn;
-    double bb = r - p;
-    double err = (p - (r - bb)) + (mn - bb);
-    if (err != 0.0 && bf16_halfway(r)) r = nextafter(r, err > 0.0 ? INFINITY : -INFINITY);
-    return or_f64_to_bf16(r);
+    float r = fmaf((float)q, or_f16_to_f32(scale_f16), or_bf16_to_f32(min_bf16));
+    return or_f64_to_bf16((double)r);
 }
 
 static void card_unpack_record(const uint8_t* rec, uint32_t d, uint32_t b, uint16_t* out) {

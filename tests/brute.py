@@ -51,6 +51,30 @@ def exact_round_to_bf16(x):
     return sign | int(f.view(np.uint32) >> np.uint32(16))
 
 
+def exact_round_to_f32(x):
+    """Nearest binary32 to the real number x (a Fraction within the normal
+    range), ties to even, by exact rational comparison."""
+    x = Fraction(x)
+    if x == 0:
+        return np.float32(0.0)
+    ax = abs(x)
+    e = math.floor(math.log2(ax))
+    if Fraction(2) ** e > ax:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= ax:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 23)
+    lo = (ax // q) * q
+    hi = lo + q
+    if ax - lo < hi - ax:
+        r = lo
+    elif ax - lo > hi - ax:
+        r = hi
+    else:
+        r = lo if (lo / q) % 2 == 0 else hi
+    return np.float32(float(r) if x > 0 else -float(r))   # exact: r has at most 24 significant bits
+
+
 def bf16_ulp(x):
     """Spacing of bf16 numbers at |x| (normal range)."""
     ax = abs(float(x))

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -182,3 +182,31 @@ def test_card_argument_errors():
     assert unpack(k=5 * A + 4) == kv.KVC_E_ALIGN
     assert unpack(v=5 * A + 1024) == kv.KVC_E_ALIAS
     assert unpack(k=3 * A + 1024) == kv.KVC_E_ALIAS
+
+
+@fake_addresses
+def test_transcode_argument_errors():
+    ws_b = kv.cachecard_transcode_workspace_bytes(S)
+    assert ws_b == 2 * kv.cachecard_workspace_bytes(S)
+    cap = kv.cachecard_max_bytes(S)
+
+    def tc(shape=S, card_in=3 * A, nin=cap, widths=2 * A, card_out=5 * A, capacity=cap, ws=4 * A, ws_bytes=ws_b,
+           nbytes=None, status=None):
+        return L.cachecard_transcode(ctypes.byref(shape) if shape is not None else None, card_in, nin, widths,
+                                     card_out, capacity, nbytes, status, ws, ws_bytes, None)
+
+    assert tc(shape=None) == kv.KVC_E_NULL
+    assert tc(card_in=None) == kv.KVC_E_NULL
+    assert tc(widths=None) == kv.KVC_E_NULL
+    assert tc(card_out=None) == kv.KVC_E_NULL
+    assert tc(shape=kv.kvc_shape(1, 1, 4, 48)) == kv.KVC_E_SHAPE
+    assert tc(ws_bytes=ws_b - 1) == kv.KVC_E_SIZE
+    assert tc(nin=300) == kv.KVC_E_SIZE
+    assert tc(capacity=300) == kv.KVC_E_SIZE
+    assert tc(card_in=3 * A + 128) == kv.KVC_E_ALIGN
+    assert tc(card_out=5 * A + 16) == kv.KVC_E_ALIGN
+    assert tc(nbytes=6 * A + 4) == kv.KVC_E_ALIGN
+    assert tc(card_out=3 * A + 1024) == kv.KVC_E_ALIAS     # output inside the input card
+    assert tc(ws=5 * A + 512) == kv.KVC_E_ALIAS            # workspace inside the output card
+    assert tc(card_out=2 * A) == kv.KVC_E_ALIAS            # output over the new widths
+    assert tc(status=4 * A + 8) == kv.KVC_E_ALIAS          # status inside the workspace

@@ -10,7 +10,7 @@ from agent_handoff_amd import synth
 from agent_handoff_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
 from fractions import Fraction
 
-from brute import bf16_ulp, card_record_size, exact_round_to_bf16
+from brute import bf16_ulp, card_record_size, exact_round_to_bf16, exact_round_to_f32
 
 
 def _kv(shape, seed):
@@ -232,29 +232,27 @@ def _bf16_value(bits):
     return Fraction(float(bf16_bits_to_f32(np.array([bits], np.uint16))[0]))
 
 
-def test_card_dequant_is_the_exact_value_rounded_once():
-    """q * s + mn as a real number, rounded once to bf16 (ties to even):
-    random operands, and operands built so that q * s lies exactly halfway
-    between two bf16 values while mn nudges it by far less than a binary64
-    ulp (where forming the sum in binary64 first would round twice)."""
+def test_card_dequant_is_binary32_sum_then_bf16():
+    """q * s + mn rounded once to binary32 (q * s is exact), then to bf16,
+    both ties to even, by exact rational arithmetic: random operands, and
+    operands where the binary32 sum lies exactly halfway between two bf16
+    values (the second rounding then goes to the even neighbour, whatever
+    the discarded part of the exact sum)."""
     rng = np.random.default_rng(21)
     cases = []
     for _ in range(4000):
         q = int(rng.integers(0, 256))
         s = int(rng.integers(0x0001, 0x7C00))             # finite positive fp16
-        mn = int(rng.integers(0, 0x7F80)) | (int(rng.integers(0, 2)) << 15)  # finite bf16
+        mn = int(rng.integers(0x0080, 0x7F80)) | (int(rng.integers(0, 2)) << 15)  # normal bf16
         cases.append((q, s, mn))
-    # 3 * (1 + 2^-7) = 193.5 bf16 quanta in [2, 4): a tie; mn = +-2^-100 breaks it
+    # 3 * (1 + 2^-7) = 193.5 bf16 quanta in [2, 4): halfway; mn = +-2^-100 is lost in binary32
     s_tie = int(np.array([1.0078125], np.float16).view(np.uint16)[0])
     tiny = int(f32_to_bf16_bits(np.array([2.0 ** -100], np.float32))[0])
-    for q, s in [(3, s_tie), (5, s_tie), (129, s_tie)]:
-        cases += [(q, s, tiny), (q, s, tiny | 0x8000), (q, s, 0)]
+    for q in (3, 5, 129):
+        cases += [(q, s_tie, tiny), (q, s_tie, tiny | 0x8000), (q, s_tie, 0)]
     for q, s, mn in cases:
-        exact = Fraction(q) * _f16_value(s) + _bf16_value(mn)
-        want = int(exact_round_to_bf16(exact))
+        r32 = exact_round_to_f32(Fraction(q) * _f16_value(s) + _bf16_value(mn))
+        want = int(exact_round_to_bf16(Fraction(float(r32))))
         got = oracle.card_dequant(q, s, mn)
-        assert got == want or (exact == 0 and (got & 0x7FFF) == 0), (q, hex(s), hex(mn), hex(got), hex(want))
-    # the tie cases really go different ways
-    up = oracle.card_dequant(3, s_tie, tiny)
-    down = oracle.card_dequant(3, s_tie, tiny | 0x8000)
-    assert up == down + 1
+        assert got == want or (r32 == 0 and (got & 0x7FFF) == 0), (q, hex(s), hex(mn), hex(got), hex(want))
+    assert oracle.card_dequant(3, s_tie, tiny) == oracle.card_dequant(3, s_tie, tiny | 0x8000)
