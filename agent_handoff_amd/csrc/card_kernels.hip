@@ -41,6 +41,7 @@ struct ScanParams {
     int32_t* status;           // nullable
     uint32_t L, H, T, d;
     CardMetaDev meta;
+    const uint8_t* meta_src;   // transcode: card whose model ID and position offset are carried over
 };
 
 struct CardParams {
@@ -151,6 +152,10 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
                           ((uint32_t)(uint8_t)p.meta.model_id[c + 2] << 16) |
                           ((uint32_t)(uint8_t)p.meta.model_id[c + 3] << 24);
                 }
+        }
+        if (p.meta_src && (tid == 8 || tid == 9 || (tid >= 18 && tid < 34))) {
+            val = reinterpret_cast<const uint32_t*>(p.meta_src)[tid];
+            if (tid == 33) val &= 0x00FFFFFFu;  // at most 63 characters, NUL-terminated
         }
         hdr[tid] = val;
     }
@@ -304,6 +309,8 @@ __device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, ui
     }
     constexpr int PER = 32 / B;
     constexpr uint32_t MASK = (1u << B) - 1u;
+    // q*s + mn in binary32 with one rounding (q*s alone is exact), then bf16
+    // round to nearest even (pack_bf16x2)
     float y[32];
 #pragma unroll
     for (int w = 0; w < B; ++w)
@@ -382,6 +389,127 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     }
 }
 
+// ---------------------------------------------------------------- hop transcode
+//
+// One hop of a handoff chain: card_in re-encoded at new per-token widths
+// into card_out, equal byte for byte to unpacking it and packing the bf16
+// result again (the same exactly rounded values, then the same
+// quantisation), without the bf16 round trip through HBM. A wave takes one
+// token block of one stream, as in unpack: the input records' span comes
+// into LDS with coalesced loads, each lane rebuilds its group's 32 values
+// and quantises them at the new width into the output span in LDS, which
+// then goes out with coalesced stores.
+struct TranscodeParams {
+    const uint8_t* card_in;
+    uint8_t* card_out;
+    const uint8_t* w_in;   // card_in + 256
+    const uint8_t* w_out;  // new widths
+    const uint64_t* info_in;
+    const uint64_t* off_in;
+    const uint64_t* info_out;
+    const uint64_t* off_out;
+    uint32_t L, H, T, nbk;
+    uint64_t payload;  // the same for both cards (it depends on T only)
+    uint64_t n_waves;
+};
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(TranscodeParams p) {
+    constexpr uint32_t G = D / kCardGroup;  // lanes per token
+    constexpr uint32_t TPW = kWave / G;     // tokens per wave
+    const uint32_t lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    if (wave >= p.n_waves) return;
+    const uint64_t s = wave / p.nbk;
+    const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
+    const uint32_t tok = t0 + lane / G;
+    const uint32_t g = lane % G;
+    const bool valid = tok < p.T;
+    const uint32_t tc = valid ? tok : t0;
+    const uint32_t nv = (p.T - t0 < TPW) ? p.T - t0 : TPW;
+    const uint64_t flags = p.info_in[2] | p.info_out[2];
+    const uint64_t S_in = p.info_in[0], S_out = p.info_out[0];
+    const uint64_t a0 = p.off_in[t0], a1 = p.off_in[t0 + nv], my_a = p.off_in[tc];
+    const uint64_t b0 = p.off_out[t0], b1 = p.off_out[t0 + nv], my_b = p.off_out[tc];
+    const uint32_t w_in = p.w_in[tc], w_out = p.w_out[tc];
+    if (flags != 0) return;
+
+    __shared__ uint4 stage_in[kBlockThreads / kWave][kSpanChunks];
+    __shared__ uint4 stage_out[kBlockThreads / kWave][kSpanChunks];
+    uint4* si = stage_in[threadIdx.x / kWave];
+    uint4* so = stage_out[threadIdx.x / kWave];
+    {
+        const uint32_t n16 = (uint32_t)((a1 - a0) / 16);
+        const uint4* src = reinterpret_cast<const uint4*>(p.card_in + p.payload + s * S_in + a0);
+        uint4 c[kSpanChunks / kWave];
+#pragma unroll
+        for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
+            const uint32_t idx = kWave * j + lane;
+            c[j] = idx < n16 ? src[idx] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) si[kWave * j + lane] = c[j];
+    }
+    if (valid) {
+        // rebuild the group (as unpack does) ...
+        uint32_t o[16];
+        const uint8_t* rin = reinterpret_cast<const uint8_t*>(si) + (uint32_t)(my_a - a0);
+        if (w_in == 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rin + 64 * g)[i];
+        } else if (w_in == 2) {
+            dequant_group<2>(rin, G, g, o);
+        } else if (w_in == 4) {
+            dequant_group<4>(rin, G, g, o);
+        } else {
+            dequant_group<8>(rin, G, g, o);
+        }
+        // ... and quantise it at the new width (as pack does)
+        uint8_t* rout = reinterpret_cast<uint8_t*>(so) + (uint32_t)(my_b - b0);
+        if (w_out == 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rout + 64 * g)[i] = reinterpret_cast<const uint4*>(o)[i];
+        } else {
+            float x[32];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                x[2 * j] = bf16_lo(o[j]);
+                x[2 * j + 1] = bf16_hi(o[j]);
+            }
+            uint16_t sb, mb;
+            uint32_t codes[8];
+            if (w_out == 2) {
+                quant_group<2>(x, sb, mb, codes);
+                store_group<2>(rout, G, g, sb, mb, codes);
+            } else if (w_out == 4) {
+                quant_group<4>(x, sb, mb, codes);
+                store_group<4>(rout, G, g, sb, mb, codes);
+            } else {
+                quant_group<8>(x, sb, mb, codes);
+                store_group<8>(rout, G, g, sb, mb, codes);
+            }
+            // zero the record's tail padding (present for d = 64)
+            const uint32_t used = 4 * G + D * w_out / 8;
+            const uint32_t R = card_record_bytes(D, w_out);
+            if (g == 0)
+                for (uint32_t i = used; i < R; i += 8) *reinterpret_cast<uint2*>(rout + i) = make_uint2(0, 0);
+        }
+    }
+    // the output span, 16 bytes per lane per store
+    uint8_t* stream = p.card_out + p.payload + s * S_out;
+    const uint32_t n16 = (uint32_t)((b1 - b0) / 16);
+    uint4* dst = reinterpret_cast<uint4*>(stream + b0);
+#pragma unroll
+    for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
+        const uint32_t idx = kWave * j + lane;
+        if (idx < n16) dst[idx] = so[idx];
+    }
+    // zero the stream's tail padding after the last record
+    if (t0 + nv == p.T && lane == 0)
+        for (uint64_t i = p.off_out[p.T]; i < S_out; i += 16)
+            *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
 
 static CardParams card_params(const Shape& s, const void* ws) {
@@ -453,6 +581,63 @@ hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_by
     p.card_in = static_cast<const uint8_t*>(card);
     const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
     return launch_kernel(s.d == 64 ? card_unpack_kernel<64> : card_unpack_kernel<128>, dim3(nblocks),
+                         dim3(kBlockThreads), stream, p);
+}
+
+hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t card_in_bytes,
+                                 const uint8_t* new_widths, void* card_out, uint64_t capacity,
+                                 uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, hipStream_t stream) {
+    uint8_t* ws_in = static_cast<uint8_t*>(ws);
+    uint8_t* ws_out = ws_in + card_workspace_half(s.T);
+    // offsets of the input records (and a check of its header) ...
+    ScanParams a{};
+    a.widths = static_cast<const uint8_t*>(card_in) + kCardHeaderBytes;
+    a.card_in = static_cast<const uint8_t*>(card_in);
+    a.info = reinterpret_cast<uint64_t*>(ws_in);
+    a.off = reinterpret_cast<uint64_t*>(ws_in + kCardInfoBytes);
+    a.limit = card_in_bytes;
+    a.status = dev_status;
+    a.L = s.L;
+    a.H = s.H;
+    a.T = s.T;
+    a.d = s.d;
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, a);
+    if (e != hipSuccess) return e;
+    // ... and of the output's, whose header and widths are written with the
+    // input's model ID and position offset
+    ScanParams b{};
+    b.widths = new_widths;
+    b.card_out = static_cast<uint8_t*>(card_out);
+    b.info = reinterpret_cast<uint64_t*>(ws_out);
+    b.off = reinterpret_cast<uint64_t*>(ws_out + kCardInfoBytes);
+    b.limit = capacity;
+    b.dev_card_bytes = dev_card_bytes;
+    b.status = dev_status;
+    b.L = s.L;
+    b.H = s.H;
+    b.T = s.T;
+    b.d = s.d;
+    b.meta_src = static_cast<const uint8_t*>(card_in);
+    e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, b);
+    if (e != hipSuccess) return e;
+    const CardParams cp = card_params(s, ws);
+    TranscodeParams p{};
+    p.card_in = static_cast<const uint8_t*>(card_in);
+    p.card_out = static_cast<uint8_t*>(card_out);
+    p.w_in = a.widths;
+    p.w_out = new_widths;
+    p.info_in = a.info;
+    p.off_in = a.off;
+    p.info_out = b.info;
+    p.off_out = b.off;
+    p.L = s.L;
+    p.H = s.H;
+    p.T = s.T;
+    p.nbk = cp.nbk;
+    p.payload = cp.payload;
+    p.n_waves = cp.n_waves;
+    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    return launch_kernel(s.d == 64 ? card_transcode_kernel<64> : card_transcode_kernel<128>, dim3(nblocks),
                          dim3(kBlockThreads), stream, p);
 }
 

@@ -40,9 +40,7 @@ kvc::Shape to_shape(const kvc_shape* s) {
     return kvc::Shape{s->num_layers, s->num_kv_heads, s->num_tokens, s->head_dim};
 }
 
-uint64_t card_ws_bytes(const kvc_shape* s) {
-    return align_up(kvc::kCardInfoBytes + 8ull * ((uint64_t)s->num_tokens + 1), 256);
-}
+uint64_t card_ws_bytes(const kvc_shape* s) { return kvc::card_workspace_half(s->num_tokens); }
 
 uint32_t rd32(const uint8_t* p) { return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24; }
 uint64_t rd64(const uint8_t* p) { return (uint64_t)rd32(p) | (uint64_t)rd32(p + 4) << 32; }
@@ -168,6 +166,35 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
     m.position_offset = meta->position_offset;
     const hipError_t e = kvc::launch_card_pack(to_shape(shape), k, v, widths, m, card, card_capacity,
                                                dev_card_bytes, dev_status, ws, stream);
+    return e == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+size_t cachecard_transcode_workspace_bytes(const kvc_shape* shape) {
+    if (!card_shape(shape)) return 0;
+    return (size_t)(2 * card_ws_bytes(shape));
+}
+
+int cachecard_transcode(const kvc_shape* shape, const void* card_in, size_t card_in_bytes,
+                        const uint8_t* new_widths, void* card_out, size_t card_capacity, uint64_t* dev_card_bytes,
+                        int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!shape || !card_in || !new_widths || !card_out || !ws) return KVC_E_NULL;
+    if (!card_shape(shape)) return KVC_E_SHAPE;
+    const uint64_t ws_need = 2 * card_ws_bytes(shape), T = shape->num_tokens;
+    const uint64_t head = kvc::card_payload_offset(shape->num_tokens);
+    if (ws_bytes < ws_need || card_in_bytes < head || card_capacity < head) return KVC_E_SIZE;
+    if (!aligned(card_in, 256) || !aligned(card_out, 256) || !aligned(ws, 16) ||
+        (dev_card_bytes && !aligned(dev_card_bytes, 8)) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_E_ALIGN;
+    const void* outs[4] = {card_out, ws, dev_card_bytes, dev_status};
+    const uint64_t outn[4] = {card_capacity, ws_need, dev_card_bytes ? 8u : 0u, dev_status ? 4u : 0u};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], outn[i], card_in, card_in_bytes) || overlap(outs[i], outn[i], new_widths, T))
+            return KVC_E_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return KVC_E_ALIAS;
+    }
+    const hipError_t e = kvc::launch_card_transcode(to_shape(shape), card_in, card_in_bytes, new_widths, card_out,
+                                                    card_capacity, dev_card_bytes, dev_status, ws, stream);
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 

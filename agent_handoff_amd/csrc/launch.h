@@ -21,8 +21,10 @@ hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uin
                               int32_t* dev_status, hipStream_t stream);
 
 // CacheCard workspace: 256-byte info block {u64 S, u64 total, u32 flags},
-// then u64 record offsets[T + 1].
+// then u64 record offsets[T + 1], rounded up to 256 bytes. The transcode
+// uses two of these (input card, output card).
 constexpr uint64_t kCardInfoBytes = 256;
+inline uint64_t card_workspace_half(uint32_t T) { return (kCardInfoBytes + 8ull * ((uint64_t)T + 1) + 255) & ~255ull; }
 
 struct CardMetaDev {
     char model_id[64];
@@ -36,5 +38,9 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
 
 hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_bytes, void* k_out,
                               void* v_out, int32_t* dev_status, void* ws, hipStream_t stream);
+
+hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t card_in_bytes,
+                                 const uint8_t* new_widths, void* card_out, uint64_t capacity,
+                                 uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, hipStream_t stream);
 
 }  // namespace kvc

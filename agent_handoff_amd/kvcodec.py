@@ -61,6 +61,8 @@ def _load():
         "cachecard_workspace_bytes": (sz, [sp]),
         "cachecard_pack": (i32, [sp, p, p, p, ctypes.POINTER(kvc_card_meta), p, sz, p, p, p, sz, p]),
         "cachecard_unpack": (i32, [sp, p, sz, p, p, p, p, sz, p]),
+        "cachecard_transcode_workspace_bytes": (sz, [sp]),
+        "cachecard_transcode": (i32, [sp, p, sz, p, p, sz, p, p, p, sz, p]),
         "kvc_parse_header": (i32, [p, sz, sp, ctypes.POINTER(u32)]),
         "kvc_strerror": (ctypes.c_char_p, [i32]),
         "kvc_codebook": (None, [p, p]),
@@ -75,7 +77,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_decode",
             "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
-            "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack", "kvc_parse_header",
+            "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack",
+            "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_parse_header",
             "kvc_strerror", "kvc_codebook")
 
 
@@ -190,6 +193,20 @@ def cachecard_unpack(shape, card, k_out, v_out, ws, card_bytes=None, dev_status=
     n = _nbytes(card) if card_bytes is None else int(card_bytes)
     _check(_lib.cachecard_unpack(ctypes.byref(_shape(shape)), _ptr(card), n, _ptr(k_out), _ptr(v_out),
                                  _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_unpack")
+
+
+def cachecard_transcode_workspace_bytes(shape):
+    return int(_lib.cachecard_transcode_workspace_bytes(ctypes.byref(_shape(shape))))
+
+
+def cachecard_transcode(shape, card_in, new_widths, card_out, ws, card_in_bytes=None, dev_card_bytes=None,
+                        dev_status=None, stream=None):
+    """card_in, card_out, ws: uint8 device buffers; new_widths: uint8 [T]
+    device tensor; dev_card_bytes: int64 device tensor of 1 element or None."""
+    n = _nbytes(card_in) if card_in_bytes is None else int(card_in_bytes)
+    _check(_lib.cachecard_transcode(ctypes.byref(_shape(shape)), _ptr(card_in), n, _ptr(new_widths),
+                                    _ptr(card_out), _nbytes(card_out), _ptr(dev_card_bytes), _ptr(dev_status),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_transcode")
 
 
 # ------------------------------------------------------------------ host utils

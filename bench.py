@@ -174,6 +174,21 @@ def main():
     b1 = pool_b + 2 * kv_bytes
     ops_out["decode_1_agent"] = {"us": round(t1 * 1e6, 2), "bytes": b1, "GB/s": round(b1 / t1 / 1e9, 1),
                                  "frac_hbm_peak": round(b1 / t1 / 1e9 / HBM_PEAK_GBS, 4)}
+    # one hop of a card chain: the step's card re-encoded at the next agent's widths
+    w_next_np = synth.card_widths(synth.WORKLOADS[4], args.seed + 1, T=T)
+    w_next = torch.from_numpy(w_next_np).to(dev)
+    card2_n = kv.cachecard_bytes_host(shape, w_next_np)
+    card2 = torch.empty(card2_n, dtype=torch.uint8, device=dev)
+    tws = torch.empty(kv.cachecard_transcode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    tt = timed(lambda: kv.cachecard_transcode(shape, card, w_next, card2, tws, card_in_bytes=card_n, dev_status=status,
+                                              stream=stream), 10)
+    bt = card_n + card2_n
+    ops_out["transcode"] = {"us": round(tt * 1e6, 2), "bytes": bt, "GB/s": round(bt / tt / 1e9, 1),
+                            "frac_hbm_peak": round(bt / tt / 1e9 / HBM_PEAK_GBS, 4)}
+    drift = hop_drift(kv, synth, k, v, shape, widths_np, args.seed, stream, dev)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set beside the step"
+
     half = alg["decode"] // 2 // 4096 * 4096
     cs = torch.empty(half, dtype=torch.uint8, device=dev)
     cd = torch.empty_like(cs)
@@ -229,10 +244,51 @@ def main():
         "ops": ops_out,
         "step_ms_events": round(med(step_s) * 1e3, 4),
         "copy_ceiling": copy_ceiling,
+        "hop_drift": drift,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def hop_drift(kv, synth, k, v, shape, widths_np, seed, stream, dev, hops=5):
+    """Reconstruction error of a card passed along a chain of agents, each
+    re-encoding it at its own widths (cachecard_transcode, then unpack to
+    measure): sum of squared errors over sum of squares of the original K
+    and V, after 0..hops hops, for uniform 4-bit, for one fixed mix of
+    widths, and for a mix redrawn at every hop."""
+    import numpy as np
+    import torch
+    L, H, T, d = shape
+    ref = torch.stack([k.float(), v.float()])
+    den = float((ref * ref).sum())
+    card_cap = kv.cachecard_max_bytes(shape)
+    cards = [torch.empty(card_cap, dtype=torch.uint8, device=dev) for _ in range(2)]
+    cws = torch.empty(kv.cachecard_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    tws = torch.empty(kv.cachecard_transcode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    schemes = {"uniform_4": lambda h: np.full(T, 4, np.uint8),
+               "mixed_fixed": lambda h: widths_np,
+               "mixed_redrawn": lambda h: synth.card_widths(synth.WORKLOADS[4], seed + 100 + h, T=T)}
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, wf in schemes.items():
+            errs = []
+            for h in range(hops + 1):
+                w_np = wf(h)
+                w = torch.from_numpy(w_np).to(dev)
+                n = kv.cachecard_bytes_host(shape, w_np)
+                cur, prev = cards[h % 2], cards[(h + 1) % 2]
+                if h == 0:
+                    kv.cachecard_pack(shape, k, v, w, cur, cws, b"chain", 0, stream=stream)
+                else:
+                    kv.cachecard_transcode(shape, prev, w, cur, tws, card_in_bytes=prev_n, stream=stream)
+                kv.cachecard_unpack(shape, cur, ko, vo, cws, card_bytes=n, stream=stream)
+                diff = torch.stack([ko.float(), vo.float()]) - ref
+                errs.append(float((diff * diff).sum()) / den)
+                prev_n = n
+            out[name] = [float(f"{e:.4e}") for e in errs]
+    return {"metric": "relative reconstruction MSE after 0..5 hops", **out}
 
 
 CALIBRATION_BYTES = 1 << 30

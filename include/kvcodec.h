@@ -181,7 +181,8 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
                    hipStream_t stream);
 
 /* Rebuild bf16 K and V from a CacheCard (QKVShare item 3: full-width
- * past_key_values for the receiver): x = bf16(q * s + mn), width 16 copies.
+ * past_key_values for the receiver): x = bf16(fmaf(q, s, mn)), the binary32
+ * value rounded to nearest even; width 16 copies.
  *   card        device, card_bytes valid bytes, read only
  *   k_out, v_out device bf16 [L][H][T][d]
  *   dev_status  device int32 or NULL; KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH
@@ -190,6 +191,34 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
 int cachecard_unpack(const kvc_shape* shape, const void* card, size_t card_bytes, void* k_out,
                      void* v_out, int32_t* dev_status, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* Workspace bytes needed by cachecard_transcode (two sets of record
+ * offsets: the input card's and the output card's). */
+size_t cachecard_transcode_workspace_bytes(const kvc_shape* shape);
+
+/* One hop of a handoff chain (QKVShare: each agent forwards the cache as a
+ * card at its own per-token widths; the pages call for a fused card-to-card
+ * path): card_in re-encoded at new_widths into card_out without bf16 K/V
+ * in between. The result equals, byte for byte, cachecard_unpack followed
+ * by cachecard_pack at new_widths, with card_in's model ID and position
+ * offset carried into the new header.
+ *   card_in         device, card_in_bytes valid bytes, 256-byte aligned, read
+ *                   only; its header must match shape
+ *   new_widths      device u8[T], each 2, 4, 8 or 16
+ *   card_out        device, card_capacity bytes, 256-byte aligned; header,
+ *                   widths and payload written (cachecard_bytes_host of
+ *                   new_widths gives the exact size)
+ *   dev_card_bytes  device u64 or NULL; receives card_out's exact size
+ *   dev_status      device int32 or NULL; KVC_DEV_BAD_HEADER (card_in),
+ *                   KVC_DEV_BAD_WIDTH (either card), KVC_DEV_CAPACITY; on a
+ *                   nonzero status card_out's payload is unspecified
+ *   ws              device workspace, >= cachecard_transcode_workspace_bytes
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
+ * KVC_E_HIP. */
+int cachecard_transcode(const kvc_shape* shape, const void* card_in, size_t card_in_bytes,
+                        const uint8_t* new_widths, void* card_out, size_t card_capacity,
+                        uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* --------------------------------------------------------------- host utils */
 
