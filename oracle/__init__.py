@@ -71,6 +71,8 @@ def lib():
         L.or_card_unpack.argtypes = [u32] * 4 + [p, u64, p, p]
         L.or_card_dequant.restype = ctypes.c_uint16
         L.or_card_dequant.argtypes = [u32, ctypes.c_uint16, ctypes.c_uint16]
+        L.or_realign_keys.restype = ctypes.c_int
+        L.or_realign_keys.argtypes = [u32] * 4 + [p, p, i64, p, u32]
         L.or_set_threads.restype = None
         L.or_set_threads.argtypes = [ctypes.c_int]
         L.or_max_threads.restype = ctypes.c_int
@@ -254,6 +256,24 @@ def card_transcode(card, shape, new_widths):
     k, v = card_unpack(card, shape)
     model_id, position_offset = card_meta(card)
     return card_pack(k, v, new_widths, model_id, position_offset)
+
+
+# ---------------------------------------------------------------- key re-alignment
+
+def realign_keys(k, delta, inv_freq, pairing=0):
+    """k: uint16 bf16 bits [L, H, T, d]; rotate every channel pair j by
+    delta * inv_freq[j] (pairs (j, j + d/2) for pairing 0, (2j, 2j + 1) for
+    pairing 1); returns new bf16 bits."""
+    L, H, T, d = k.shape
+    k = _check_bf16(k, (L, H, T, d))
+    f = np.ascontiguousarray(inv_freq, np.float32)
+    if f.size != d // 2 or d > 256:
+        raise ValueError("inv_freq must hold d/2 values, d <= 256")
+    out = np.zeros_like(k)
+    rc = lib().or_realign_keys(L, H, T, d, _ptr(k), _ptr(out), int(delta), _ptr(f), int(pairing))
+    if rc:
+        raise ValueError(f"or_realign_keys failed: {rc}")
+    return out
 
 
 # ---------------------------------------------------------------- scalar formats

@@ -604,3 +604,48 @@ int or_card_unpack(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uint8_t
     free(rec_off);
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Key position re-alignment (KVCMAS procedure: a shared segment's key  */
+/* positions are re-aligned to the target's before reuse; the card      */
+/* carries the source position offset, QKVShare item 2). Rotary keys at */
+/* position p hold each channel pair rotated by p * f_j; moving them by */
+/* delta positions rotates pair j by delta * f_j more. Pairs are        */
+/* (j, j + d/2) (pairing 0, halves) or (2j, 2j + 1) (pairing 1,         */
+/* adjacent); f_j are the model's inverse frequencies (an input).       */
+/* Computed in binary64, rounded once to bf16.                          */
+/* ------------------------------------------------------------------ */
+int or_realign_keys(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uint16_t* k_in, uint16_t* k_out,
+                    int64_t delta, const float* inv_freq, uint32_t pairing) {
+    if (d == 0 || d % 2 || pairing > 1) return OR_E_ARG;
+    uint32_t half = d / 2;
+    double* c = (double*)malloc(sizeof(double) * half);
+    double* s = (double*)malloc(sizeof(double) * half);
+    if (!c || !s) {
+        free(c);
+        free(s);
+        return OR_E_ARG;
+    }
+    for (uint32_t j = 0; j < half; ++j) {
+        double phi = (double)delta * (double)inv_freq[j];
+        c[j] = cos(phi);
+        s[j] = sin(phi);
+    }
+    int64_t vecs = (int64_t)L * H * T;
+    #pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < vecs; ++v) {
+        const uint16_t* x = k_in + (uint64_t)v * d;
+        uint16_t* y = k_out + (uint64_t)v * d;
+        uint16_t tmp[256];
+        for (uint32_t j = 0; j < half; ++j) {
+            uint32_t ia = pairing == 0 ? j : 2 * j, ib = pairing == 0 ? j + half : 2 * j + 1;
+            double a = (double)or_bf16_to_f32(x[ia]), b = (double)or_bf16_to_f32(x[ib]);
+            tmp[ia] = or_f64_to_bf16(a * c[j] - b * s[j]);
+            tmp[ib] = or_f64_to_bf16(a * s[j] + b * c[j]);
+        }
+        memcpy(y, tmp, sizeof(uint16_t) * d);
+    }
+    free(c);
+    free(s);
+    return OR_OK;
+}
