@@ -6,6 +6,7 @@
 // GPU.
 #include "kvcodec.h"
 
+#include <math.h>
 #include <string.h>
 
 #include "codebook.h"
@@ -166,6 +167,24 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
     m.position_offset = meta->position_offset;
     const hipError_t e = kvc::launch_card_pack(to_shape(shape), k, v, widths, m, card, card_capacity,
                                                dev_card_bytes, dev_status, ws, stream);
+    return e == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int64_t delta, const float* inv_freq,
+                     uint32_t pairing, hipStream_t stream) {
+    if (!shape || !k_in || !k_out || !inv_freq) return KVC_E_NULL;
+    if (!pool_shape(shape)) return KVC_E_SHAPE;
+    if (pairing > 1) return KVC_E_RANGE;
+    if (!aligned(k_in, 16) || !aligned(k_out, 16)) return KVC_E_ALIGN;
+    const uint64_t kb = kv_bytes(shape);
+    if (k_in != k_out && overlap(k_in, kb, k_out, kb)) return KVC_E_ALIAS;
+    double c[kvc::kMaxRealignPairs], s[kvc::kMaxRealignPairs];
+    for (uint32_t j = 0; j < shape->head_dim / 2; ++j) {
+        const double phi = (double)delta * (double)inv_freq[j];
+        c[j] = cos(phi);
+        s[j] = sin(phi);
+    }
+    const hipError_t e = kvc::launch_realign_keys(to_shape(shape), k_in, k_out, c, s, pairing, stream);
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 

@@ -43,4 +43,10 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
                                  const uint8_t* new_widths, void* card_out, uint64_t capacity,
                                  uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, hipStream_t stream);
 
+// Key re-alignment: at most 64 channel pairs (d <= 128); cos and sin of
+// delta * f_j per pair, binary64.
+constexpr int kMaxRealignPairs = 64;
+hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, const double* cos_tab,
+                               const double* sin_tab, uint32_t pairing, hipStream_t stream);
+
 }  // namespace kvc

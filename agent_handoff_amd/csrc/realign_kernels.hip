@@ -1,0 +1,120 @@
+// realign_kernels.hip - key position re-alignment for gfx950.
+//
+// KVCMAS (cache reuse across agents), procedure: before a shared segment's
+// cache is reused by another agent, its key positions are re-aligned to the
+// target's; a QKVShare CacheCard carries the source position offset for
+// this. Rotary keys at position p hold each channel pair j rotated by
+// p * f_j, so moving them by delta positions rotates pair j by delta * f_j
+// more. The pairing of channels and the inverse frequencies f_j belong to
+// the model and are inputs; cos and sin of delta * f_j arrive from the host
+// in binary64 as kernel arguments. Each rotated value is a*c - b*s (or
+// a*s + b*c) in binary64, two products and a difference, then rounded once
+// to bf16: binary32 cos and sin lose too much when the two products nearly
+// cancel.
+//
+// Work mapping: a lane rotates 8 channel pairs of one vector, so d/16 lanes
+// cover a vector (8 vectors per wave at d = 128); every access is a 16-byte
+// load or store, in place allowed (a lane reads its chunks before writing
+// them, and no chunk is shared between lanes).
+#include "kernels_common.h"
+#include "launch.h"
+
+namespace kvc {
+namespace {
+
+struct RealignParams {
+    const uint16_t* k_in;
+    uint16_t* k_out;
+    uint64_t vecs;      // L * H * T
+    uint32_t pairing;   // 0: (j, j + d/2); 1: (2j, 2j + 1)
+    double c[kMaxRealignPairs];
+    double s[kMaxRealignPairs];
+};
+
+// Binary64 to bf16, round to nearest even, with one correct rounding: the
+// value is first rounded to binary32 by round-to-odd (round to nearest, then,
+// if inexact and the result is even, one step towards the exact value), which
+// keeps the information the second rounding needs (binary32 has more than
+// 8 + 2 significant bits), then rounded to bf16 by the hardware conversion.
+__device__ __forceinline__ float to_odd_binary32(double x) {
+    const float r = (float)x;
+    uint32_t u = __float_as_uint(r);
+    if ((double)r != x && (u & 1u) == 0u) {
+        if (r == 0.0f)
+            u = x < 0.0 ? 0x80000001u : 1u;
+        else
+            u += ((x > (double)r) == (r > 0.0f)) ? 1u : 0xFFFFFFFFu;
+    }
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ void rotate_pair(float a, float b, double c, double s, float& ra, float& rb) {
+    const double da = a, db = b;
+    ra = to_odd_binary32(da * c - db * s);
+    rb = to_odd_binary32(da * s + db * c);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void realign_keys_kernel(RealignParams p) {
+    constexpr uint32_t LPV = D / 16;         // lanes per vector (8 pairs each)
+    constexpr uint32_t VPW = kWave / LPV;    // vectors per wave
+    const uint32_t lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    const uint64_t vec = wave * VPW + lane / LPV;
+    if (vec >= p.vecs) return;
+    const uint32_t i = lane % LPV;           // pairs 8i .. 8i + 7
+    const uint16_t* x = p.k_in + vec * D;
+    uint16_t* y = p.k_out + vec * D;
+    // chunk A holds the 8 first members, chunk B the 8 second members (halves),
+    // or the two chunks hold 8 interleaved pairs (adjacent)
+    const uint32_t oa = p.pairing == 0 ? 8 * i : 16 * i;
+    const uint32_t ob = p.pairing == 0 ? D / 2 + 8 * i : 16 * i + 8;
+    const uint4 A = *reinterpret_cast<const uint4*>(x + oa);
+    const uint4 B = *reinterpret_cast<const uint4*>(x + ob);
+    const uint32_t wa[4] = {A.x, A.y, A.z, A.w}, wb[4] = {B.x, B.y, B.z, B.w};
+    uint32_t ra[4], rb[4];
+    if (p.pairing == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float a0, b0, a1, b1;
+            rotate_pair(bf16_lo(wa[t]), bf16_lo(wb[t]), p.c[8 * i + 2 * t], p.s[8 * i + 2 * t], a0, b0);
+            rotate_pair(bf16_hi(wa[t]), bf16_hi(wb[t]), p.c[8 * i + 2 * t + 1], p.s[8 * i + 2 * t + 1], a1, b1);
+            ra[t] = pack_bf16x2(a0, a1);
+            rb[t] = pack_bf16x2(b0, b1);
+        }
+    } else {
+        // word t of a chunk is one pair (first member low, second high)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float a0, b0, a1, b1;
+            rotate_pair(bf16_lo(wa[t]), bf16_hi(wa[t]), p.c[8 * i + t], p.s[8 * i + t], a0, b0);
+            rotate_pair(bf16_lo(wb[t]), bf16_hi(wb[t]), p.c[8 * i + 4 + t], p.s[8 * i + 4 + t], a1, b1);
+            ra[t] = pack_bf16x2(a0, b0);
+            rb[t] = pack_bf16x2(a1, b1);
+        }
+    }
+    *reinterpret_cast<uint4*>(y + oa) = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    *reinterpret_cast<uint4*>(y + ob) = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+}  // namespace
+
+hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, const double* cos_tab,
+                               const double* sin_tab, uint32_t pairing, hipStream_t stream) {
+    RealignParams p{};
+    p.k_in = static_cast<const uint16_t*>(k_in);
+    p.k_out = static_cast<uint16_t*>(k_out);
+    p.vecs = (uint64_t)s.L * s.H * s.T;
+    p.pairing = pairing;
+    for (uint32_t j = 0; j < s.d / 2; ++j) {
+        p.c[j] = cos_tab[j];
+        p.s[j] = sin_tab[j];
+    }
+    const uint32_t vpw = kWave / (s.d / 16);
+    const uint64_t waves = (p.vecs + vpw - 1) / vpw;
+    const uint32_t nblocks = (uint32_t)((waves + 3) / 4);
+    return launch_kernel(s.d == 64 ? realign_keys_kernel<64> : realign_keys_kernel<128>, dim3(nblocks),
+                         dim3(kBlockThreads), stream, p);
+}
+
+}  // namespace kvc

@@ -63,6 +63,7 @@ def _load():
         "cachecard_unpack": (i32, [sp, p, sz, p, p, p, p, sz, p]),
         "cachecard_transcode_workspace_bytes": (sz, [sp]),
         "cachecard_transcode": (i32, [sp, p, sz, p, p, sz, p, p, p, sz, p]),
+        "kvc_realign_keys": (i32, [sp, p, p, ctypes.c_int64, p, u32, p]),
         "kvc_parse_header": (i32, [p, sz, sp, ctypes.POINTER(u32)]),
         "kvc_strerror": (ctypes.c_char_p, [i32]),
         "kvc_codebook": (None, [p, p]),
@@ -78,7 +79,7 @@ _lib = _load()
 EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_decode",
             "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
             "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack",
-            "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_parse_header",
+            "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_realign_keys", "kvc_parse_header",
             "kvc_strerror", "kvc_codebook")
 
 
@@ -207,6 +208,20 @@ def cachecard_transcode(shape, card_in, new_widths, card_out, ws, card_in_bytes=
     _check(_lib.cachecard_transcode(ctypes.byref(_shape(shape)), _ptr(card_in), n, _ptr(new_widths),
                                     _ptr(card_out), _nbytes(card_out), _ptr(dev_card_bytes), _ptr(dev_status),
                                     _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_transcode")
+
+
+KVC_ROPE_HALVES, KVC_ROPE_ADJACENT = 0, 1
+
+
+def kvc_realign_keys(shape, k_in, k_out, delta, inv_freq, pairing=KVC_ROPE_HALVES, stream=None):
+    """k_in, k_out: bf16 device tensors [L, H, T, d] (the same tensor for in
+    place); inv_freq: d/2 host floats."""
+    f = np.ascontiguousarray(inv_freq, np.float32)
+    if f.size != shape[3] // 2:
+        raise ValueError("inv_freq must hold d/2 values")
+    _check(_lib.kvc_realign_keys(ctypes.byref(_shape(shape)), _ptr(k_in), _ptr(k_out), int(delta),
+                                 f.ctypes.data_as(ctypes.c_void_p), int(pairing), _stream(stream)),
+           "kvc_realign_keys")
 
 
 # ------------------------------------------------------------------ host utils

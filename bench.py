@@ -185,6 +185,12 @@ def main():
     bt = card_n + card2_n
     ops_out["transcode"] = {"us": round(tt * 1e6, 2), "bytes": bt, "GB/s": round(bt / tt / 1e9, 1),
                             "frac_hbm_peak": round(bt / tt / 1e9 / HBM_PEAK_GBS, 4)}
+    # key position re-alignment of the shared keys by 4096 positions (rotary
+    # frequencies of the Llama-3 family: base 500000 over d channels)
+    inv_freq = (500000.0 ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d)).astype(np.float32)
+    tr = timed(lambda: kv.kvc_realign_keys(shape, k, k_rt, 4096, inv_freq, stream=stream), 10)
+    ops_out["realign_keys"] = {"us": round(tr * 1e6, 2), "bytes": 2 * kv_bytes, "GB/s": round(2 * kv_bytes / tr / 1e9, 1),
+                               "frac_hbm_peak": round(2 * kv_bytes / tr / 1e9 / HBM_PEAK_GBS, 4)}
     drift = hop_drift(kv, synth, k, v, shape, widths_np, args.seed, stream, dev)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set beside the step"

@@ -220,6 +220,32 @@ int cachecard_transcode(const kvc_shape* shape, const void* card_in, size_t card
                         uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ------------------------------------------------------- key re-alignment */
+
+/* Pairing of rotary channels: pair j is (j, j + d/2) or (2j, 2j + 1). */
+#define KVC_ROPE_HALVES 0u
+#define KVC_ROPE_ADJACENT 1u
+
+/* Re-align the positions of rotary keys (KVCMAS, procedure: the key
+ * positions of a shared segment are re-aligned to the target agent's before
+ * reuse; a CacheCard carries the source position offset, QKVShare item 2).
+ * Keys at position p hold channel pair j rotated by p * inv_freq[j];
+ * re-aligning by delta rotates every pair j of every key vector by
+ * delta * inv_freq[j] more.
+ *   k_in, k_out  device bf16 [L][H][T][d], d = 64 or 128, 16-byte aligned;
+ *                k_out == k_in re-aligns in place, any other overlap is an
+ *                error
+ *   delta        target position minus source position
+ *   inv_freq     host, d/2 floats: the model's rotary inverse frequencies
+ *   pairing      KVC_ROPE_HALVES or KVC_ROPE_ADJACENT
+ * cos and sin of delta * inv_freq[j] are taken in binary64 on the host; each
+ * rotated value is a*c - b*s or a*s + b*c in binary64 (two products, then
+ * the sum), rounded once to bf16, ties to even.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_RANGE (pairing), KVC_E_ALIGN,
+ * KVC_E_ALIAS, KVC_E_HIP. */
+int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int64_t delta,
+                     const float* inv_freq, uint32_t pairing, hipStream_t stream);
+
 /* --------------------------------------------------------------- host utils */
 
 /* Parse a pool or card header from host bytes; *kind = 1 (pool) or 2

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -210,3 +210,21 @@ def test_transcode_argument_errors():
     assert tc(ws=5 * A + 512) == kv.KVC_E_ALIAS            # workspace inside the output card
     assert tc(card_out=2 * A) == kv.KVC_E_ALIAS            # output over the new widths
     assert tc(status=4 * A + 8) == kv.KVC_E_ALIAS          # status inside the workspace
+
+
+@fake_addresses
+def test_realign_argument_errors():
+    f = np.ones(64, np.float32)
+    fp = f.ctypes.data_as(ctypes.c_void_p)
+
+    def ra(shape=S, k_in=A, k_out=2 * A, freq=fp, pairing=0):
+        return L.kvc_realign_keys(ctypes.byref(shape) if shape is not None else None, k_in, k_out, 5, freq,
+                                  pairing, None)
+
+    assert ra(shape=None) == kv.KVC_E_NULL
+    assert ra(k_in=None) == kv.KVC_E_NULL
+    assert ra(freq=None) == kv.KVC_E_NULL
+    assert ra(shape=kv.kvc_shape(2, 2, 32, 96)) == kv.KVC_E_SHAPE
+    assert ra(pairing=2) == kv.KVC_E_RANGE
+    assert ra(k_out=2 * A + 8) == kv.KVC_E_ALIGN
+    assert ra(k_out=A + 1024) == kv.KVC_E_ALIAS     # partial overlap (in place means the same address)
