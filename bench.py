@@ -300,7 +300,8 @@ def hop_drift(kv, synth, k, v, shape, widths_np, seed, stream, dev, hops=5):
 CALIBRATION_BYTES = 1 << 30
 CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_kernel",
                  "key_absmax_kernel",
-                 "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel"]
+                 "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
+                 "card_transcode_kernel", "realign_keys_kernel"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
