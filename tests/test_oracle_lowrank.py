@@ -1,0 +1,95 @@
+"""Pins of the low-rank anchor oracle (KVCMAS: base caches and delta
+corrections stored as truncated SVDs, Z ~ A B with A = U_r S_r, B = R_r^T;
+the target cache materialised as the aligned source plus a weighted sum of
+the stored low-rank corrections)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from agent_handoff_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+from brute import exact_round_to_bf16
+from oracle import lowrank
+
+
+def _bf(x):
+    return f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _f(b):
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def test_round_bf16_is_exact_rounding():
+    rng = np.random.default_rng(0)
+    x = list(rng.standard_normal(3000) * np.exp(rng.standard_normal(3000) * 10))
+    x += [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -126, 2 ** -130, 0.0, 3.3e38, 1e-45]
+    x += [float(Fraction(257, 256) + Fraction(1, 2 ** 60))]
+    got = lowrank.round_bf16(np.array(x))
+    for v, g in zip(x, got):
+        assert g == exact_round_to_bf16(Fraction(v)) or (v == 0 and (g & 0x7FFF) == 0), v
+
+
+def test_matrix_view_of_the_cache_layout():
+    x = np.arange(3 * 5 * 4, dtype=np.uint16).reshape(3, 5, 4)  # [H][T][d]
+    m = lowrank.as_matrix(x)
+    assert m.shape == (5, 12) and m[2, 1 * 4 + 3] == x[1, 2, 3]
+    assert np.array_equal(lowrank.from_matrix(m, 3, 4), x)
+
+
+def test_singular_values_agree_with_an_eigendecomposition():
+    rng = np.random.default_rng(1)
+    z = _bf(rng.standard_normal((48, 80)))
+    _, _, s = lowrank.factor(z, 8)
+    ev = np.sort(np.linalg.eigvalsh(_f(z).T @ _f(z)))[::-1][:48]
+    assert np.allclose(s, np.sqrt(np.maximum(ev, 0)), rtol=1e-9, atol=1e-9 * s[0])
+
+
+def test_truncation_error_is_eckart_young():
+    """||Z - A B||_F equals the norm of the dropped singular values, up to
+    the rounding of the stored bf16 factors."""
+    rng = np.random.default_rng(2)
+    z = _bf(rng.standard_normal((96, 64)) * np.exp(-np.arange(64) / 8.0))
+    for r in (4, 16, 32):
+        a, b, s = lowrank.factor(z, r)
+        err = np.linalg.norm(_f(z) - _f(a) @ _f(b))
+        tail = np.sqrt(np.sum(s[r:] ** 2))
+        assert abs(err - tail) <= 2 ** -7 * np.linalg.norm(_f(z)), (r, err, tail)
+
+
+def test_low_rank_matrix_is_recovered():
+    rng = np.random.default_rng(3)
+    z = _bf(rng.standard_normal((64, 5)) @ rng.standard_normal((5, 96)))
+    a, b, s = lowrank.factor(z, 32)
+    assert np.all(s[5:] < 2 ** -8 * s[0])      # what remains is the bf16 rounding of z itself
+    assert np.allclose(_f(a) @ _f(b), _f(z), atol=2 ** -6 * np.abs(_f(z)).max())
+
+
+def test_materialize_brute_force_and_identities():
+    rng = np.random.default_rng(4)
+    T, D, r, V = 6, 10, 3, 2
+    src = _bf(rng.standard_normal((T, D)))
+    a = _bf(rng.standard_normal((V, T, r)))
+    b = _bf(rng.standard_normal((V, r, D)))
+    w = np.array([0.75, -1.5], np.float32)
+    got = lowrank.materialize(src, a, b, w)
+    for i in range(T):
+        for j in range(D):
+            x = Fraction(float(_f(src)[i, j]))
+            for v in range(V):
+                x += Fraction(float(w[v])) * sum(Fraction(float(_f(a)[v, i, k])) * Fraction(float(_f(b)[v, k, j]))
+                                              for k in range(r))
+            assert got[i, j] == exact_round_to_bf16(x)
+    assert np.array_equal(lowrank.materialize(src, a, b, np.zeros(V, np.float32)), src)
+
+
+def test_materialize_is_linear_in_the_weights():
+    rng = np.random.default_rng(5)
+    src = _bf(rng.standard_normal((32, 40)))
+    a = _bf(rng.standard_normal((1, 32, 8)))
+    b = _bf(rng.standard_normal((1, 8, 40)))
+    two = lowrank.materialize(src, np.concatenate([a, a]), np.concatenate([b, b]), np.array([0.25, 0.5], np.float32))
+    one = lowrank.materialize(src, a, b, np.array([0.75], np.float32))
+    d = np.abs(_f(two) - _f(one))
+    assert np.all(d <= 2 ** -7 * np.maximum(np.abs(_f(one)), 1e-30))
