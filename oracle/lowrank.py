@@ -8,9 +8,10 @@ TEST INFRASTRUCTURE, like the rest of this package (see oracle/__init__.py).
 
 A matrix Z here is one layer's K or V of one cache: T rows (tokens) by H*d
 columns (heads x channels), read from the cache layout [H][T][d]. Factors
-are stored as bf16: A = U_r S_r (T x r), B = R_r^T (r x H*d). Everything is
-computed in binary64 (numpy's SVD, a library primitive, for the
-factorisation) and rounded once to bf16 where a bf16 is stored.
+are stored as bf16, both row-major: A = U_r S_r (T x r) and R = R_r
+(H*d x r), so that Z ~ A R^T. Everything is computed in binary64 (numpy's
+SVD, a library primitive, for the factorisation) and rounded once to bf16
+where a bf16 is stored.
 """
 
 import numpy as np
@@ -53,22 +54,33 @@ def from_matrix(m, H, d):
 
 
 def factor(z_bits, r):
-    """Truncated SVD of the T x D matrix z (bf16 bits): returns (A, B) bf16
-    bits, A = U_r S_r (T x r), B = R_r^T (r x D), and the singular values."""
+    """Truncated SVD of the T x D matrix z (bf16 bits): returns (A, R) bf16
+    bits, A = U_r S_r (T x r), R = R_r (D x r), and the singular values."""
     z = bf16_bits_to_f32(z_bits).astype(np.float64)
     u, s, vt = np.linalg.svd(z, full_matrices=False)
     a = u[:, :r] * s[:r]
-    b = vt[:r, :]
-    return round_bf16(a), round_bf16(b), s
+    rr = vt[:r, :].T
+    return round_bf16(a), round_bf16(rr), s
 
 
-def materialize(src_bits, a_bits, b_bits, w):
-    """bf16(src + sum_v w_v A_v B_v) for src T x D, A [V][T][r], B [V][r][D],
-    w [V] (binary32 weights), in binary64, rounded once."""
+def materialize(src_bits, a_bits, r_bits, w):
+    """bf16(src + sum_v w_v A_v R_v^T) for src T x D, A [V][T][r],
+    R [V][D][r], w [V] (binary32 weights), in binary64, rounded once."""
     src = bf16_bits_to_f32(src_bits).astype(np.float64)
     acc = src.copy()
     for v in range(len(w)):
         av = bf16_bits_to_f32(a_bits[v]).astype(np.float64)
-        bv = bf16_bits_to_f32(b_bits[v]).astype(np.float64)
-        acc += float(np.float32(w[v])) * (av @ bv)
+        rv = bf16_bits_to_f32(r_bits[v]).astype(np.float64)
+        acc += float(np.float32(w[v])) * (av @ rv.T)
     return round_bf16(acc)
+
+
+def materialize_cache(src, a, r, w):
+    """The whole cache: src bf16 bits [L][H][T][d] (one of K or V), factors
+    A [L][V][T][r] and R [L][V][H*d][r], weights [L][V]; per layer the
+    matrix view materialised, back in the cache layout."""
+    L, H, T, d = src.shape
+    out = np.empty_like(src)
+    for l in range(L):
+        out[l] = from_matrix(materialize(as_matrix(src[l]), a[l], r[l], w[l]), H, d)
+    return out

@@ -1,5 +1,5 @@
 """Pins of the low-rank anchor oracle (KVCMAS: base caches and delta
-corrections stored as truncated SVDs, Z ~ A B with A = U_r S_r, B = R_r^T;
+corrections stored as truncated SVDs, Z ~ A R^T with A = U_r S_r, R = R_r;
 the target cache materialised as the aligned source plus a weighted sum of
 the stored low-rank corrections)."""
 
@@ -53,7 +53,7 @@ def test_truncation_error_is_eckart_young():
     z = _bf(rng.standard_normal((96, 64)) * np.exp(-np.arange(64) / 8.0))
     for r in (4, 16, 32):
         a, b, s = lowrank.factor(z, r)
-        err = np.linalg.norm(_f(z) - _f(a) @ _f(b))
+        err = np.linalg.norm(_f(z) - _f(a) @ _f(b).T)
         tail = np.sqrt(np.sum(s[r:] ** 2))
         assert abs(err - tail) <= 2 ** -7 * np.linalg.norm(_f(z)), (r, err, tail)
 
@@ -63,7 +63,7 @@ def test_low_rank_matrix_is_recovered():
     z = _bf(rng.standard_normal((64, 5)) @ rng.standard_normal((5, 96)))
     a, b, s = lowrank.factor(z, 32)
     assert np.all(s[5:] < 2 ** -8 * s[0])      # what remains is the bf16 rounding of z itself
-    assert np.allclose(_f(a) @ _f(b), _f(z), atol=2 ** -6 * np.abs(_f(z)).max())
+    assert np.allclose(_f(a) @ _f(b).T, _f(z), atol=2 ** -6 * np.abs(_f(z)).max())
 
 
 def test_materialize_brute_force_and_identities():
@@ -71,14 +71,14 @@ def test_materialize_brute_force_and_identities():
     T, D, r, V = 6, 10, 3, 2
     src = _bf(rng.standard_normal((T, D)))
     a = _bf(rng.standard_normal((V, T, r)))
-    b = _bf(rng.standard_normal((V, r, D)))
+    b = _bf(rng.standard_normal((V, D, r)))
     w = np.array([0.75, -1.5], np.float32)
     got = lowrank.materialize(src, a, b, w)
     for i in range(T):
         for j in range(D):
             x = Fraction(float(_f(src)[i, j]))
             for v in range(V):
-                x += Fraction(float(w[v])) * sum(Fraction(float(_f(a)[v, i, k])) * Fraction(float(_f(b)[v, k, j]))
+                x += Fraction(float(w[v])) * sum(Fraction(float(_f(a)[v, i, k])) * Fraction(float(_f(b)[v, j, k]))
                                               for k in range(r))
             assert got[i, j] == exact_round_to_bf16(x)
     assert np.array_equal(lowrank.materialize(src, a, b, np.zeros(V, np.float32)), src)
@@ -88,8 +88,21 @@ def test_materialize_is_linear_in_the_weights():
     rng = np.random.default_rng(5)
     src = _bf(rng.standard_normal((32, 40)))
     a = _bf(rng.standard_normal((1, 32, 8)))
-    b = _bf(rng.standard_normal((1, 8, 40)))
+    b = _bf(rng.standard_normal((1, 40, 8)))
     two = lowrank.materialize(src, np.concatenate([a, a]), np.concatenate([b, b]), np.array([0.25, 0.5], np.float32))
     one = lowrank.materialize(src, a, b, np.array([0.75], np.float32))
     d = np.abs(_f(two) - _f(one))
     assert np.all(d <= 2 ** -7 * np.maximum(np.abs(_f(one)), 1e-30))
+
+
+def test_materialize_cache_is_per_layer_matrix_view():
+    rng = np.random.default_rng(6)
+    L, H, T, d, V, r = 2, 3, 5, 4, 2, 2
+    src = _bf(rng.standard_normal((L, H, T, d)))
+    a = _bf(rng.standard_normal((L, V, T, r)))
+    rr = _bf(rng.standard_normal((L, V, H * d, r)))
+    w = rng.standard_normal((L, V)).astype(np.float32)
+    out = lowrank.materialize_cache(src, a, rr, w)
+    l, h, t, c = 1, 2, 3, 1
+    x = _f(src)[l, h, t, c] + sum(float(w[l, v]) * float(_f(a)[l, v, t] @ _f(rr)[l, v, h * d + c]) for v in range(V))
+    assert out[l, h, t, c] == lowrank.round_bf16(np.array([x]))[0]
