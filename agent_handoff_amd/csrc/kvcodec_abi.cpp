@@ -188,6 +188,28 @@ int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int6
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
+int kvc_lowrank_materialize(const kvc_shape* shape, uint32_t rank, uint32_t n_anchors, const void* src,
+                            const void* a, const void* r, const float* weights, void* out, hipStream_t stream) {
+    if (!shape || !src || !a || !r || !weights || !out) return KVC_E_NULL;
+    if (!pool_shape(shape)) return KVC_E_SHAPE;
+    const uint32_t L = shape->num_layers, H = shape->num_kv_heads, T = shape->num_tokens, d = shape->head_dim;
+    if ((rank != 32 && rank != 64) || n_anchors < 1 || n_anchors > kvc::kLowrankMaxAnchors ||
+        kvc::lowrank_lds_bytes(d, n_anchors, rank) > kvc::kLowrankMaxLds)
+        return KVC_E_RANGE;
+    const uint64_t tiles = ((uint64_t)T + 255) / 256, groups = ((uint64_t)L + 7) / 8;
+    if (groups * 8 * tiles * H > 0x7FFFFFFFull) return KVC_E_SHAPE;
+    if (!aligned(src, 16) || !aligned(a, 16) || !aligned(r, 16) || !aligned(out, 16) || !aligned(weights, 4))
+        return KVC_E_ALIGN;
+    const uint64_t kb = kv_bytes(shape);
+    const uint64_t ab = (uint64_t)L * n_anchors * T * rank * 2, rb = (uint64_t)L * n_anchors * H * d * rank * 2;
+    const uint64_t wb = (uint64_t)L * n_anchors * 4;
+    if ((out != src && overlap(out, kb, src, kb)) || overlap(out, kb, a, ab) || overlap(out, kb, r, rb) ||
+        overlap(out, kb, weights, wb))
+        return KVC_E_ALIAS;
+    const hipError_t e = kvc::launch_lowrank_materialize(L, H, T, d, n_anchors, rank, src, a, r, weights, out, stream);
+    return e == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
 size_t cachecard_transcode_workspace_bytes(const kvc_shape* shape) {
     if (!card_shape(shape)) return 0;
     return (size_t)(2 * card_ws_bytes(shape));
@@ -278,7 +300,7 @@ const char* kvc_strerror(int code) {
         case KVC_E_ALIGN: return "a pointer is not aligned as required";
         case KVC_E_ALIAS: return "an output overlaps an input or another output";
         case KVC_E_FORMAT: return "malformed pool or card header";
-        case KVC_E_RANGE: return "bad layer range or agent count";
+        case KVC_E_RANGE: return "argument out of range (layer range, agent count, pairing, rank or anchors)";
         case KVC_E_HIP: return "kernel launch failed";
         default: return "unknown error";
     }

@@ -49,4 +49,14 @@ constexpr int kMaxRealignPairs = 64;
 hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, const double* cos_tab,
                                const double* sin_tab, uint32_t pairing, hipStream_t stream);
 
+// Low-rank anchor materialisation over M matrices of T x (H*d); r is 32 or
+// 64, V <= 32 (the weights sit one per lane), and V anchors' R rows for one
+// head (V*d*r*2 bytes) must fit in the LDS budget.
+constexpr uint64_t kLowrankMaxLds = 128 * 1024;
+constexpr uint32_t kLowrankMaxAnchors = 32;
+uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r);
+hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
+                                      const void* src, const void* a, const void* rf, const float* w, void* out,
+                                      hipStream_t stream);
+
 }  // namespace kvc

@@ -1,0 +1,264 @@
+// lowrank_kernels.hip - low-rank anchor materialisation for gfx950 (MFMA).
+//
+// KVCMAS (cache reuse across agents), "low-rank anchor" storage: a stored
+// cache matrix Z (T tokens x D = H*d channels of one layer's K or V) is kept
+// as the truncated SVD factors A = U_r S_r (T x r) and R = R_r (D x r),
+// Z ~ A R^T, and a reused cache is corrected by a similarity-weighted sum
+// of stored anchors. This kernel materialises, for every matrix m,
+//
+//     out = bf16( src + sum_v w_v * (A_v R_v^T) )
+//
+// with src and out in the cache layout [H][T][d] and A_v R_v^T a dense
+// contraction over r, done on the matrix cores: v_mfma_f32_16x16x32_bf16
+// (bf16 operands, binary32 accumulation). Each anchor's product is reduced
+// over r on its own, then scaled by its binary32 weight and added in
+// binary32 (fmaf), anchors in index order; src is added last and the sum is
+// rounded once to bf16, ties to even.
+//
+// Work mapping. A workgroup (8 waves) owns 256 tokens of one head of one
+// matrix: its source and output tile is one contiguous 64 KB block at
+// d = 128. The anchors' R rows for that head (V x d x r bf16) are staged
+// once into LDS in MFMA-fragment order, so every operand read is a
+// lane-contiguous ds_read_b128. Wave w owns token blocks 2w and 2w + 1 of
+// the tile (16 tokens each) and all d channels, computed transposed:
+// out^T block = R_block (16 channels x r) * A_block^T (r x 16 tokens).
+// MFMA row i of channel block cb is channel (d/4)(i/4) + 4cb + i%4, which
+// leaves lane l holding token l%16 and the d/4 consecutive channels from
+// (d/4)(l/16) on, so source loads and output stores are 16-byte accesses.
+// Matrices are dealt to XCDs (workgroup b runs on XCD b % 8) so that one
+// matrix's factors are read from HBM by one XCD and re-read from its L2 by
+// the 8 heads and 16 token tiles that share them.
+#include "kernels_common.h"
+#include "launch.h"
+
+namespace kvc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLrWaves = 8;
+constexpr int kLrThreads = kLrWaves * kWave;
+constexpr int kLrTileTokens = kLrWaves * 2 * 16;  // 256
+constexpr int kXcds = 8;
+
+struct LowrankParams {
+    const uint16_t* src;  // [M][H][T][d]
+    const uint16_t* a;    // [M][V][T][r]
+    const uint16_t* rf;   // [M][V][H*d][r]
+    const float* w;       // [M][V]
+    uint16_t* out;        // [M][H][T][d]
+    uint32_t M, H, T, V, r;
+    uint32_t tiles;       // ceil(T / 256)
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <int D, int KC>
+__global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(LowrankParams p) {
+    constexpr int NCB = D / 16;   // channel blocks of 16
+    constexpr int CPL = D / 4;    // channels per lane in the output layout
+    constexpr int SQ = CPL / 8;   // 16-byte source chunks per lane and token
+    extern __shared__ u32x4 frag[];  // [V][r/32][NCB][64 lanes]
+
+    // workgroup -> (matrix, token tile, head), matrices grouped by XCD
+    const uint32_t b = blockIdx.x;
+    const uint32_t per_matrix = p.tiles * p.H;
+    const uint32_t m = b % kXcds + kXcds * ((b / kXcds) / per_matrix);
+    if (m >= p.M) return;
+    const uint32_t rem = (b / kXcds) % per_matrix;
+    const uint32_t tile = rem / p.H, h = rem % p.H;
+    const uint64_t HD = (uint64_t)p.H * D;
+
+    // stage R rows h*d .. h*d + d - 1 of every anchor into fragment order:
+    // fragment (v, kc, cb), lane i + 16 g holds channel (d/4)(i/4) + 4cb + i%4,
+    // k = 32 kc + 8 g .. + 7
+    {
+        const uint32_t per_anchor = D * p.r / 8;  // 16-byte chunks
+        const uint32_t total = p.V * per_anchor;
+        const uint32_t qpr = p.r / 8;             // chunks per row
+        for (uint32_t c0 = 0; c0 < total; c0 += 8 * kLrThreads) {
+            u32x4 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t c = min(c0 + u * kLrThreads + threadIdx.x, total - 1);
+                const uint32_t v = c / per_anchor, rest = c % per_anchor;
+                const uint32_t row = rest / qpr, q = rest % qpr;
+                x[u] = ld16(p.rf + (((uint64_t)m * p.V + v) * HD + (uint64_t)h * D + row) * p.r + q * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t c = c0 + u * kLrThreads + threadIdx.x;
+                if (c < total) {
+                    const uint32_t v = c / per_anchor, rest = c % per_anchor;
+                    const uint32_t row = rest / qpr, q = rest % qpr;
+                    const uint32_t kc = q / 4, g = q % 4;
+                    const uint32_t i = 4 * (row / CPL) + row % 4, cb = (row % CPL) / 4;
+                    frag[((v * KC + kc) * NCB + cb) * kWave + i + 16 * g] = x[u];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint32_t lane = lane_id();
+    const uint32_t wave = wave_uniform(threadIdx.x / kWave);
+    const uint32_t t_base = tile * kLrTileTokens + wave * 32;
+    if (t_base >= p.T) return;  // no barrier follows
+    const uint32_t g = lane / 16;
+    uint32_t tok[2];
+    tok[0] = t_base + lane % 16;
+    tok[1] = t_base + 16 + lane % 16;
+    const uint32_t tc[2] = {min(tok[0], p.T - 1), min(tok[1], p.T - 1)};
+
+    // source chunks for the epilogue; at r = 32 they are loaded first, so
+    // they fly during the contraction (at r = 64 the registers are needed
+    // for the operands and the source is read in the epilogue)
+    const uint16_t* src = p.src + ((uint64_t)m * p.H + h) * p.T * D;
+    u32x4 s[2][SQ];
+    auto load_src = [&]() {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < SQ; ++q) s[j][q] = ld16(src + (uint64_t)tc[j] * D + g * CPL + 8 * q);
+    };
+    if (KC == 1) load_src();
+
+    // A fragments: token row of the block, k = 32 kc + 8 g .. + 7
+    const uint16_t* a = p.a + (uint64_t)m * p.V * p.T * p.r;
+    auto load_a = [&](uint32_t v, u32x4 (&x)[2][KC]) {
+        const uint16_t* av = a + (uint64_t)v * p.T * p.r;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) x[j][kc] = ld16(av + (uint64_t)tc[j] * p.r + 32 * kc + 8 * g);
+    };
+
+    float acc[2][NCB][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][cb][e] = 0.0f;
+
+    // Software pipeline over anchors. The A fragments (global memory) of
+    // anchor v + 1 are requested before anchor v's products, into the other
+    // of two register sets (the loop is unrolled by two so that no copy
+    // waits on them). The R fragments (LDS) of anchor v + 1 are read into
+    // the same registers right after anchor v's products are issued. The
+    // first anchor's operands pass through an empty asm so that the
+    // compiler keeps the loop-carried values in registers (it would
+    // otherwise merge the loads feeding each one into a single load at the
+    // loop head, issued just before its use).
+    u32x4 a0[2][KC], a1[2][KC], rc[KC][NCB];
+    auto load_r = [&](uint32_t v) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) rc[kc][cb] = frag[((v * KC + kc) * NCB + cb) * kWave + lane];
+    };
+    load_a(0, a0);
+    load_r(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+v"(a0[j][kc]));
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(rc[kc][cb]));
+    // weights: lane v holds w_v; each is moved to a scalar register in turn
+    const float wl = p.w[(uint64_t)m * p.V + min(lane, p.V - 1)];
+
+    auto step = [&](uint32_t v, const u32x4 (&ca)[2][KC], u32x4 (&na)[2][KC]) {
+        const uint32_t vn = min(v + 1, p.V - 1);
+        load_a(vn, na);
+        f32x4 t[2][NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                t[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rc[0][cb]),
+                                                                   __builtin_bit_cast(bf16x8, ca[j][0]),
+                                                                   f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                for (int kc = 1; kc < KC; ++kc)
+                    t[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rc[kc][cb]),
+                                                                       __builtin_bit_cast(bf16x8, ca[j][kc]),
+                                                                       t[j][cb], 0, 0, 0);
+            }
+        load_r(vn);
+        const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), v));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][cb][e] = fmaf(wv, t[j][cb][e], acc[j][cb][e]);
+    };
+    uint32_t v = 0;
+    for (; v + 1 < p.V; v += 2) {
+        step(v, a0, a1);
+        step(v + 1, a1, a0);
+    }
+    if (v < p.V) step(v, a0, a1);
+    if (KC != 1) load_src();
+
+    // lane holds token tok[j], channels (d/4) g + 4cb + e: add the source,
+    // round once, store 16 bytes (two channel blocks) at a time
+    uint16_t* out = p.out + ((uint64_t)m * p.H + h) * p.T * D;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (tok[j] >= p.T) continue;
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const uint32_t sw[4] = {s[j][q].x, s[j][q].y, s[j][q].z, s[j][q].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
+                o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
+            }
+            *reinterpret_cast<u32x4*>(out + (uint64_t)tok[j] * D + g * CPL + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+}  // namespace
+
+uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r) { return (uint64_t)V * d * r * 2; }
+
+hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
+                                      const void* src, const void* a, const void* rf, const float* w, void* out,
+                                      hipStream_t stream) {
+    LowrankParams p{};
+    p.src = static_cast<const uint16_t*>(src);
+    p.a = static_cast<const uint16_t*>(a);
+    p.rf = static_cast<const uint16_t*>(rf);
+    p.w = w;
+    p.out = static_cast<uint16_t*>(out);
+    p.M = M;
+    p.H = H;
+    p.T = T;
+    p.V = V;
+    p.r = r;
+    p.tiles = (T + kLrTileTokens - 1) / kLrTileTokens;
+    const uint64_t groups = (M + kXcds - 1) / kXcds;
+    const uint64_t nblocks = groups * kXcds * p.tiles * H;
+    if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    const uint32_t lds = (uint32_t)lowrank_lds_bytes(d, V, r);
+    void (*kernel)(LowrankParams) =
+        d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2> : lowrank_materialize_kernel<64, 1>)
+                : (r == 64 ? lowrank_materialize_kernel<128, 2> : lowrank_materialize_kernel<128, 1>);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return report_launch(e, "lowrank_materialize (LDS attribute)");
+    void* argv[] = {&p};
+    return report_launch(hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((uint32_t)nblocks),
+                                         dim3(kLrThreads), argv, lds, stream),
+                         "lowrank_materialize");
+}
+
+}  // namespace kvc

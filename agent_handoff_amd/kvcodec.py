@@ -64,6 +64,7 @@ def _load():
         "cachecard_transcode_workspace_bytes": (sz, [sp]),
         "cachecard_transcode": (i32, [sp, p, sz, p, p, sz, p, p, p, sz, p]),
         "kvc_realign_keys": (i32, [sp, p, p, ctypes.c_int64, p, u32, p]),
+        "kvc_lowrank_materialize": (i32, [sp, u32, u32, p, p, p, p, p, p]),
         "kvc_parse_header": (i32, [p, sz, sp, ctypes.POINTER(u32)]),
         "kvc_strerror": (ctypes.c_char_p, [i32]),
         "kvc_codebook": (None, [p, p]),
@@ -79,7 +80,8 @@ _lib = _load()
 EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_decode",
             "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
             "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack",
-            "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_realign_keys", "kvc_parse_header",
+            "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_realign_keys",
+            "kvc_lowrank_materialize", "kvc_parse_header",
             "kvc_strerror", "kvc_codebook")
 
 
@@ -222,6 +224,15 @@ def kvc_realign_keys(shape, k_in, k_out, delta, inv_freq, pairing=KVC_ROPE_HALVE
     _check(_lib.kvc_realign_keys(ctypes.byref(_shape(shape)), _ptr(k_in), _ptr(k_out), int(delta),
                                  f.ctypes.data_as(ctypes.c_void_p), int(pairing), _stream(stream)),
            "kvc_realign_keys")
+
+
+def kvc_lowrank_materialize(shape, rank, n_anchors, src, a, r, weights, out, stream=None):
+    """src, out: bf16 device tensors [L, H, T, d] (the same tensor for in
+    place); a: bf16 [L, V, T, rank]; r: bf16 [L, V, H*d, rank]; weights:
+    float32 device tensor [L, V]."""
+    _check(_lib.kvc_lowrank_materialize(ctypes.byref(_shape(shape)), int(rank), int(n_anchors), _ptr(src),
+                                        _ptr(a), _ptr(r), _ptr(weights), _ptr(out), _stream(stream)),
+           "kvc_lowrank_materialize")
 
 
 # ------------------------------------------------------------------ host utils

@@ -18,7 +18,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-K_TENSOR, V_TENSOR, STRUCT_TENSOR = 0, 1, 2
+K_TENSOR, V_TENSOR, STRUCT_TENSOR, ANCHOR_TENSOR = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
@@ -152,6 +152,32 @@ def card_widths(w, seed=0, T=None, mean_run=16.0):
     return out
 
 
+# Low-rank anchors (KVCMAS stores corrections as truncated-SVD factors, rank
+# r = 32 and V = 10 anchors by default). Synthetic factors with the shape of
+# an SVD: R has near-orthonormal columns (entries N(0, 1/D)), A's column k
+# has scale delta * s_k * sqrt(D) with s_k = decay**k normalised so that
+# sum s_k^2 = 1, making every element of A R^T about N(0, delta^2). Weights
+# are similarity weights: positive, summing to one (flat Dirichlet).
+
+def anchor_column_scales(r, delta=0.25, decay=0.85):
+    s = decay ** np.arange(r, dtype=np.float64)
+    return delta * s / np.sqrt(np.sum(s * s))
+
+
+def anchor_factors(seed, cfg, L, V, T, D, r, delta=0.25, decay=0.85):
+    """(A bits [L][V][T][r], R bits [L][V][D][r], weights float32 [L][V])."""
+    A = np.empty((L, V, T, r), np.uint16)
+    R = np.empty((L, V, D, r), np.uint16)
+    w = np.empty((L, V), np.float32)
+    col = (anchor_column_scales(r, delta, decay) * np.sqrt(D)).astype(np.float32)
+    for l in range(L):
+        g = rng(seed, cfg, ANCHOR_TENSOR, l)
+        f32_to_bf16_bits(g.standard_normal((V, T, r), dtype=np.float32) * col, out=A[l])
+        f32_to_bf16_bits(g.standard_normal((V, D, r), dtype=np.float32) / np.float32(np.sqrt(D)), out=R[l])
+        w[l] = g.dirichlet(np.ones(V)).astype(np.float32)
+    return A, R, w
+
+
 # ------------------------------------------------------------------ on-device
 # The same recipes drawn on the GPU with torch's generator (Philox), for the
 # large workloads of the benchmark. Values differ from the numpy streams of
@@ -204,3 +230,20 @@ def kv_tensors_torch(w, seed=0, device="cuda", shape=None):
             t[l] = layer_values_torch(w.recipe, seed, w.cfg, tensor, l, H, T, d, device).to(torch.bfloat16)
         out.append(t)
     return out[0], out[1]
+
+
+def anchor_factors_torch(seed, cfg, L, V, T, D, r, device="cuda", delta=0.25, decay=0.85):
+    """The anchor recipe drawn on `device` with torch's generator: A, R as
+    bf16 tensors [L, V, T, r] and [L, V, D, r], weights float32 [L, V]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(seed, cfg, ANCHOR_TENSOR, 0))
+    col = torch.tensor(anchor_column_scales(r, delta, decay) * np.sqrt(D), dtype=torch.float32, device=device)
+    A = torch.empty((L, V, T, r), dtype=torch.bfloat16, device=device)
+    R = torch.empty((L, V, D, r), dtype=torch.bfloat16, device=device)
+    for l in range(L):
+        A[l] = (torch.randn((V, T, r), generator=g, device=device) * col).to(torch.bfloat16)
+        R[l] = (torch.randn((V, D, r), generator=g, device=device) / float(np.sqrt(D))).to(torch.bfloat16)
+    e = -torch.log(torch.rand((L, V), generator=g, device=device).clamp_min(1e-12))
+    w = (e / e.sum(dim=1, keepdim=True)).to(torch.float32)
+    return A, R, w

@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 FANOUT_MIN_AGENTS = 8  # the library decodes into this many agents or more as decode + fan-out copy
 METRIC = "KV codec encode/decode GB/s and % of HBM peak, Llama-3-8B shape 4K tok"
 
@@ -191,6 +192,26 @@ def main():
     tr = timed(lambda: kv.kvc_realign_keys(shape, k, k_rt, 4096, inv_freq, stream=stream), 10)
     ops_out["realign_keys"] = {"us": round(tr * 1e6, 2), "bytes": 2 * kv_bytes, "GB/s": round(2 * kv_bytes / tr / 1e9, 1),
                                "frac_hbm_peak": round(2 * kv_bytes / tr / 1e9 / HBM_PEAK_GBS, 4)}
+    # low-rank anchor materialisation (KVCMAS defaults: V = 10 anchors of
+    # rank 32) of the K and the V cache, one launch per tensor over its layers
+    n_anc, rank = 10, 32
+    fk = synth.anchor_factors_torch(args.seed, 6, L, n_anc, T, H * d, rank, device=dev)
+    fv = synth.anchor_factors_torch(args.seed + 1, 6, L, n_anc, T, H * d, rank, device=dev)
+    torch.cuda.synchronize()
+
+    def lowrank():
+        kv.kvc_lowrank_materialize(shape, rank, n_anc, k, *fk, k_rt, stream=stream)
+        kv.kvc_lowrank_materialize(shape, rank, n_anc, v, *fv, v_rt, stream=stream)
+
+    tl = timed(lowrank, 10)
+    bl = 2 * (2 * kv_bytes + sum(t.numel() * t.element_size() for t in fk))
+    fl = 2 * (2.0 * L * n_anc * T * H * d * rank)
+    ops_out["lowrank_materialize"] = {"us": round(tl * 1e6, 2), "bytes": bl, "GB/s": round(bl / tl / 1e9, 1),
+                                      "frac_hbm_peak": round(bl / tl / 1e9 / HBM_PEAK_GBS, 4),
+                                      "TFLOP/s": round(fl / tl / 1e12, 1),
+                                      "frac_mfma_bf16_peak": round(fl / tl / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                      "anchors": n_anc, "rank": rank}
+    del fk, fv
     drift = hop_drift(kv, synth, k, v, shape, widths_np, args.seed, stream, dev)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set beside the step"
@@ -301,7 +322,7 @@ CALIBRATION_BYTES = 1 << 30
 CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_kernel",
                  "key_absmax_kernel",
                  "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
-                 "card_transcode_kernel", "realign_keys_kernel"]
+                 "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 

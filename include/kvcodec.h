@@ -74,7 +74,7 @@ enum {
     KVC_E_ALIGN = -4,  /* a pointer is not aligned as required */
     KVC_E_ALIAS = -5,  /* an output overlaps an input or another output */
     KVC_E_FORMAT = -6, /* malformed header bytes */
-    KVC_E_RANGE = -7,  /* bad layer range or agent count */
+    KVC_E_RANGE = -7,  /* argument out of range (layer range, agent count, ...) */
     KVC_E_HIP = -8     /* a kernel launch failed */
 };
 
@@ -245,6 +245,38 @@ int cachecard_transcode(const kvc_shape* shape, const void* card_in, size_t card
  * KVC_E_ALIAS, KVC_E_HIP. */
 int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int64_t delta,
                      const float* inv_freq, uint32_t pairing, hipStream_t stream);
+
+/* ------------------------------------------------------ low-rank anchors */
+
+/* Materialise a cache from a source cache and low-rank anchors (KVCMAS,
+ * low-rank anchor storage: a cache matrix Z of T tokens by D = H*d channels
+ * is stored as truncated-SVD factors A = U_r S_r (T x r) and R = R_r
+ * (D x r), Z ~ A R^T; a reused cache is corrected by a similarity-weighted
+ * sum of stored anchors). For each of the L matrices (layers of one of K
+ * or V) and every token t, head h and channel c:
+ *     out[l][h][t][c] = bf16( src[l][h][t][c]
+ *                      + sum_v w[l][v] * sum_k A[l][v][t][k] * R[l][v][h*d + c][k] )
+ * The inner sum runs on the matrix cores with bf16 operands and binary32
+ * accumulation; each anchor's sum is scaled by its weight and added in
+ * binary32 (fused multiply-add, anchors in index order), src is added last
+ * and the total rounded once to bf16, ties to even. Against the binary64
+ * value rounded once, the result is within 1 bf16 ulp plus the binary32
+ * error, at most (2r + V + 1) * 2^-24 * (|src| + sum_v |w_v| sum_k |A R|)
+ * to first order (the products of bf16 operands are exact in binary32; 2r
+ * covers r - 1 additions inside the matrix core even if they truncate).
+ *   shape      L (matrices), H, T, d (64 or 128)
+ *   rank       r: 32 or 64
+ *   n_anchors  V: 1 .. 32, and V * d * r * 2 <= 131072 (at d = 128, r = 32:
+ *              V <= 16)
+ *   src, out   device bf16 [L][H][T][d], 16-byte aligned; out == src
+ *              materialises in place, any other overlap is an error
+ *   a          device bf16 [L][V][T][r] (row-major A factors), 16-byte aligned
+ *   r          device bf16 [L][V][H*d][r] (row-major R factors), 16-byte aligned
+ *   weights    device f32 [L][V]
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_RANGE (rank, n_anchors), KVC_E_ALIGN,
+ * KVC_E_ALIAS, KVC_E_HIP. */
+int kvc_lowrank_materialize(const kvc_shape* shape, uint32_t rank, uint32_t n_anchors, const void* src,
+                            const void* a, const void* r, const float* weights, void* out, hipStream_t stream);
 
 /* --------------------------------------------------------------- host utils */
 

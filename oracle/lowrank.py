@@ -1,5 +1,5 @@
 """Low-rank anchor storage (KVCMAS, "what differs": base caches and delta
-corrections kept as truncated SVDs, Z ~ U_r S_r R_r^T = A B, rank r = 32 and
+corrections kept as truncated SVDs, Z ~ U_r S_r R_r^T = A R^T, rank r = 32 and
 V = 10 anchors per slot by default; "how it is used": the correction for a
 target is a weighted sum of the stored low-rank factors, added to the aligned
 source cache to materialise the full-width target cache).

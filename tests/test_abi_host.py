@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -228,3 +228,30 @@ def test_realign_argument_errors():
     assert ra(pairing=2) == kv.KVC_E_RANGE
     assert ra(k_out=2 * A + 8) == kv.KVC_E_ALIGN
     assert ra(k_out=A + 1024) == kv.KVC_E_ALIAS     # partial overlap (in place means the same address)
+
+
+def test_lowrank_argument_errors():
+    w = 5 * A
+
+    def lr(shape=S, rank=32, V=4, src=A, a=2 * A, r=3 * A, weights=w, out=4 * A):
+        return L.kvc_lowrank_materialize(ctypes.byref(shape) if shape is not None else None, rank, V, src, a, r,
+                                         weights, out, None)
+
+    assert lr(shape=None) == kv.KVC_E_NULL
+    assert lr(a=None) == kv.KVC_E_NULL
+    assert lr(weights=None) == kv.KVC_E_NULL
+    assert lr(shape=kv.kvc_shape(2, 2, 32, 96)) == kv.KVC_E_SHAPE
+    assert lr(shape=kv.kvc_shape(0, 2, 32, 128)) == kv.KVC_E_SHAPE
+    assert lr(rank=16) == kv.KVC_E_RANGE
+    assert lr(rank=48) == kv.KVC_E_RANGE
+    assert lr(V=0) == kv.KVC_E_RANGE
+    assert lr(V=17) == kv.KVC_E_RANGE                        # 17 * 128 * 32 * 2 bytes exceed the LDS budget
+    assert lr(rank=64, V=9) == kv.KVC_E_RANGE
+    assert lr(shape=kv.kvc_shape(2, 2, 32, 64), V=33) == kv.KVC_E_RANGE   # one weight per lane, at most 32
+    assert lr(a=2 * A + 8) == kv.KVC_E_ALIGN
+    assert lr(out=4 * A + 8) == kv.KVC_E_ALIGN
+    assert lr(weights=w + 2) == kv.KVC_E_ALIGN
+    assert lr(out=A + 1024) == kv.KVC_E_ALIAS                # partial overlap with src
+    assert lr(out=2 * A + 512) == kv.KVC_E_ALIAS             # output over the A factors
+    assert lr(out=3 * A) == kv.KVC_E_ALIAS
+    assert lr(weights=4 * A + 16) == kv.KVC_E_ALIAS
