@@ -15,19 +15,22 @@
 // binary32 (fmaf), anchors in index order; src is added last and the sum is
 // rounded once to bf16, ties to even.
 //
-// Work mapping. A workgroup (8 waves) owns 256 tokens of one head of one
-// matrix: its source and output tile is one contiguous 64 KB block at
-// d = 128. The anchors' R rows for that head (V x d x r bf16) are staged
-// once into LDS in MFMA-fragment order, so every operand read is a
-// lane-contiguous ds_read_b128. Wave w owns token blocks 2w and 2w + 1 of
-// the tile (16 tokens each) and all d channels, computed transposed:
-// out^T block = R_block (16 channels x r) * A_block^T (r x 16 tokens).
-// MFMA row i of channel block cb is channel (d/4)(i/4) + 4cb + i%4, which
-// leaves lane l holding token l%16 and the d/4 consecutive channels from
-// (d/4)(l/16) on, so source loads and output stores are 16-byte accesses.
-// Matrices are dealt to XCDs (workgroup b runs on XCD b % 8) so that one
-// matrix's factors are read from HBM by one XCD and re-read from its L2 by
-// the 8 heads and 16 token tiles that share them.
+// Work mapping. A workgroup (8 waves) owns one head of one matrix over a
+// chunk of token tiles (256 tokens each; at Llama-3-8B sizes a chunk is the
+// whole sequence, one workgroup per CU): its source and output are one
+// contiguous block of [H][T][d]. The anchors' R rows for that head
+// (V x d x r bf16) are staged once into LDS in MFMA-fragment order, so every
+// operand read is a lane-contiguous ds_read_b128. In each tile, wave w owns
+// token blocks 2w and 2w + 1 (16 tokens each) and all d channels, computed
+// transposed: out^T block = R_block (16 channels x r) * A_block^T
+// (r x 16 tokens). MFMA row i of channel block cb is channel
+// (d/4)(i/4) + 4cb + i%4, which leaves lane l holding token l%16 and the d/4
+// consecutive channels from (d/4)(l/16) on, so source loads and output
+// stores are 16-byte accesses. The (tile, anchor) steps of a chunk form one
+// pipeline: A fragments are requested five steps ahead (at r = 32), a
+// tile's source at its first step, its output stored at its last. Matrices are
+// dealt to XCDs (workgroup b runs on XCD b % 8) so that the 8 heads sharing
+// one matrix's A factors run on one XCD and re-read them from its L2.
 #include "kernels_common.h"
 #include "launch.h"
 
@@ -42,6 +45,7 @@ constexpr int kLrWaves = 8;
 constexpr int kLrThreads = kLrWaves * kWave;
 constexpr int kLrTileTokens = kLrWaves * 2 * 16;  // 256
 constexpr int kXcds = 8;
+constexpr uint64_t kLowrankTargetGroups = 256;  // one workgroup per CU
 
 struct LowrankParams {
     const uint16_t* src;  // [M][H][T][d]
@@ -51,6 +55,8 @@ struct LowrankParams {
     uint16_t* out;        // [M][H][T][d]
     uint32_t M, H, T, V, r;
     uint32_t tiles;       // ceil(T / 256)
+    uint32_t chunks;      // token chunks per (matrix, head)
+    uint32_t chunk_tiles; // tiles per chunk
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -62,13 +68,16 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     constexpr int SQ = CPL / 8;   // 16-byte source chunks per lane and token
     extern __shared__ u32x4 frag[];  // [V][r/32][NCB][64 lanes]
 
-    // workgroup -> (matrix, token tile, head), matrices grouped by XCD
+    // workgroup -> (matrix, token chunk, head), matrices grouped by XCD
     const uint32_t b = blockIdx.x;
-    const uint32_t per_matrix = p.tiles * p.H;
+    const uint32_t per_matrix = p.chunks * p.H;
     const uint32_t m = b % kXcds + kXcds * ((b / kXcds) / per_matrix);
     if (m >= p.M) return;
     const uint32_t rem = (b / kXcds) % per_matrix;
-    const uint32_t tile = rem / p.H, h = rem % p.H;
+    const uint32_t chunk = rem / p.H, h = rem % p.H;
+    const uint32_t tile0 = chunk * p.chunk_tiles;
+    if (tile0 >= p.tiles) return;
+    const uint32_t n_tiles = min(p.chunk_tiles, p.tiles - tile0);
     const uint64_t HD = (uint64_t)p.H * D;
 
     // stage R rows h*d .. h*d + d - 1 of every anchor into fragment order:
@@ -104,35 +113,46 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 
     const uint32_t lane = lane_id();
     const uint32_t wave = wave_uniform(threadIdx.x / kWave);
-    const uint32_t t_base = tile * kLrTileTokens + wave * 32;
-    if (t_base >= p.T) return;  // no barrier follows
     const uint32_t g = lane / 16;
-    uint32_t tok[2];
-    tok[0] = t_base + lane % 16;
-    tok[1] = t_base + 16 + lane % 16;
-    const uint32_t tc[2] = {min(tok[0], p.T - 1), min(tok[1], p.T - 1)};
-
-    // source chunks for the epilogue; at r = 32 they are loaded first, so
-    // they fly during the contraction (at r = 64 the registers are needed
-    // for the operands and the source is read in the epilogue)
+    const uint32_t row_in_tile = wave * 32 + lane % 16;  // + 16 j
     const uint16_t* src = p.src + ((uint64_t)m * p.H + h) * p.T * D;
-    u32x4 s[2][SQ];
-    auto load_src = [&]() {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int q = 0; q < SQ; ++q) s[j][q] = ld16(src + (uint64_t)tc[j] * D + g * CPL + 8 * q);
-    };
-    if (KC == 1) load_src();
-
-    // A fragments: token row of the block, k = 32 kc + 8 g .. + 7
+    uint16_t* out = p.out + ((uint64_t)m * p.H + h) * p.T * D;
     const uint16_t* a = p.a + (uint64_t)m * p.V * p.T * p.r;
-    auto load_a = [&](uint32_t v, u32x4 (&x)[2][KC]) {
+    const uint32_t S = n_tiles * p.V;  // pipeline steps
+
+    // A fragments of step s (tile s / V, anchor s % V): token row of the
+    // block, k = 32 kc + 8 g .. + 7; rows past T (and steps past the end)
+    // are clamped to valid ones and their results discarded
+    auto load_a = [&](uint32_t s, u32x4 (&x)[2][KC]) {
+        s = min(s, S - 1);
+        const uint32_t tile = tile0 + s / p.V, v = s % p.V;
         const uint16_t* av = a + (uint64_t)v * p.T * p.r;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) x[j][kc] = ld16(av + (uint64_t)tc[j] * p.r + 32 * kc + 8 * g);
+            for (int kc = 0; kc < KC; ++kc) x[j][kc] = ld16(av + (uint64_t)t * p.r + 32 * kc + 8 * g);
+        }
+    };
+    u32x4 rc[KC][NCB];
+    auto load_r = [&](uint32_t v) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) rc[kc][cb] = frag[((v * KC + kc) * NCB + cb) * kWave + lane];
+    };
+    // source chunks of a tile, requested at its first step and used at its
+    // last (at r = 64 the registers hold operands, and the source is read
+    // at the last step)
+    constexpr bool kEarlySrc = KC == 1;
+    u32x4 sv[2][SQ];
+    auto load_src = [&](uint32_t tile) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
+#pragma unroll
+            for (int q = 0; q < SQ; ++q) sv[j][q] = ld16(src + (uint64_t)t * D + g * CPL + 8 * q);
+        }
     };
 
     float acc[2][NCB][4];
@@ -143,38 +163,60 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[j][cb][e] = 0.0f;
 
-    // Software pipeline over anchors. The A fragments (global memory) of
-    // anchor v + 1 are requested before anchor v's products, into the other
-    // of two register sets (the loop is unrolled by two so that no copy
-    // waits on them). The R fragments (LDS) of anchor v + 1 are read into
-    // the same registers right after anchor v's products are issued. The
-    // first anchor's operands pass through an empty asm so that the
-    // compiler keeps the loop-carried values in registers (it would
-    // otherwise merge the loads feeding each one into a single load at the
-    // loop head, issued just before its use).
-    u32x4 a0[2][KC], a1[2][KC], rc[KC][NCB];
-    auto load_r = [&](uint32_t v) {
+    // lane holds token t, channels (d/4) g + 4cb + e: add the source, round
+    // once, store 16 bytes (two channel blocks) at a time
+    auto store_tile = [&](uint32_t tile) {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t t = tile * kLrTileTokens + row_in_tile + 16 * j;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) rc[kc][cb] = frag[((v * KC + kc) * NCB + cb) * kWave + lane];
+            for (int q = 0; q < SQ; ++q) {
+                const uint32_t sw[4] = {sv[j][q].x, sv[j][q].y, sv[j][q].z, sv[j][q].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
+                    o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
+                }
+                if (t < p.T) *reinterpret_cast<u32x4*>(out + (uint64_t)t * D + g * CPL + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][cb][e] = 0.0f;
+        }
     };
-    load_a(0, a0);
+
+    // weights: lane v holds w_v; each is moved to a scalar register in turn
+    const float wl = p.w[(uint64_t)m * p.V + min(lane, p.V - 1)];
+
+    // NSET register sets of A fragments in a ring: step s computes with set
+    // s % NSET and requests step s + NSET - 1 into the set step s - 1 used.
+    // The loop is unrolled by NSET so that the set index is a constant. The
+    // first sets pass through an empty asm so that the compiler keeps the
+    // loop-carried sets in registers (it would otherwise merge the loads
+    // feeding one into a single load at the loop head, just before its use).
+    constexpr int NSET = KC == 1 ? 6 : 2;
+    u32x4 set[NSET][2][KC];
+#pragma unroll
+    for (int u = 0; u + 1 < NSET; ++u) load_a(u, set[u]);
     load_r(0);
+    if (kEarlySrc) load_src(tile0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int u = 0; u + 1 < NSET; ++u)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+v"(a0[j][kc]));
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+v"(set[u][j][kc]));
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(rc[kc][cb]));
-    // weights: lane v holds w_v; each is moved to a scalar register in turn
-    const float wl = p.w[(uint64_t)m * p.V + min(lane, p.V - 1)];
 
-    auto step = [&](uint32_t v, const u32x4 (&ca)[2][KC], u32x4 (&na)[2][KC]) {
-        const uint32_t vn = min(v + 1, p.V - 1);
-        load_a(vn, na);
+    auto step = [&](uint32_t s, const u32x4 (&ca)[2][KC], u32x4 (&na)[2][KC]) {
+        const uint32_t tile = tile0 + s / p.V, v = s % p.V;
+        load_a(s + NSET - 1, na);
+        if (kEarlySrc && v == 0 && s != 0) load_src(tile);
         f32x4 t[2][NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -189,7 +231,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
                                                                        __builtin_bit_cast(bf16x8, ca[j][kc]),
                                                                        t[j][cb], 0, 0, 0);
             }
-        load_r(vn);
+        load_r(v + 1 == p.V ? 0 : v + 1);
         const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), v));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -197,33 +239,21 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[j][cb][e] = fmaf(wv, t[j][cb][e], acc[j][cb][e]);
-    };
-    uint32_t v = 0;
-    for (; v + 1 < p.V; v += 2) {
-        step(v, a0, a1);
-        step(v + 1, a1, a0);
-    }
-    if (v < p.V) step(v, a0, a1);
-    if (KC != 1) load_src();
-
-    // lane holds token tok[j], channels (d/4) g + 4cb + e: add the source,
-    // round once, store 16 bytes (two channel blocks) at a time
-    uint16_t* out = p.out + ((uint64_t)m * p.H + h) * p.T * D;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        if (tok[j] >= p.T) continue;
-#pragma unroll
-        for (int q = 0; q < SQ; ++q) {
-            const uint32_t sw[4] = {s[j][q].x, s[j][q].y, s[j][q].z, s[j][q].w};
-            uint32_t o[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
-                o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
-            }
-            *reinterpret_cast<u32x4*>(out + (uint64_t)tok[j] * D + g * CPL + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
+        if (v + 1 == p.V) {
+            if (!kEarlySrc) load_src(tile);
+            store_tile(tile);
         }
+    };
+    // whole rounds of NSET steps, then the remainder (fewer than NSET), so
+    // that no step inside the loop is conditional
+    uint32_t s = 0;
+    for (; s + NSET <= S; s += NSET) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) step(s + u, set[u], set[(u + NSET - 1) % NSET]);
     }
+#pragma unroll
+    for (int u = 0; u + 1 < NSET; ++u)
+        if (s + u < S) step(s + u, set[u], set[(u + NSET - 1) % NSET]);
 }
 
 }  // namespace
@@ -245,8 +275,14 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     p.V = V;
     p.r = r;
     p.tiles = (T + kLrTileTokens - 1) / kLrTileTokens;
+    // enough (matrix, head, chunk) items to give every CU one workgroup
+    const uint64_t mh = (uint64_t)M * H;
+    const uint64_t per_mh = (kLowrankTargetGroups + mh - 1) / mh;
+    const uint32_t want = (uint32_t)(per_mh < p.tiles ? per_mh : p.tiles);
+    p.chunk_tiles = (p.tiles + want - 1) / want;
+    p.chunks = (p.tiles + p.chunk_tiles - 1) / p.chunk_tiles;
     const uint64_t groups = (M + kXcds - 1) / kXcds;
-    const uint64_t nblocks = groups * kXcds * p.tiles * H;
+    const uint64_t nblocks = groups * kXcds * p.chunks * H;
     if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const uint32_t lds = (uint32_t)lowrank_lds_bytes(d, V, r);
     void (*kernel)(LowrankParams) =

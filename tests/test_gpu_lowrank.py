@@ -86,6 +86,7 @@ def run(shape, V, r, seed, weights=None, in_place=False, cfg=3):
     ((2, 2, 64, 64), 32, 32),      # most anchors at d = 64 (one weight per lane)
     ((1, 1, 16, 128), 8, 64),      # most anchors at d = 128, r = 64
     ((2, 8, 1024, 128), 10, 32),   # the pages' defaults, Llama-3-8B heads
+    ((16, 8, 700, 64), 3, 32),     # chunks of two tiles per workgroup, ragged last chunk
 ])
 def test_materialize_matches_oracle(shape, V, r):
     *_, exact = run(shape, V, r, seed=11)
