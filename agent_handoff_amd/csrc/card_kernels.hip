@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
 #pragma unroll
     for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
         const uint32_t idx = kWave * j + lane;
-        if (idx < n16) dst[idx] = img[idx];
+        if (idx < n16) st_stream(dst + idx, img[idx]);
     }
     // zero the stream's tail padding after the last record
     if (t0 + nv == p.T && lane == 0)
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint4 chunk = st[64 * j + lane];
-        if ((64 * j + lane) / (2 * D / 16) < nv) dst[64 * j + lane] = chunk;
+        if ((64 * j + lane) / (2 * D / 16) < nv) st_stream(dst + 64 * j + lane, chunk);
     }
 }
 
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
 #pragma unroll
     for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) {
         const uint32_t idx = kWave * j + lane;
-        if (idx < n16) dst[idx] = so[idx];
+        if (idx < n16) st_stream(dst + idx, so[idx]);
     }
     // zero the stream's tail padding after the last record
     if (t0 + nv == p.T && lane == 0)

@@ -178,6 +178,9 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
                     const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
                     o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
                 }
+                // plain stores: a wave's later waits for its A fragments also
+                // wait for these, and non-temporal stores took longer to
+                // retire (the call ran 1.9x slower with them)
                 if (t < p.T) *reinterpret_cast<u32x4*>(out + (uint64_t)t * D + g * CPL + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
             }
 #pragma unroll

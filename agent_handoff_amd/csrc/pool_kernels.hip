@@ -331,7 +331,7 @@ __device__ __forceinline__ void encode_values(const EncodeParams& p, const Block
         const uint32_t idx = 64 * j + lane;
         if (idx < kBlockTokens * VW) {
             const uint32_t wv = stg.v[idx];
-            if (idx / VW < b.nv) dst[idx] = wv;
+            if (idx / VW < b.nv) st_stream(dst + idx, wv);
         }
     }
 }
@@ -367,7 +367,7 @@ __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const Block
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         const uint4 chunk16 = stg.k[64 * j + lane];
-        if ((64 * j + lane) / (D / 16) < b.nv) dst[64 * j + lane] = chunk16;
+        if ((64 * j + lane) / (D / 16) < b.nv) st_stream(dst + 64 * j + lane, chunk16);
     }
     if (b.bidx == 0 && lane == 0)
         reinterpret_cast<float*>(p.pool + p.lay.k_scale)[b.l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
@@ -824,8 +824,8 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
         if ((64 * j + lane) / (4 * CH) < nv) {
             const uint4 kj = kc[j], vj = vc[j];
             for (uint32_t ag = 0; ag < p.n_out; ++ag) {
-                (reinterpret_cast<uint4*>(p.k_out[ag]) + out_base)[64 * j + lane] = kj;
-                (reinterpret_cast<uint4*>(p.v_out[ag]) + out_base)[64 * j + lane] = vj;
+                st_stream(reinterpret_cast<uint4*>(p.k_out[ag]) + out_base + 64 * j + lane, kj);
+                st_stream(reinterpret_cast<uint4*>(p.v_out[ag]) + out_base + 64 * j + lane, vj);
             }
         }
     }
@@ -870,7 +870,7 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
     // load first, check the header while the load is in flight
     const uint4 x = p.src[s & 1u][e];
     if (!pool_header_valid(p.pool, p.L, p.H, p.T, p.D, p.total)) return;
-    p.dst[s][e] = x;
+    st_stream(p.dst[s] + e, x);
 }
 
 }  // namespace

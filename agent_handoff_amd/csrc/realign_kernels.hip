@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kBlockThreads) void realign_keys_kernel(RealignPara
             rb[t] = pack_bf16x2(a1, b1);
         }
     }
-    *reinterpret_cast<uint4*>(y + oa) = make_uint4(ra[0], ra[1], ra[2], ra[3]);
-    *reinterpret_cast<uint4*>(y + ob) = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+    st_stream(reinterpret_cast<uint4*>(y + oa), make_uint4(ra[0], ra[1], ra[2], ra[3]));
+    st_stream(reinterpret_cast<uint4*>(y + ob), make_uint4(rb[0], rb[1], rb[2], rb[3]));
 }
 
 }  // namespace
