@@ -706,7 +706,10 @@ __device__ __forceinline__ bool pool_header_valid(const uint8_t* pool, uint32_t 
            hd[5] == D && t == total;
 }
 
-template <int D>
+// KEEP: plain stores (a fan-out copy reads the output back at once); else
+// non-temporal. A template argument, not a runtime flag: the compiler
+// merges two otherwise identical store branches and drops the hint.
+template <int D, bool KEEP>
 __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams p) {
     constexpr int C = D / 4;
     const uint32_t lane = lane_id();
@@ -824,8 +827,15 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
         if ((64 * j + lane) / (4 * CH) < nv) {
             const uint4 kj = kc[j], vj = vc[j];
             for (uint32_t ag = 0; ag < p.n_out; ++ag) {
-                st_stream(reinterpret_cast<uint4*>(p.k_out[ag]) + out_base + 64 * j + lane, kj);
-                st_stream(reinterpret_cast<uint4*>(p.v_out[ag]) + out_base + 64 * j + lane, vj);
+                uint4* kd = reinterpret_cast<uint4*>(p.k_out[ag]) + out_base + 64 * j + lane;
+                uint4* vd = reinterpret_cast<uint4*>(p.v_out[ag]) + out_base + 64 * j + lane;
+                if (KEEP) {
+                    *kd = kj;
+                    *vd = vj;
+                } else {
+                    st_stream(kd, kj);
+                    st_stream(vd, vj);
+                }
             }
         }
     }
@@ -960,7 +970,14 @@ hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uin
         p.v_out[a] = a < p.n_out ? static_cast<uint16_t*>(v_out[a]) : nullptr;
     }
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    hipError_t e = launch_kernel(s.d == 64 ? pool_decode_kernel<64> : pool_decode_kernel<128>,
+    // agent 0's output is read back at once by the fan-out copy: plain
+    // stores leave it in the caches for that (15 agents: 1378 -> 1350 us);
+    // without a fan-out the non-temporal hint is faster (one agent:
+    // 131 -> 107 us)
+    void (*kernel)(DecodeParams) =
+        s.d == 64 ? (fanout ? pool_decode_kernel<64, true> : pool_decode_kernel<64, false>)
+                  : (fanout ? pool_decode_kernel<128, true> : pool_decode_kernel<128, false>);
+    hipError_t e = launch_kernel(kernel,
                                  dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
     if (e != hipSuccess || !fanout) return e;
 
