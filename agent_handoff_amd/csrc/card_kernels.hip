@@ -467,10 +467,14 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
     const uint32_t w_in = p.w_in[tc], w_out = p.w_out[tc];
     if (flags != 0) return;
 
-    __shared__ uint4 stage_in[kBlockThreads / kWave][kSpanChunks];
-    __shared__ uint4 stage_out[kBlockThreads / kWave][kSpanChunks];
-    uint4* si = stage_in[threadIdx.x / kWave];
-    uint4* so = stage_out[threadIdx.x / kWave];
+    // One LDS image per wave holds the input span, then the output span: every
+    // lane's group reads (in the rebuild below, whatever its width) are issued
+    // before any lane's group writes, and a wave's LDS operations complete in
+    // order. (A second image doubled the LDS of a workgroup and halved the
+    // waves a CU can hold.)
+    __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
+    uint4* si = stage[threadIdx.x / kWave];
+    uint4* so = si;
     {
         const uint32_t n16 = (uint32_t)((a1 - a0) / 16);
         const uint4* src = reinterpret_cast<const uint4*>(p.card_in + p.payload + s * S_in + a0);
@@ -497,7 +501,9 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
         } else {
             dequant_group<8>(rin, G, g, o);
         }
-        // ... and quantise it at the new width (as pack does)
+        // ... and quantise it at the new width (as pack does); the barrier
+        // keeps every lane's reads above ahead of the writes below
+        __builtin_amdgcn_wave_barrier();
         uint8_t* rout = reinterpret_cast<uint8_t*>(so) + (uint32_t)(my_b - b0);
         if (w_out == 16) {
 #pragma unroll
