@@ -60,12 +60,18 @@ struct CardParams {
 };
 
 __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
-    __shared__ uint64_t sums[kScanThreads];
+    constexpr int kScanWaves = kScanThreads / kWave;
+    __shared__ uint32_t wave_tot[kScanWaves];
     __shared__ uint32_t bad;
     __shared__ uint32_t flags_sh;
     const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid % kWave, w = tid / kWave;
     if (tid == 0) bad = 0;
     __syncthreads();
+    // Chunks of kScanThreads * kScanItems tokens: each thread sums its
+    // tokens' record sizes, the wave scans the sums with lane shifts, and the
+    // waves' totals go through LDS (two barriers per chunk). A chunk's bytes
+    // fit 32 bits (at most 8192 records of at most 256 bytes).
     uint64_t carry = 0;
     for (uint64_t base = 0; base < p.T; base += (uint64_t)kScanThreads * kScanItems) {
         const uint64_t t0 = base + (uint64_t)tid * kScanItems;
@@ -81,22 +87,28 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
             rs[i] = r;
             local += r;
         }
-        sums[tid] = local;
-        __syncthreads();
-        // Hillis-Steele inclusive scan of the per-thread totals
-        for (int o = 1; o < kScanThreads; o <<= 1) {
-            const uint64_t add = tid >= (uint32_t)o ? sums[tid - o] : 0;
-            __syncthreads();
-            sums[tid] += add;
-            __syncthreads();
+        uint32_t inc = local;  // inclusive scan within the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t t = (uint32_t)__shfl_up((int)inc, o);
+            if (lane >= (uint32_t)o) inc += t;
         }
-        uint64_t run = carry + sums[tid] - local;  // exclusive prefix of this thread
+        if (lane == kWave - 1) wave_tot[w] = inc;
+        __syncthreads();
+        uint32_t before = 0, chunk = 0;
+#pragma unroll
+        for (int k = 0; k < kScanWaves; ++k) {
+            const uint32_t v = wave_tot[k];
+            before += (uint32_t)k < w ? v : 0u;
+            chunk += v;
+        }
+        uint64_t run = carry + before + inc - local;  // exclusive prefix of this thread
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) {
             if (t0 + i < p.T) p.off[t0 + i] = run;
             run += rs[i];
         }
-        carry += sums[kScanThreads - 1];
+        carry += chunk;
         __syncthreads();
     }
     const uint64_t S = align_up(carry, 256);
