@@ -425,11 +425,11 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     // half the write bandwidth).
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) st[lane * 4 + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    for (int c = 0; c < 4; ++c) st[stage_slot<4>(lane, c)] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     uint4* dst = reinterpret_cast<uint4*>((kv ? p.v_out : p.k_out) + (((uint64_t)l * p.H + h) * p.T + t0) * D);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint4 chunk = st[64 * j + lane];
+        const uint4 chunk = st[stage_pos<4>(64 * j + lane)];
         if ((64 * j + lane) / (2 * D / 16) < nv) st_stream(dst + 64 * j + lane, chunk);
     }
 }

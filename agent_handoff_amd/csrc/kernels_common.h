@@ -119,6 +119,22 @@ inline hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, 
 
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Swizzled per-wave LDS staging of an output image of 64 * N 16-byte chunks,
+// where lane l produces chunks l*N .. l*N + N - 1 and lane i later reads
+// chunks 64j + i. Chunk c of lane l goes to slot (c + l / (16 / N)) mod N of
+// the lane's N slots: without it the lanes of one 16-lane LDS cycle write at
+// a stride of N chunks and meet in the same banks (N-way conflicts); with it
+// they cover all 64 banks, and the reads stay within one 256-byte run.
+template <int N>
+__device__ __forceinline__ uint32_t stage_slot(uint32_t l, uint32_t c) {
+    constexpr uint32_t S = N == 4 ? 2 : (N == 2 ? 3 : 4);
+    return l * N + ((c + (l >> S)) & (N - 1));
+}
+template <int N>
+__device__ __forceinline__ uint32_t stage_pos(uint32_t p) {
+    return stage_slot<N>(p / N, p % N);
+}
+
 // Stores of the big outputs (written once, not read again by the same
 // kernel) carry the non-temporal hint. Measured on MI355X over the codec
 // step: encode 194 -> 170 us, card pack 192 -> 153 us, one-agent decode

@@ -362,11 +362,11 @@ __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const Block
     constexpr int KC = C / 16;  // 16-byte chunks of codes per lane
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-        stg.k[lane * KC + c] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
+        stg.k[stage_slot<KC>(lane, c)] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
     uint4* dst = reinterpret_cast<uint4*>(p.pool + p.lay.k_codes + b.vec0 * D);
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-        const uint4 chunk16 = stg.k[64 * j + lane];
+        const uint4 chunk16 = stg.k[stage_pos<KC>(64 * j + lane)];
         if ((64 * j + lane) / (D / 16) < b.nv) st_stream(dst + 64 * j + lane, chunk16);
     }
     if (b.bidx == 0 && lane == 0)
@@ -783,11 +783,11 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
             o[2 * j + 1] = pack_bf16x2(f2, f3);
         }
 #pragma unroll
-        for (int c = 0; c < CH; ++c) st[lane * CH + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+        for (int c = 0; c < CH; ++c) st[stage_slot<CH>(lane, c)] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     }
     uint4 kc[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) kc[j] = st[64 * j + lane];
+    for (int j = 0; j < CH; ++j) kc[j] = st[stage_pos<CH>(64 * j + lane)];
 
     // ---- values: level lookup by the code bits of this lane, then the
     // butterfly, then * (s / sqrt(d)).
@@ -813,11 +813,11 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
 #pragma unroll
         for (int j = 0; j < C / 2; ++j) o[j] = pack_bf16x2(y[2 * j] * a, y[2 * j + 1] * a);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) st[lane * CH + c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+        for (int c = 0; c < CH; ++c) st[stage_slot<CH>(lane, c)] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     }
     uint4 vc[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) vc[j] = st[64 * j + lane];
+    for (int j = 0; j < CH; ++j) vc[j] = st[stage_pos<CH>(64 * j + lane)];
 
     // chunk 64*j + lane of the image belongs to token (64*j + lane) / (4*CH).
     // (Writing each agent's spans back to back instead of interleaving the
