@@ -210,6 +210,42 @@ int kvc_lowrank_materialize(const kvc_shape* shape, uint32_t rank, uint32_t n_an
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
+size_t kvc_lowrank_factor_workspace_bytes(const kvc_shape* shape, uint32_t rank) {
+    if (!pool_shape(shape) || rank != 32) return 0;
+    return (size_t)kvc::lowrank_factor_ws(shape->num_layers, shape->num_kv_heads, shape->num_tokens, shape->head_dim)
+        .total;
+}
+
+int kvc_lowrank_factor(const kvc_shape* shape, uint32_t rank, const void* z, const float* omega, void* a_out,
+                       uint64_t a_stride, void* r_out, uint64_t r_stride, float* sigma_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    if (!shape || !z || !omega || !a_out || !r_out || !ws) return KVC_E_NULL;
+    if (!pool_shape(shape)) return KVC_E_SHAPE;
+    const uint32_t L = shape->num_layers, H = shape->num_kv_heads, T = shape->num_tokens, d = shape->head_dim;
+    if ((uint64_t)L * H > 65535 || L > 65535) return KVC_E_SHAPE;
+    if (rank != 32) return KVC_E_RANGE;
+    const uint64_t Dt = (uint64_t)H * d;
+    if (a_stride < (uint64_t)T * rank || r_stride < Dt * rank) return KVC_E_RANGE;
+    const uint64_t need = kvc::lowrank_factor_ws(L, H, T, d).total;
+    if (ws_bytes < need) return KVC_E_SIZE;
+    if (!aligned(z, 16) || !aligned(omega, 16) || !aligned(a_out, 16) || !aligned(r_out, 16) || !aligned(ws, 256) ||
+        a_stride % 8 != 0 || r_stride % 8 != 0 || (sigma_out && !aligned(sigma_out, 4)))
+        return KVC_E_ALIGN;
+    const uint64_t zb = kv_bytes(shape), ob = Dt * kvc::kLowrankSketch * 4;
+    const uint64_t ab = ((uint64_t)(L - 1) * a_stride + (uint64_t)T * rank) * 2;
+    const uint64_t rb = ((uint64_t)(L - 1) * r_stride + Dt * rank) * 2, sb = sigma_out ? (uint64_t)L * rank * 4 : 0;
+    const void* outs[4] = {a_out, r_out, ws, sigma_out};
+    const uint64_t outn[4] = {ab, rb, need, sb};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], outn[i], z, zb) || overlap(outs[i], outn[i], omega, ob)) return KVC_E_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return KVC_E_ALIAS;
+    }
+    const hipError_t e = kvc::launch_lowrank_factor(L, H, T, d, z, omega, a_out, a_stride, r_out, r_stride, sigma_out,
+                                                    ws, stream);
+    return e == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
 size_t cachecard_transcode_workspace_bytes(const kvc_shape* shape) {
     if (!card_shape(shape)) return 0;
     return (size_t)(2 * card_ws_bytes(shape));

@@ -59,4 +59,16 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
                                       const void* src, const void* a, const void* rf, const float* w, void* out,
                                       hipStream_t stream);
 
+// Rank-32 truncated SVD of M matrices T x (H*d) (randomized range finder,
+// 48-column Gaussian sketch supplied by the caller). Workspace offsets in
+// bytes (256-aligned) and total.
+constexpr uint32_t kLowrankSketch = 48;
+struct LowrankFactorWs {
+    uint64_t y, w, part, rinv, ua, ur, sigma, total;
+};
+LowrankFactorWs lowrank_factor_ws(uint32_t M, uint32_t H, uint32_t T, uint32_t d);
+hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d, const void* z, const float* omega,
+                                 void* a_out, uint64_t a_stride, void* r_out, uint64_t r_stride, float* sigma_out,
+                                 void* ws, hipStream_t stream);
+
 }  // namespace kvc

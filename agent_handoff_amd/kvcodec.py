@@ -65,6 +65,8 @@ def _load():
         "cachecard_transcode": (i32, [sp, p, sz, p, p, sz, p, p, p, sz, p]),
         "kvc_realign_keys": (i32, [sp, p, p, ctypes.c_int64, p, u32, p]),
         "kvc_lowrank_materialize": (i32, [sp, u32, u32, p, p, p, p, p, p]),
+        "kvc_lowrank_factor_workspace_bytes": (sz, [sp, u32]),
+        "kvc_lowrank_factor": (i32, [sp, u32, p, p, p, ctypes.c_uint64, p, ctypes.c_uint64, p, p, sz, p]),
         "kvc_parse_header": (i32, [p, sz, sp, ctypes.POINTER(u32)]),
         "kvc_strerror": (ctypes.c_char_p, [i32]),
         "kvc_codebook": (None, [p, p]),
@@ -81,7 +83,8 @@ EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_d
             "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
             "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack",
             "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_realign_keys",
-            "kvc_lowrank_materialize", "kvc_parse_header",
+            "kvc_lowrank_materialize", "kvc_lowrank_factor_workspace_bytes", "kvc_lowrank_factor",
+            "kvc_parse_header",
             "kvc_strerror", "kvc_codebook")
 
 
@@ -233,6 +236,43 @@ def kvc_lowrank_materialize(shape, rank, n_anchors, src, a, r, weights, out, str
     _check(_lib.kvc_lowrank_materialize(ctypes.byref(_shape(shape)), int(rank), int(n_anchors), _ptr(src),
                                         _ptr(a), _ptr(r), _ptr(weights), _ptr(out), _stream(stream)),
            "kvc_lowrank_materialize")
+
+
+LOWRANK_SKETCH = 48
+
+
+def kvc_lowrank_factor_workspace_bytes(shape, rank=32):
+    return int(_lib.kvc_lowrank_factor_workspace_bytes(ctypes.byref(_shape(shape)), int(rank)))
+
+
+def kvc_lowrank_factor(shape, rank, z, omega, a_out, r_out, ws, a_stride=None, r_stride=None, sigma_out=None,
+                       stream=None):
+    """z: bf16 device tensor [L, H, T, d]; omega: float32 device tensor
+    [H*d, 48]; a_out / r_out: bf16 device tensors holding A (T x rank) and R
+    (H*d x rank) of matrix l at element offset l * a_stride / l * r_stride
+    (defaults: packed); ws: device bytes; sigma_out: float32 [L, rank] or
+    None."""
+    L, H, T, d = shape
+    a_stride = T * rank if a_stride is None else a_stride
+    r_stride = H * d * rank if r_stride is None else r_stride
+
+    def base(t, row):
+        # a view of strided outputs (e.g. anchor v of [L][V][T][r]): its own
+        # rows must be contiguous; the layer stride is the explicit argument
+        if not t.is_cuda:
+            raise ValueError("expected a GPU tensor")
+        if t.dim() != 3 or t.shape[0] != L or t.shape[2] != rank or t.stride(2) != 1 or t.stride(1) != rank \
+                or t.shape[1] != row:
+            raise ValueError("expected a [L, rows, rank] view with contiguous rows")
+        return ctypes.c_void_p(t.data_ptr())
+
+    a_ptr, r_ptr = base(a_out, T), base(r_out, H * d)
+    if L > 1 and (a_out.stride(0) != a_stride or r_out.stride(0) != r_stride):
+        raise ValueError("layer strides of the views differ from a_stride / r_stride")
+    _check(_lib.kvc_lowrank_factor(ctypes.byref(_shape(shape)), int(rank), _ptr(z), _ptr(omega), a_ptr,
+                                   int(a_stride), r_ptr, int(r_stride), _ptr(sigma_out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)),
+           "kvc_lowrank_factor")
 
 
 # ------------------------------------------------------------------ host utils

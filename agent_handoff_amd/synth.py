@@ -178,6 +178,27 @@ def anchor_factors(seed, cfg, L, V, T, D, r, delta=0.25, decay=0.85):
     return A, R, w
 
 
+def lowrank_caches(seed, cfg, L, H, T, d, rank=32, noise=0.02, decay=0.9):
+    """bf16 bits [L, H, T, d] whose per-layer T x (H*d) view is a rank-`rank`
+    signal (singular profile 3 * decay**k on near-orthonormal directions)
+    plus N(0, noise^2) elements: the low effective rank the pages report for
+    base caches and delta corrections."""
+    D = H * d
+    out = np.empty((L, H, T, d), np.uint16)
+    for l in range(L):
+        g = rng(seed, cfg, ANCHOR_TENSOR, 10000 + l)
+        a = g.standard_normal((T, rank)) * (3.0 * decay ** np.arange(rank))
+        r = np.linalg.qr(g.standard_normal((D, rank)))[0]
+        z = a @ r.T + noise * g.standard_normal((T, D))
+        f32_to_bf16_bits(z.reshape(T, H, d).transpose(1, 0, 2).astype(np.float32), out=out[l])
+    return out
+
+
+def sketch(seed, cfg, D, k=48):
+    """The Gaussian test matrix of the randomized SVD: float32 [D, k], N(0, 1)."""
+    return rng(seed, cfg, ANCHOR_TENSOR, 20000).standard_normal((D, k), dtype=np.float32)
+
+
 # ------------------------------------------------------------------ on-device
 # The same recipes drawn on the GPU with torch's generator (Philox), for the
 # large workloads of the benchmark. Values differ from the numpy streams of

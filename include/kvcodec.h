@@ -278,6 +278,43 @@ int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int6
 int kvc_lowrank_materialize(const kvc_shape* shape, uint32_t rank, uint32_t n_anchors, const void* src,
                             const void* a, const void* r, const float* weights, void* out, hipStream_t stream);
 
+/* Workspace bytes for kvc_lowrank_factor (0 if the shape or rank is invalid). */
+size_t kvc_lowrank_factor_workspace_bytes(const kvc_shape* shape, uint32_t rank);
+
+/* Rank-r truncated SVD of cache matrices (KVCMAS, "what differs": the base
+ * caches and delta corrections an anchor stores are kept as truncated SVDs
+ * Z ~ U_r S_r R_r^T, A = U_r S_r, R = R_r). Matrix l is the T x (H*d) view of
+ * z[l] (row t, column h*d + c = element [l][h][t][c]). The page does not fix
+ * the algorithm; this is the randomized range finder with one power
+ * iteration (Halko, Martinsson and Tropp, 2011) on a caller-supplied
+ * Gaussian sketch, CholeskyQR in binary64 for every orthonormalisation, and
+ * a binary64 Jacobi eigensolver for the 48 x 48 projected problem; the
+ * matrix products run in binary32. Where the spectrum has a gap at r
+ * (sigma_r clearly above sigma_{r+1}) the result agrees with the exact
+ * truncated SVD up to the bf16 rounding of the factors; otherwise A R^T is
+ * a rank-r approximation whose error is within a few percent of the
+ * optimal one.
+ *   shape       L matrices, H, T, d (64 or 128); L * H <= 65535
+ *   rank        r: 32
+ *   z           device bf16 [L][H][T][d], 16-byte aligned
+ *   omega       device f32 [H*d][48], row-major: independent N(0, 1) draws
+ *               (the sketch; the caller owns the random numbers)
+ *   a_out       device bf16: A of matrix l at a_out + l * a_stride, T x r
+ *               row-major; a_stride >= T * r, a multiple of 8 (so anchor v
+ *               of a [L][V][T][r] array is a_out = base + v*T*r,
+ *               a_stride = V*T*r)
+ *   r_out       device bf16: R of matrix l at r_out + l * r_stride, (H*d) x r
+ *               row-major; r_stride >= H*d*r, a multiple of 8
+ *   sigma_out   device f32 [L][r] or NULL: singular values, descending
+ *   ws          device workspace, 256-byte aligned,
+ *               >= kvc_lowrank_factor_workspace_bytes
+ * Singular values equal to 0 give zero columns in A and R.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_RANGE (rank, strides), KVC_E_SIZE,
+ * KVC_E_ALIGN, KVC_E_ALIAS, KVC_E_HIP. */
+int kvc_lowrank_factor(const kvc_shape* shape, uint32_t rank, const void* z, const float* omega, void* a_out,
+                       uint64_t a_stride, void* r_out, uint64_t r_stride, float* sigma_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
 /* --------------------------------------------------------------- host utils */
 
 /* Parse a pool or card header from host bytes; *kind = 1 (pool) or 2

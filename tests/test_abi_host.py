@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -255,3 +255,34 @@ def test_lowrank_argument_errors():
     assert lr(out=2 * A + 512) == kv.KVC_E_ALIAS             # output over the A factors
     assert lr(out=3 * A) == kv.KVC_E_ALIAS
     assert lr(weights=4 * A + 16) == kv.KVC_E_ALIAS
+
+
+def test_lowrank_factor_argument_errors():
+    S2 = kv.kvc_shape(2, 2, 64, 128)
+    need = L.kvc_lowrank_factor_workspace_bytes(ctypes.byref(S2), 32)
+    assert need > 0
+    assert L.kvc_lowrank_factor_workspace_bytes(ctypes.byref(S2), 16) == 0
+    assert L.kvc_lowrank_factor_workspace_bytes(ctypes.byref(kv.kvc_shape(2, 2, 64, 96)), 32) == 0
+
+    def lf(shape=S2, rank=32, z=A, om=2 * A, a=3 * A, a_stride=64 * 32, r=4 * A, r_stride=256 * 32, sig=None,
+           ws=5 * A, ws_bytes=need):
+        return L.kvc_lowrank_factor(ctypes.byref(shape) if shape is not None else None, rank, z, om, a, a_stride, r,
+                                    r_stride, sig, ws, ws_bytes, None)
+
+    assert lf(shape=None) == kv.KVC_E_NULL
+    assert lf(om=None) == kv.KVC_E_NULL
+    assert lf(ws=None) == kv.KVC_E_NULL
+    assert lf(shape=kv.kvc_shape(2, 2, 64, 96)) == kv.KVC_E_SHAPE
+    assert lf(shape=kv.kvc_shape(70000, 1, 64, 128)) == kv.KVC_E_SHAPE
+    assert lf(rank=64) == kv.KVC_E_RANGE
+    assert lf(a_stride=64 * 32 - 8) == kv.KVC_E_RANGE
+    assert lf(r_stride=256 * 32 - 8) == kv.KVC_E_RANGE
+    assert lf(ws_bytes=need - 1) == kv.KVC_E_SIZE
+    assert lf(a=3 * A + 8) == kv.KVC_E_ALIGN
+    assert lf(ws=5 * A + 128) == kv.KVC_E_ALIGN
+    assert lf(a_stride=64 * 32 + 4) == kv.KVC_E_ALIGN
+    assert lf(sig=6 * A + 2) == kv.KVC_E_ALIGN
+    assert lf(a=A + 256) == kv.KVC_E_ALIAS                  # A written over the cache
+    assert lf(r=3 * A + 1024) == kv.KVC_E_ALIAS             # R over A
+    assert lf(ws=4 * A + 1024) == kv.KVC_E_ALIAS                # workspace over R
+    assert lf(sig=2 * A + 64) == kv.KVC_E_ALIAS             # sigma over the sketch
