@@ -64,7 +64,7 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
 // bytes (256-aligned) and total.
 constexpr uint32_t kLowrankSketch = 48;
 struct LowrankFactorWs {
-    uint64_t y, w, part, rinv, ua, ur, sigma, total;
+    uint64_t y, w, part, rinv, gpart, ua, ur, sigma, total;
 };
 LowrankFactorWs lowrank_factor_ws(uint32_t M, uint32_t H, uint32_t T, uint32_t d);
 hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d, const void* z, const float* omega,

@@ -13,9 +13,9 @@
 //   W = Z^T Q (= B^T, B = Q^T Z);  C = W^T W = U Lambda U^T (Jacobi)
 //   A = Q U_r Lambda_r^(1/2),  R = W U_r Lambda_r^(-1/2)
 //
-// orth() is CholeskyQR applied twice (Gram matrix and Cholesky factor in
-// binary64, a pivot at or below 1e-12 of the largest diagonal drops its
-// column), the products with Z run in binary32 on the vector units (Z is
+// orth() is CholeskyQR (Gram matrix and Cholesky factor in binary64, a
+// pivot at or below 1e-12 of the largest diagonal drops its column), once
+// inside the power iteration and twice for the final Q, the products with Z run in binary32 on the vector units (Z is
 // bf16, exact in binary32), and the 48 x 48 eigenproblem is solved by
 // parallel cyclic Jacobi in binary64. A and R are rounded once to bf16.
 //
@@ -32,7 +32,6 @@ constexpr int kFR = 32;              // rank
 constexpr int kFChunk = 256;         // tokens per partial product of Z^T Q
 constexpr int kFThreads = 256;
 constexpr int kFSweeps = 16;         // Jacobi sweep limit
-constexpr int kFEntries = kFK * (kFK + 1) / 2;  // 1176 Gram entries (i <= j)
 
 // Y[m](t, :) = Z[m](t, :) X[m]; X is D x 48 row-major binary32, x_stride
 // elements apart per matrix (0: one X for all). Block: 64 tokens x 4 waves
@@ -149,52 +148,68 @@ __global__ __launch_bounds__(kFThreads) void fac_reduce_kernel(const float* part
     w[i] = s;
 }
 
-// G = Y^T Y (48 x 48, binary64) of an N x 48 binary32 matrix, by one block:
-// rows pass through LDS 64 at a time; thread k owns Gram entries k, k + 256,
-// ... of the upper triangle (i <= j, row-major).
-__device__ __forceinline__ void entry_ij(uint32_t e, uint32_t& i, uint32_t& j) {
-    // e -> (i, j) with i <= j, rows of the upper triangle in order
-    uint32_t r = 0, n = kFK;
+// Partial Gram matrices: Gp[m][chunk] = Y_chunk^T Y_chunk (48 x 48,
+// binary64) over chunks of 256 rows, one block per (chunk, matrix); the
+// chunk's rows pass through LDS and each thread owns a 3 x 3 tile of the
+// upper triangle of tiles.
+constexpr int kGRows = 256;
+constexpr int kGTile = 3;
+constexpr int kGTiles = kFK / kGTile;                    // 16 tiles per side
+constexpr int kGTilePairs = kGTiles * (kGTiles + 1) / 2;  // 136
+
+__global__ __launch_bounds__(kFThreads) void fac_gram_partial_kernel(const float* y, uint32_t N, uint32_t nchunks,
+                                                                     double* gpart) {
+    __shared__ float4 ys[kGRows * kFK / 4];
+    const uint32_t chunk = blockIdx.x, m = blockIdx.y;
+    const uint32_t r0 = chunk * kGRows;
+    const uint32_t nr = (N - r0 < (uint32_t)kGRows) ? N - r0 : (uint32_t)kGRows;
+    const float4* src = reinterpret_cast<const float4*>(y + ((uint64_t)m * N + r0) * kFK);
+    for (uint32_t i = threadIdx.x; i < nr * kFK / 4; i += kFThreads) ys[i] = src[i];
+    __syncthreads();
+    double* out = gpart + ((uint64_t)m * nchunks + chunk) * kFK * kFK;
+    if (threadIdx.x >= (uint32_t)kGTilePairs) return;  // no barrier follows
+    uint32_t ti = 0, e = threadIdx.x, n = kGTiles;
     while (e >= n) {
         e -= n;
-        ++r;
+        ++ti;
         --n;
     }
-    i = r;
-    j = r + e;
+    const uint32_t tj = ti + e;  // tile (ti, tj), ti <= tj
+    const float* yf = reinterpret_cast<const float*>(ys);
+    double acc[kGTile][kGTile];
+#pragma unroll
+    for (int a = 0; a < kGTile; ++a)
+#pragma unroll
+        for (int b = 0; b < kGTile; ++b) acc[a][b] = 0.0;
+    for (uint32_t r = 0; r < nr; ++r) {
+        double u[kGTile], v[kGTile];
+#pragma unroll
+        for (int a = 0; a < kGTile; ++a) {
+            u[a] = yf[r * kFK + ti * kGTile + a];
+            v[a] = yf[r * kFK + tj * kGTile + a];
+        }
+#pragma unroll
+        for (int a = 0; a < kGTile; ++a)
+#pragma unroll
+            for (int b = 0; b < kGTile; ++b) acc[a][b] = fma(u[a], v[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < kGTile; ++a)
+#pragma unroll
+        for (int b = 0; b < kGTile; ++b) {
+            const uint32_t i = ti * kGTile + a, j = tj * kGTile + b;
+            out[i * kFK + j] = acc[a][b];
+            out[j * kFK + i] = acc[a][b];
+        }
 }
 
-__device__ void block_gram(const float* ym, uint32_t N, double* g, float* ys) {
-    constexpr int EP = (kFEntries + kFThreads - 1) / kFThreads;  // 5
-    double acc[EP];
-    uint32_t ei[EP], ej[EP];
-#pragma unroll
-    for (int u = 0; u < EP; ++u) {
-        acc[u] = 0.0;
-        const uint32_t e = threadIdx.x + u * kFThreads;
-        if (e < (uint32_t)kFEntries) entry_ij(e, ei[u], ej[u]);
-        else ei[u] = ej[u] = 0;
-    }
-    for (uint32_t r0 = 0; r0 < N; r0 += 64) {
-        const uint32_t nr = (N - r0 < 64u) ? N - r0 : 64u;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nr * kFK / 4; i += kFThreads)
-            reinterpret_cast<float4*>(ys)[i] = reinterpret_cast<const float4*>(ym + (uint64_t)r0 * kFK)[i];
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < EP; ++u) {
-            double s = acc[u];
-            for (uint32_t rr = 0; rr < nr; ++rr) s = fma((double)ys[rr * kFK + ei[u]], (double)ys[rr * kFK + ej[u]], s);
-            acc[u] = s;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < EP; ++u) {
-        const uint32_t e = threadIdx.x + u * kFThreads;
-        if (e < (uint32_t)kFEntries) {
-            g[ei[u] * kFK + ej[u]] = acc[u];
-            g[ej[u] * kFK + ei[u]] = acc[u];
-        }
+// g = sum of the chunks' partial Gram matrices, chunks in order
+__device__ __forceinline__ void sum_gram(const double* gpart, uint32_t m, uint32_t nchunks, double* g) {
+    const double* gp = gpart + (uint64_t)m * nchunks * kFK * kFK;
+    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) {
+        double s = 0.0;
+        for (uint32_t c = 0; c < nchunks; ++c) s += gp[(uint64_t)c * kFK * kFK + i];
+        g[i] = s;
     }
     __syncthreads();
 }
@@ -202,12 +217,11 @@ __device__ void block_gram(const float* ym, uint32_t N, double* g, float* ys) {
 // One CholeskyQR step, factor part: G = Y^T Y = L L^T, then Rinv = (L^T)^-1
 // (upper triangular), binary64. A pivot at or below 1e-12 of the largest
 // diagonal entry drops its column: its row and column of Rinv are zero.
-__global__ __launch_bounds__(kFThreads) void fac_gram_chol_kernel(const float* y, uint32_t N, double* rinv) {
-    __shared__ float ys[64 * kFK];
+__global__ __launch_bounds__(kFThreads) void fac_chol_kernel(const double* gpart, uint32_t nchunks, double* rinv) {
     __shared__ double g[kFK * kFK];
     __shared__ double L[kFK * kFK];
     const uint32_t m = blockIdx.x;
-    block_gram(y + (uint64_t)m * N * kFK, N, g, ys);
+    sum_gram(gpart, m, nchunks, g);
     for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) L[i] = 0.0;
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -282,27 +296,26 @@ __global__ __launch_bounds__(kFThreads) void fac_apply_rinv_kernel(float* y, uin
     for (int q = 0; q < kFK / 4; ++q) yr[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
 
-// C = W^T W, eigenpairs by parallel cyclic Jacobi (round-robin pairing: 24
-// disjoint rotations per step, 47 steps per sweep), binary64; writes
-// ua = U_r diag(sigma), ur = U_r diag(1/sigma) (0 where sigma = 0), both
-// 48 x 32 binary32, and sigma (descending).
-__global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const float* w, uint32_t N, float* ua, float* ur,
-                                                                  float* sigma) {
-    __shared__ float ys[64 * kFK];
+// C = W^T W (from its partial Gram matrices), eigenpairs by parallel cyclic
+// Jacobi (round-robin pairing: 24 disjoint rotations per step, 47 steps per
+// sweep; each thread applies both sides of the rotations to whole 2 x 2
+// blocks, so a step is one pass), binary64, until the off-diagonal part is
+// below 1e-12 of the diagonal (in norm); writes ua = U_r diag(sigma),
+// ur = U_r diag(1/sigma) (0 where sigma = 0), both 48 x 32 binary32, and
+// sigma (descending).
+__global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const double* gpart, uint32_t nchunks, float* ua,
+                                                                  float* ur, float* sigma) {
     __shared__ double a[kFK * kFK];
     __shared__ double v[kFK * kFK];
     __shared__ double rc[kFK / 2], rs[kFK / 2];
     __shared__ uint32_t rp[kFK / 2], rq[kFK / 2];
-    __shared__ double red[kFThreads / kWave];
+    __shared__ double red[2][kFThreads / kWave];
     __shared__ uint32_t order[kFK];
-    __shared__ uint32_t done;
     const uint32_t m = blockIdx.x;
-    block_gram(w + (uint64_t)m * N * kFK, N, a, ys);
+    sum_gram(gpart, m, nchunks, a);
     for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) v[i] = (i / kFK == i % kFK) ? 1.0 : 0.0;
-    if (threadIdx.x == 0) done = 0;
     __syncthreads();
     for (int sweep = 0; sweep < kFSweeps; ++sweep) {
-        // convergence: off-diagonal mass against the diagonal's
         double off = 0.0, dia = 0.0;
         for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) {
             const double x = a[i];
@@ -313,72 +326,71 @@ __global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const float* w
             off += __shfl_xor(off, o);
             dia += __shfl_xor(dia, o);
         }
-        __syncthreads();
-        if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = off;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double so = 0.0;
-            for (int k = 0; k < kFThreads / kWave; ++k) so += red[k];
-            red[0] = so;
+        if (threadIdx.x % kWave == 0) {
+            red[0][threadIdx.x / kWave] = off;
+            red[1][threadIdx.x / kWave] = dia;
         }
         __syncthreads();
-        const double off_all = red[0];
-        __syncthreads();
-        if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = dia;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double sd = 0.0;
-            for (int k = 0; k < kFThreads / kWave; ++k) sd += red[k];
-            done = (off_all <= 1e-30 * sd) ? 1u : 0u;
+        double so = 0.0, sd = 0.0;
+        for (int k = 0; k < kFThreads / kWave; ++k) {
+            so += red[0][k];
+            sd += red[1][k];
         }
-        __syncthreads();
-        if (done) break;
+        __syncthreads();  // red is rewritten at the next sweep
+        if (so <= 1e-24 * sd) break;  // every thread takes the same branch
         for (uint32_t step = 0; step < (uint32_t)kFK - 1; ++step) {
             // pairs: position 0 holds index 0, positions 1..47 rotate
             if (threadIdx.x < (uint32_t)kFK / 2) {
                 const uint32_t i = threadIdx.x;
-                auto at = [&](uint32_t pos) -> uint32_t { return pos == 0 ? 0u : 1u + (pos - 1 + step) % (kFK - 1); };
-                uint32_t p = at(i), q = at(kFK - 1 - i);
+                const uint32_t pa = i, pb = kFK - 1 - i;
+                uint32_t p = pa == 0 ? 0u : 1u + (pa - 1 + step) % (kFK - 1);
+                uint32_t q = 1u + (pb - 1 + step) % (kFK - 1);
                 if (p > q) {
                     const uint32_t t = p;
                     p = q;
                     q = t;
                 }
                 const double apq = a[p * kFK + q];
-                double c = 1.0, s = 0.0;
+                double c = 1.0, sn = 0.0;
                 if (apq != 0.0) {
                     const double tau = (a[q * kFK + q] - a[p * kFK + p]) / (2.0 * apq);
                     const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
                     c = 1.0 / sqrt(1.0 + t * t);
-                    s = t * c;
+                    sn = t * c;
                 }
                 rp[i] = p;
                 rq[i] = q;
                 rc[i] = c;
-                rs[i] = s;
+                rs[i] = sn;
             }
             __syncthreads();
-            // rows p, q of A <- J^T A
-            for (uint32_t k = threadIdx.x; k < (uint32_t)(kFK / 2) * kFK; k += kFThreads) {
-                const uint32_t i = k / kFK, j = k % kFK;
-                const uint32_t p = rp[i], q = rq[i];
-                const double c = rc[i], s = rs[i];
-                const double x = a[p * kFK + j], y2 = a[q * kFK + j];
-                a[p * kFK + j] = c * x - s * y2;
-                a[q * kFK + j] = s * x + c * y2;
-            }
-            __syncthreads();
-            // columns p, q of A <- A J, and of V <- V J
-            for (uint32_t k = threadIdx.x; k < (uint32_t)(kFK / 2) * kFK; k += kFThreads) {
-                const uint32_t i = k / kFK, j = k % kFK;
-                const uint32_t p = rp[i], q = rq[i];
-                const double c = rc[i], s = rs[i];
-                const double x = a[j * kFK + p], y2 = a[j * kFK + q];
-                a[j * kFK + p] = c * x - s * y2;
-                a[j * kFK + q] = s * x + c * y2;
-                const double vx = v[j * kFK + p], vy = v[j * kFK + q];
-                v[j * kFK + p] = c * vx - s * vy;
-                v[j * kFK + q] = s * vx + c * vy;
+            // A <- J^T A J on 2 x 2 blocks (pair P rows, pair Q columns), and
+            // V <- V J on rows j, pair Q
+            constexpr uint32_t NP = kFK / 2;
+            for (uint32_t k = threadIdx.x; k < NP * NP + kFK * NP; k += kFThreads) {
+                if (k < NP * NP) {
+                    const uint32_t P = k / NP, Q = k % NP;
+                    const uint32_t p0 = rp[P], p1 = rq[P], q0 = rp[Q], q1 = rq[Q];
+                    const double cP = rc[P], sP = rs[P], cQ = rc[Q], sQ = rs[Q];
+                    const double m00 = a[p0 * kFK + q0], m01 = a[p0 * kFK + q1];
+                    const double m10 = a[p1 * kFK + q0], m11 = a[p1 * kFK + q1];
+                    // rows: J^T M
+                    const double r00 = cP * m00 - sP * m10, r01 = cP * m01 - sP * m11;
+                    const double r10 = sP * m00 + cP * m10, r11 = sP * m01 + cP * m11;
+                    // columns: (J^T M) J
+                    a[p0 * kFK + q0] = cQ * r00 - sQ * r01;
+                    a[p0 * kFK + q1] = sQ * r00 + cQ * r01;
+                    a[p1 * kFK + q0] = cQ * r10 - sQ * r11;
+                    a[p1 * kFK + q1] = sQ * r10 + cQ * r11;
+                } else {
+                    const uint32_t t = k - NP * NP;
+                    const uint32_t j = t / NP, Q = t % NP;
+                    const uint32_t q0 = rp[Q], q1 = rq[Q];
+                    const double c = rc[Q], sn = rs[Q];
+                    const double x = v[j * kFK + q0], y2 = v[j * kFK + q1];
+                    v[j * kFK + q0] = c * x - sn * y2;
+                    v[j * kFK + q1] = sn * x + c * y2;
+                }
             }
             __syncthreads();
         }
@@ -463,6 +475,8 @@ LowrankFactorWs lowrank_factor_ws(uint32_t M, uint32_t H, uint32_t T, uint32_t d
     w.w = take((uint64_t)M * Dt * kFK * 4);
     w.part = take((uint64_t)M * nchunks * Dt * kFK * 4);
     w.rinv = take((uint64_t)M * kFK * kFK * 8);
+    const uint64_t gchunks = (((uint64_t)T > Dt ? (uint64_t)T : Dt) + kGRows - 1) / kGRows;
+    w.gpart = take((uint64_t)M * gchunks * kFK * kFK * 8);
     w.ua = take((uint64_t)M * kFK * kFR * 4);
     w.ur = take((uint64_t)M * kFK * kFR * 4);
     w.sigma = take((uint64_t)M * kFR * 4);
@@ -479,6 +493,7 @@ hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d,
     float* W = reinterpret_cast<float*>(base + L.w);
     float* P = reinterpret_cast<float*>(base + L.part);
     double* Rinv = reinterpret_cast<double*>(base + L.rinv);
+    double* Gp = reinterpret_cast<double*>(base + L.gpart);
     float* UA = reinterpret_cast<float*>(base + L.ua);
     float* UR = reinterpret_cast<float*>(base + L.ur);
     float* sig = sigma_out ? sigma_out : reinterpret_cast<float*>(base + L.sigma);
@@ -504,23 +519,35 @@ hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d,
         e = launch_kernel(fac_reduce_kernel, dim3((uint32_t)((n + kFThreads - 1) / kFThreads)), blk, stream,
                           (const float*)P, W, M, per, nchunks);
     };
-    auto orth = [&](float* x, uint32_t N) {
-        for (int rep = 0; rep < 2 && e == hipSuccess; ++rep) {
-            e = launch_kernel(fac_gram_chol_kernel, dim3(M), blk, stream, (const float*)x, N, Rinv);
+    auto gram = [&](const float* x, uint32_t N) -> uint32_t {
+        const uint32_t nc = (N + kGRows - 1) / kGRows;
+        if (e == hipSuccess) e = launch_kernel(fac_gram_partial_kernel, dim3(nc, M), blk, stream, x, N, nc, Gp);
+        return nc;
+    };
+    auto orth = [&](float* x, uint32_t N, int reps) {
+        for (int rep = 0; rep < reps && e == hipSuccess; ++rep) {
+            const uint32_t nc = gram(x, N);
+            if (e != hipSuccess) return;
+            e = launch_kernel(fac_chol_kernel, dim3(M), blk, stream, (const double*)Gp, nc, Rinv);
             if (e != hipSuccess) return;
             e = launch_kernel(fac_apply_rinv_kernel, dim3((N + kFThreads - 1) / kFThreads, M), blk, stream, x, N,
                               (const double*)Rinv);
         }
     };
-    zx(omega, 0);          // Y = Z Omega
-    orth(Y, T);            // Q
-    ztq();                 // W = Z^T Q
-    orth(W, Dt);           // orth(W)
+    // the power iteration's bases only need to be well conditioned (one
+    // CholeskyQR pass); the final Q is orthonormalised twice
+    zx(omega, 0);               // Y = Z Omega
+    orth(Y, T, 1);              // Q
+    ztq();                      // W = Z^T Q
+    orth(W, Dt, 1);             // orth(W)
     zx(W, (uint64_t)Dt * kFK);  // Y = Z W
-    orth(Y, T);            // Q
-    ztq();                 // W = Z^T Q = B^T
-    if (e == hipSuccess)
-        e = launch_kernel(fac_small_svd_kernel, dim3(M), blk, stream, (const float*)W, Dt, UA, UR, sig);
+    orth(Y, T, 2);              // Q
+    ztq();                      // W = Z^T Q = B^T
+    {
+        const uint32_t nc = gram(W, Dt);
+        if (e == hipSuccess)
+            e = launch_kernel(fac_small_svd_kernel, dim3(M), blk, stream, (const double*)Gp, nc, UA, UR, sig);
+    }
     if (e == hipSuccess)
         e = launch_kernel(fac_finalize_kernel, dim3((T + kFThreads - 1) / kFThreads, M), blk, stream, (const float*)Y,
                           T, (const float*)UA, static_cast<uint16_t*>(a_out), a_stride);

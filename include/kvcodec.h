@@ -287,7 +287,7 @@ size_t kvc_lowrank_factor_workspace_bytes(const kvc_shape* shape, uint32_t rank)
  * z[l] (row t, column h*d + c = element [l][h][t][c]). The page does not fix
  * the algorithm; this is the randomized range finder with one power
  * iteration (Halko, Martinsson and Tropp, 2011) on a caller-supplied
- * Gaussian sketch, CholeskyQR in binary64 for every orthonormalisation, and
+ * Gaussian sketch, CholeskyQR in binary64 for the orthonormalisations, and
  * a binary64 Jacobi eigensolver for the 48 x 48 projected problem; the
  * matrix products run in binary32. Where the spectrum has a gap at r
  * (sigma_r clearly above sigma_{r+1}) the result agrees with the exact
