@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+synth_sketch_cols = 48  # columns of the randomized SVD's Gaussian sketch
 FANOUT_MIN_AGENTS = 8  # the library decodes into this many agents or more as decode + fan-out copy
 METRIC = "KV codec encode/decode GB/s and % of HBM peak, Llama-3-8B shape 4K tok"
 
@@ -212,6 +213,18 @@ def main():
                                       "frac_mfma_bf16_peak": round(fl / tl / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                       "anchors": n_anc, "rank": rank}
     del fk, fv
+    # the write-once side of the anchors: the rank-32 truncated SVD of the K
+    # cache (32 layers of 4096 x 1024), randomized on a 48-column sketch
+    om = torch.from_numpy(synth.sketch(args.seed, 7, H * d)).to(dev)
+    fa = torch.empty((L, T, rank), dtype=torch.bfloat16, device=dev)
+    fr = torch.empty((L, H * d, rank), dtype=torch.bfloat16, device=dev)
+    fws = torch.empty(kv.kvc_lowrank_factor_workspace_bytes(shape, rank), dtype=torch.uint8, device=dev)
+    tf = timed(lambda: kv.kvc_lowrank_factor(shape, rank, k, om, fa, fr, fws, stream=stream), 5)
+    ff = 4 * 2.0 * L * T * H * d * synth_sketch_cols
+    ops_out["lowrank_factor"] = {"us": round(tf * 1e6, 2), "bytes": 4 * kv_bytes, "GB/s": round(4 * kv_bytes / tf / 1e9, 1),
+                                 "TFLOP/s": round(ff / tf / 1e12, 2), "rank": rank, "sketch": synth_sketch_cols,
+                                 "note": "Z read four times (two products with Z, two with Z^T), vector fp32"}
+    del fa, fr, fws
     drift = hop_drift(kv, synth, k, v, shape, widths_np, args.seed, stream, dev)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set beside the step"
@@ -322,7 +335,8 @@ CALIBRATION_BYTES = 1 << 30
 CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_kernel",
                  "key_absmax_kernel",
                  "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
-                 "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel"]
+                 "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel",
+                 "fac_zx_kernel", "fac_ztq_kernel"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
