@@ -26,7 +26,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
-synth_sketch_cols = 48  # columns of the randomized SVD's Gaussian sketch
 FANOUT_MIN_AGENTS = 8  # the library decodes into this many agents or more as decode + fan-out copy
 METRIC = "KV codec encode/decode GB/s and % of HBM peak, Llama-3-8B shape 4K tok"
 
@@ -220,9 +219,9 @@ def main():
     fr = torch.empty((L, H * d, rank), dtype=torch.bfloat16, device=dev)
     fws = torch.empty(kv.kvc_lowrank_factor_workspace_bytes(shape, rank), dtype=torch.uint8, device=dev)
     tf = timed(lambda: kv.kvc_lowrank_factor(shape, rank, k, om, fa, fr, fws, stream=stream), 5)
-    ff = 4 * 2.0 * L * T * H * d * synth_sketch_cols
+    ff = 4 * 2.0 * L * T * H * d * kv.LOWRANK_SKETCH
     ops_out["lowrank_factor"] = {"us": round(tf * 1e6, 2), "bytes": 4 * kv_bytes, "GB/s": round(4 * kv_bytes / tf / 1e9, 1),
-                                 "TFLOP/s": round(ff / tf / 1e12, 2), "rank": rank, "sketch": synth_sketch_cols,
+                                 "TFLOP/s": round(ff / tf / 1e12, 2), "rank": rank, "sketch": kv.LOWRANK_SKETCH,
                                  "note": "Z read four times (two products with Z, two with Z^T), vector fp32"}
     del fa, fr, fws
     drift = hop_drift(kv, synth, k, v, shape, widths_np, args.seed, stream, dev)
