@@ -175,17 +175,17 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
         p.card_out[kCardHeaderBytes + i] = i < p.T ? p.widths[i] : 0;
 }
 
-// One 32-channel group at width b (2, 4 or 8): returns the packed codes in
-// out[0 .. b-1] (b dwords = 32 codes of b bits, least significant first).
-// Code j is rne(min((x_j - mn) * inv, qmax)), which equals
-// min(rne((x_j - mn) * inv), qmax) as qmax is an integer; the rounding, the
-// clamp at 255 and the placement in a byte are one v_cvt_pk_u8_f32 (round to
-// nearest even, saturating; checked against rintf on the GPU for a million
-// values), which builds the codes as bytes; widths 4 and 2 then narrow the
-// byte fields with shifts and masks.
-template <int B>
-__device__ __forceinline__ void quant_group(const float (&x)[32], uint16_t& sbits, uint16_t& mbits,
-                                            uint32_t (&out)[8]) {
+// One 32-channel group at a per-lane width b (2, 4 or 8): the codes as
+// bytes, code j in byte j % 4 of by[j / 4]. Code j is
+// rne(min((x_j - mn) * inv, qmax)), which equals min(rne((x_j - mn) * inv),
+// qmax) as qmax is an integer; the rounding, the clamp at 255 and the
+// placement in a byte are one v_cvt_pk_u8_f32 (round to nearest even,
+// saturating; checked against rintf on the GPU for a million values). The
+// arithmetic is the same at every width but for qmax, so a wave whose tokens
+// mix widths runs it once; only the narrowing of the bytes to b-bit fields
+// (narrow_codes) depends on the width.
+__device__ __forceinline__ void quant_group(const float (&x)[32], uint32_t b, uint16_t& sbits, uint16_t& mbits,
+                                            uint32_t (&by)[8]) {
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int j = 1; j < 32; ++j) {
@@ -194,12 +194,11 @@ __device__ __forceinline__ void quant_group(const float (&x)[32], uint16_t& sbit
     }
     mn = mn + 0.0f;
     mx = mx + 0.0f;
-    constexpr float qmax = (float)((1 << B) - 1);
+    const float qmax = (float)((1u << b) - 1u);
     const float s = (mx - mn) / qmax;
     const _Float16 s16 = (_Float16)__builtin_fminf(s, 65504.0f);
     const float sf = (float)s16;
     const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
-    uint32_t by[8];  // code j in byte j % 4 of by[j / 4]
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
         uint32_t acc = 0;
@@ -210,6 +209,14 @@ __device__ __forceinline__ void quant_group(const float (&x)[32], uint16_t& sbit
         }
         by[d] = acc;
     }
+    sbits = __builtin_bit_cast(uint16_t, s16);
+    mbits = (uint16_t)(__float_as_uint(mn) >> 16);
+}
+
+// Byte codes (each below 2^B) -> B-bit fields, 32 codes in B dwords, least
+// significant first (out[0 .. B-1]).
+template <int B>
+__device__ __forceinline__ void narrow_codes(const uint32_t (&by)[8], uint32_t (&out)[8]) {
     if (B == 8) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) out[w] = by[w];
@@ -238,8 +245,6 @@ __device__ __forceinline__ void quant_group(const float (&x)[32], uint16_t& sbit
             out[w] = acc;
         }
     }
-    sbits = __builtin_bit_cast(uint16_t, s16);
-    mbits = (uint16_t)(__float_as_uint(mn) >> 16);
 }
 
 template <int B>
@@ -251,6 +256,23 @@ __device__ __forceinline__ void store_group(uint8_t* rec, uint32_t G, uint32_t g
     uint2* dst = reinterpret_cast<uint2*>(rec + 4 * G + g * 4 * B);
 #pragma unroll
     for (int i = 0; i < B / 2; ++i) dst[i] = make_uint2(codes[2 * i], codes[2 * i + 1]);
+}
+
+// Quantise one group at width b in {2, 4, 8} into its record.
+__device__ __forceinline__ void quant_store_group(const float (&x)[32], uint32_t b, uint8_t* rec, uint32_t G,
+                                                  uint32_t g) {
+    uint16_t sb, mb;
+    uint32_t by[8], codes[8];
+    quant_group(x, b, sb, mb, by);
+    if (b == 2) {
+        narrow_codes<2>(by, codes);
+        store_group<2>(rec, G, g, sb, mb, codes);
+    } else if (b == 4) {
+        narrow_codes<4>(by, codes);
+        store_group<4>(rec, G, g, sb, mb, codes);
+    } else {
+        store_group<8>(rec, G, g, sb, mb, by);
+    }
 }
 
 // Per-wave LDS image of the wave's records: its tokens are consecutive, so
@@ -307,18 +329,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
                 x[2 * j] = bf16_lo(w[j]);
                 x[2 * j + 1] = bf16_hi(w[j]);
             }
-            uint16_t sb, mb;
-            uint32_t codes[8];
-            if (width == 2) {
-                quant_group<2>(x, sb, mb, codes);
-                store_group<2>(rec, G, g, sb, mb, codes);
-            } else if (width == 4) {
-                quant_group<4>(x, sb, mb, codes);
-                store_group<4>(rec, G, g, sb, mb, codes);
-            } else {
-                quant_group<8>(x, sb, mb, codes);
-                store_group<8>(rec, G, g, sb, mb, codes);
-            }
+            quant_store_group(x, width, rec, G, g);
             // zero the record's tail padding (present for d = 64)
             const uint32_t used = 4 * G + D * width / 8;
             const uint32_t R = card_record_bytes(D, width);
@@ -340,28 +351,60 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
         for (uint64_t i = p.off[p.T]; i < S; i += 16) *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
 }
 
-template <int B>
-__device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t (&o)[16]) {
+// The codes of one group at a per-lane width b (2, 4 or 8) from its record,
+// widened to bytes: code j in byte j % 4 of by[j / 4].
+__device__ __forceinline__ void widen_codes(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t b,
+                                            uint32_t (&by)[8]) {
+    // codes start 8-byte aligned (4*G is a multiple of 8, records 16-aligned)
+    const uint2* src = reinterpret_cast<const uint2*>(rec + 4 * G + g * 4 * b);
+    if (b == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint2 c = src[i];
+            by[2 * i] = c.x;
+            by[2 * i + 1] = c.y;
+        }
+    } else if (b == 4) {
+        // codes 4k .. 4k+3 are the nibbles of half k % 2 of dword k / 2
+        uint32_t c[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint2 v = src[i];
+            c[2 * i] = v.x;
+            c[2 * i + 1] = v.y;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t t = c[k / 2] >> (16 * (k % 2));
+            const uint32_t x = (t & 0xFFu) | ((t & 0xFF00u) << 8);
+            by[k] = (x | (x << 4)) & 0x0F0F0F0Fu;
+        }
+    } else {
+        // codes 4k .. 4k+3 are the 2-bit fields of byte k % 4 of dword k / 4
+        const uint2 v = src[0];
+        const uint32_t c[2] = {v.x, v.y};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t t = (c[k / 4] >> (8 * (k % 4))) & 0xFFu;
+            const uint32_t x = (t | (t << 12)) & 0x000F000Fu;
+            by[k] = (x | (x << 6)) & 0x03030303u;
+        }
+    }
+}
+
+// One group at width b in {2, 4, 8} back to 32 bf16 values (o: pairs, channel
+// 2j in the low half of o[j]): q*s + mn in binary32 with one rounding (q*s
+// alone is exact), then bf16 round to nearest even. Only the widening of the
+// codes depends on the width: a wave whose tokens mix widths converts once.
+__device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t b,
+                                              uint32_t (&o)[16]) {
     const float sf = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(rec)[g]);
     const float mn = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rec)[G + g] << 16);
-    const uint2* src = reinterpret_cast<const uint2*>(rec + 4 * G + g * 4 * B);
-    uint32_t codes[B];
-#pragma unroll
-    for (int i = 0; i < B / 2; ++i) {
-        const uint2 c = src[i];
-        codes[2 * i] = c.x;
-        codes[2 * i + 1] = c.y;
-    }
-    constexpr int PER = 32 / B;
-    constexpr uint32_t MASK = (1u << B) - 1u;
-    // q*s + mn in binary32 with one rounding (q*s alone is exact), then bf16
-    // round to nearest even (pack_bf16x2)
+    uint32_t by[8];
+    widen_codes(rec, G, g, b, by);
     float y[32];
 #pragma unroll
-    for (int w = 0; w < B; ++w)
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            y[w * PER + j] = __builtin_fmaf((float)((codes[w] >> (B * j)) & MASK), sf, mn);
+    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf((float)((by[j / 4] >> (8 * (j % 4))) & 0xFFu), sf, mn);
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[j] = pack_bf16x2(y[2 * j], y[2 * j + 1]);
 }
@@ -411,12 +454,8 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
         if (width == 16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
-        } else if (width == 2) {
-            dequant_group<2>(rec, G, g, o);
-        } else if (width == 4) {
-            dequant_group<4>(rec, G, g, o);
         } else {
-            dequant_group<8>(rec, G, g, o);
+            dequant_group(rec, G, g, width, o);
         }
     }
     // Stage the wave's contiguous output image in LDS (over the records,
@@ -506,12 +545,8 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
         if (w_in == 16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rin + 64 * g)[i];
-        } else if (w_in == 2) {
-            dequant_group<2>(rin, G, g, o);
-        } else if (w_in == 4) {
-            dequant_group<4>(rin, G, g, o);
         } else {
-            dequant_group<8>(rin, G, g, o);
+            dequant_group(rin, G, g, w_in, o);
         }
         // ... and quantise it at the new width (as pack does); the barrier
         // keeps every lane's reads above ahead of the writes below
@@ -527,18 +562,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
                 x[2 * j] = bf16_lo(o[j]);
                 x[2 * j + 1] = bf16_hi(o[j]);
             }
-            uint16_t sb, mb;
-            uint32_t codes[8];
-            if (w_out == 2) {
-                quant_group<2>(x, sb, mb, codes);
-                store_group<2>(rout, G, g, sb, mb, codes);
-            } else if (w_out == 4) {
-                quant_group<4>(x, sb, mb, codes);
-                store_group<4>(rout, G, g, sb, mb, codes);
-            } else {
-                quant_group<8>(x, sb, mb, codes);
-                store_group<8>(rout, G, g, sb, mb, codes);
-            }
+            quant_store_group(x, w_out, rout, G, g);
             // zero the record's tail padding (present for d = 64)
             const uint32_t used = 4 * G + D * w_out / 8;
             const uint32_t R = card_record_bytes(D, w_out);
