@@ -34,6 +34,7 @@
 #include "launch.h"
 #include "layout.h"
 
+#include <cstdlib>
 #include <utility>
 
 namespace kvc {
@@ -54,6 +55,7 @@ struct EncodeParams {
     uint32_t blocks_per_layer;  // H * nb
     uint32_t layers_per_round;  // single-pass encode: whole layers per round
     uint64_t n_waves;           // L * H * nb
+    uint64_t poll_ticks;        // single-pass encode: bound on the wait for other workgroups' maxima
     PoolLayout lay;
 };
 
@@ -403,9 +405,9 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
 //
 // The key scale of a layer needs every key of the layer, so the two-pass
 // encode reads K twice. Here K is read once and parked in LDS: a
-// cooperative persistent grid (all workgroups co-resident, one per CU at
-// this LDS size) walks the layers in rounds of whole layers; each of a
-// workgroup's 8 worker waves takes 4 KiB of keys per round.
+// persistent grid (one workgroup per CU at this LDS size) walks the layers
+// in rounds of whole layers; each of a workgroup's 8 worker waves takes
+// 4 KiB of keys per round.
 //
 // Worker wave, iteration r:
 //   a. issue the loads of its round-r block(s);
@@ -421,14 +423,23 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
 // Only the coordinator waits on device-scope memory, so the workers' load
 // counters never wait for a poll, and a round of work separates each
 // publication from the wait for it.
+//
+// The grid is an ordinary launch: nothing guarantees that every workgroup
+// is resident at once (another kernel may hold CUs). A coordinator that has
+// not seen every workgroup's word for a layer within poll_ticks computes
+// the layer's maximum itself from the keys in HBM. Both routes give the same
+// exact maximum, so residency decides only the speed; no wait depends on a
+// workgroup that may not be running.
 constexpr int kFusedWorkers = 8;
 constexpr int kFusedThreads = (kFusedWorkers + 1) * kWave;
 constexpr int kHoldRounds = 3;
 constexpr uint32_t kMaxRoundLayers = 32;
 constexpr uint32_t kMaxFusedGrid = 1024;  // workgroups; sizes the flag words of the workspace
 constexpr uint32_t kFlag = 0x80000000u;
-// Spin limit of every wait, in ticks of the 100 MHz constant clock: 0.5 s,
-// far beyond any legitimate wait.
+// Spin limit of the waits inside a workgroup (workers for their
+// coordinator, coordinator for its workers), in ticks of the 100 MHz
+// constant clock: 0.5 s. These waits depend only on the workgroup's own
+// waves, so the limit is a guard against a hang, never expected to trip.
 constexpr uint64_t kWaitTicks = 50000000ull;
 
 __device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t L, uint32_t l) {
@@ -473,6 +484,27 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
     return r;
 }
 
+// Largest key magnitude (bf16 bits) of layer l, read from the keys in HBM
+// by one wave: the same exact value that the workgroups' published maxima
+// reduce to. Used by a coordinator whose wait for those maxima ran out.
+template <int D>
+__device__ uint32_t layer_absmax_direct(const EncodeParams& p, uint32_t l, uint32_t lane) {
+    const uint64_t n = (uint64_t)p.H * p.T * (D / 8);  // uint4 per layer
+    const uint4* src = reinterpret_cast<const uint4*>(p.k) + (uint64_t)l * n;
+    uint32_t m = 0;
+    for (uint64_t i = lane; i < n; i += 4 * kWave) {
+        uint4 raw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t idx = i + (uint64_t)j * kWave;
+            raw[j] = idx < n ? src[idx] : make_uint4(0, 0, 0, 0);
+        }
+        const uint32_t x = lane_absmax_bits<4>(raw);
+        m = x > m ? x : m;
+    }
+    return wave_max_u32(m);
+}
+
 struct Round {
     uint32_t l0, nl, nblk;  // first layer, layers, blocks
 };
@@ -489,11 +521,12 @@ __device__ __forceinline__ uint32_t lds_load(const uint32_t* a) {
     return __hip_atomic_load(a, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Record that a wait gave up (never expected). The wait for all of the
-// wave's memory operations makes the flag performed before the wave's later
-// work, so workgroup 0 sees it before it writes the header. (Waiting here,
-// inside the rare branch, rather than on a returned value keeps the common
-// path free of a full wait that would drain the prefetched loads.)
+// Record that a wait inside the workgroup gave up (never expected). The
+// wait for all of the wave's memory operations makes the flag performed
+// before the wave's later work (the end-of-kernel checks below read it).
+// (Waiting here, inside the rare branch, rather than on a returned value
+// keeps the common path free of a full wait that would drain the
+// prefetched loads.)
 __device__ __forceinline__ void note_timeout(const EncodeParams& p) {
     __hip_atomic_fetch_or(p.ws + kWsTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
@@ -639,15 +672,16 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
                     v[i] = g < G ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlag;
                 }
                 const uint64_t start = wall_clock64();
+                bool all_flagged = false;
                 for (;;) {
                     bool all = true;
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) all = all && (v[i] & kFlag);
-                    if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
-                    if (wall_clock64() - start > kWaitTicks) {
-                        note_timeout(p);
+                    if (p.poll_ticks != 0 && __builtin_amdgcn_ballot_w64(!all) == 0) {
+                        all_flagged = true;
                         break;
                     }
+                    if (wall_clock64() - start >= p.poll_ticks) break;
                     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) {
@@ -656,12 +690,18 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
                     }
                 }
                 uint32_t mx = 0;
+                if (all_flagged) {
 #pragma unroll
-                for (int i = 0; i < kPer; ++i) {
-                    const uint32_t x = v[i] & ~kFlag;
-                    mx = x > mx ? x : mx;
+                    for (int i = 0; i < kPer; ++i) {
+                        const uint32_t x = v[i] & ~kFlag;
+                        mx = x > mx ? x : mx;
+                    }
+                    mx = wave_max_u32(mx);
+                } else {
+                    // some workgroup has not published (not resident yet, or
+                    // slow): the layer's maximum from its keys instead
+                    mx = layer_absmax_direct<D>(p, q.l0 + lr, lane);
                 }
-                mx = wave_max_u32(mx);
                 if (lane == 0) sm.layer_max[rq % kHoldRounds][lr] = mx;
             }
             if (lane == 0)
@@ -684,15 +724,26 @@ __global__ __launch_bounds__(kFusedThreads) void pool_encode_fused_kernel(Encode
         fused_worker<D>(p, sm, w, lane, nrounds);
     else
         fused_coordinator<D>(p, sm, lane, nrounds);
-    // Header and padding last, by workgroup 0: its coordinator saw every
-    // workgroup's last publication, so any timeout flag is visible by now,
-    // and no wait can time out after it.
+    // Header and padding last, by workgroup 0. A wait that gave up anywhere
+    // leaves the header's magic word zero (decode then refuses the pool):
+    // workgroup 0 checks the timeout flag before and again after writing the
+    // header, and a workgroup whose own wait gave up clears the word when it
+    // ends. Whatever the order of those events, one of the three sees the flag
+    // after the header is written or writes zero after it.
     __syncthreads();
+    uint32_t* magic = reinterpret_cast<uint32_t*>(p.pool);
     if (blockIdx.x == 0) {
         if (threadIdx.x < kBlockThreads) pool_header_and_padding(p, D, threadIdx.x);
-        if (threadIdx.x == 0 &&
-            __hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-            reinterpret_cast<uint32_t*>(p.pool)[0] = 0;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __threadfence();
+            if (__hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                __hip_atomic_store(magic, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else if (threadIdx.x == 0 &&
+               __hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        __hip_atomic_store(magic, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -883,6 +934,21 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
     st_stream(p.dst[s] + e, x);
 }
 
+// Bound on a coordinator's wait for the other workgroups' key maxima, in
+// ticks of the 100 MHz constant clock. Default 200 us: a resident grid
+// publishes a round within a few microseconds, so the bound trips only for
+// a workgroup that is not running. KVC_ENCODE_POLL_US overrides it; 0 makes
+// every coordinator compute each layer's maximum itself (tests use it).
+uint64_t encode_poll_ticks() {
+    uint64_t us = 200;
+    if (const char* e = std::getenv("KVC_ENCODE_POLL_US")) {
+        char* end = nullptr;
+        const unsigned long long v = std::strtoull(e, &end, 10);
+        if (end != e && *end == '\0' && v <= 10000000ull) us = v;
+    }
+    return us * 100;
+}
+
 }  // namespace
 
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
@@ -899,20 +965,21 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.blocks_per_layer = s.H * p.nb;
     p.layers_per_round = 0;
     p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
+    p.poll_ticks = encode_poll_ticks();
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
     const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L);
     hipError_t e = launch_kernel(fill_zero_kernel, dim3((ws_words + 255) / 256), dim3(256), stream, ws, ws_words);
     if (e != hipSuccess) return e;
 
-    // Single pass when one workgroup per CU can be co-resident and a round of
-    // whole layers fits the grid's LDS; otherwise two passes (the per-layer
-    // key maxima, then the encode proper).
+    // Single pass when a round of whole layers fits the LDS of a grid of one
+    // workgroup per CU; otherwise two passes (the per-layer key maxima, then
+    // the encode proper). The single pass is an ordinary launch: its waits
+    // never depend on every workgroup being resident (see the kernel).
     const void* fused = s.d == 64 ? reinterpret_cast<const void*>(pool_encode_fused_kernel<64>)
                                   : reinterpret_cast<const void*>(pool_encode_fused_kernel<128>);
-    int dev = 0, cus = 0, per_cu = 0, coop = 0;
+    int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, kFusedThreads, 0) == hipSuccess && per_cu > 0 &&
         (uint64_t)cus * (uint64_t)per_cu <= kMaxFusedGrid) {
@@ -924,8 +991,7 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
         if (lpr >= 1) {
             p.layers_per_round = (uint32_t)lpr;
             void* argv[] = {&p};
-            return report_launch(hipLaunchCooperativeKernel(fused, dim3((uint32_t)grid), dim3(kFusedThreads), argv, 0,
-                                                            stream),
+            return report_launch(hipLaunchKernel(fused, dim3((uint32_t)grid), dim3(kFusedThreads), argv, 0, stream),
                                  "pool_encode_fused_kernel");
         }
     }

@@ -242,3 +242,25 @@ def test_two_concurrent_encodes():
     torch.cuda.synchronize()
     for pool in outs:
         assert_pool_equal(pool.cpu().numpy(), ref, shape)
+
+
+@pytest.mark.parametrize("poll_us", ["0", "1"])
+@pytest.mark.parametrize("shape,cfg", [((1, 4, 256, 64), 1), ((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2),
+                                       ((40, 1, 16, 64), 1), ((32, 8, 4096, 128), 3)])
+def test_encode_layer_max_computed_directly(monkeypatch, poll_us, shape, cfg):
+    """The single-pass encode gathers each layer's key maximum from every
+    workgroup's published word; a coordinator that has not seen them all
+    within the poll bound reads the layer's keys itself. With a bound of 0
+    every coordinator takes that route for every layer, with 1 us whenever
+    a word is late: the pool must be the same bytes either way."""
+    monkeypatch.setenv("KVC_ENCODE_POLL_US", poll_us)
+    say("encode, poll bound", poll_us, "us, shape", shape)
+    k, v = _inputs(shape, cfg, 6)
+    assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
+
+
+def test_encode_poll_bound_restored_after_override():
+    """An encode with the default bound after the overridden ones above."""
+    shape = (3, 8, 512, 128)
+    k, v = _inputs(shape, 3, 7)
+    assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
