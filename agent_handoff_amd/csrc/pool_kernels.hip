@@ -406,23 +406,27 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
 // The key scale of a layer needs every key of the layer, so the two-pass
 // encode reads K twice. Here K is read once and parked in LDS: a
 // persistent grid (one workgroup per CU at this LDS size) walks the layers
-// in rounds of whole layers; each of a workgroup's 8 worker waves takes
-// 4 KiB of keys per round.
+// in rounds of whole layers. A workgroup owns 8 block slots per round (one
+// 16-token block each at d = 128, two at d = 64) and splits the work by
+// role, so that a SIMD holds three or four waves and the value transform's
+// VALU stream is not the only work it can issue:
 //
-// Worker wave, iteration r:
-//   a. issue the loads of its round-r block(s);
-//   b. wait (in LDS) until its workgroup's coordinator has the maxima of
-//      round r-2, then quantise the keys it parked in round r-2;
-//   c. encode round r's values, park its keys in LDS, fold its key maxima
-//      into the workgroup's (LDS atomics) and count itself done.
-// Coordinator wave (a ninth wave), round r: when the workers are done with
-// r, publish the workgroup's maxima of r as flag|max words (one per layer
-// and workgroup; one plain device-scope store each, no returning atomic),
-// then read every workgroup's words of round r-1 until all are flagged,
-// reduce them to the layer maxima and hand those to the workers in LDS.
-// Only the coordinator waits on device-scope memory, so the workers' load
-// counters never wait for a poll, and a round of work separates each
-// publication from the wait for it.
+// Value wave (8, one per slot): load round r+1's values, encode round r's
+// (scale, rotation, codes, stores). It never waits on another wave.
+// Key wave (4, two slots each), iteration r:
+//   a. issue the key loads of round r+1;
+//   b. park round r's keys in LDS, fold their maxima into the workgroup's
+//      (LDS atomics) and count itself done;
+//   c. wait (in LDS) until the coordinator has the layer maxima of round
+//      r-2, then quantise the keys parked in round r-2.
+// Coordinator wave, round r: when the key waves are done with r, publish
+// the workgroup's maxima of r as flag|max words (one per layer and
+// workgroup; one plain device-scope store each, no returning atomic), then
+// read every workgroup's words of round r-1 until all are flagged, reduce
+// them to the layer maxima and hand those to the key waves in LDS. Only the
+// coordinator waits on device-scope memory, so no load counter waits for a
+// poll, and a round of work separates each publication from the wait for
+// it.
 //
 // The grid is an ordinary launch: nothing guarantees that every workgroup
 // is resident at once (another kernel may hold CUs). A coordinator that has
@@ -430,14 +434,16 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
 // the layer's maximum itself from the keys in HBM. Both routes give the same
 // exact maximum, so residency decides only the speed; no wait depends on a
 // workgroup that may not be running.
-constexpr int kFusedWorkers = 8;
-constexpr int kFusedThreads = (kFusedWorkers + 1) * kWave;
+constexpr int kFusedSlots = 8;     // block slots per workgroup and round
+constexpr int kFusedKeyWaves = 4;    // key waves, kSlotsPerKeyWave slots each
+constexpr int kSlotsPerKeyWave = kFusedSlots / kFusedKeyWaves;
+constexpr int kFusedThreads = (kFusedSlots + kFusedKeyWaves + 1) * kWave;
 constexpr int kHoldRounds = 3;
 constexpr uint32_t kMaxRoundLayers = 32;
 constexpr uint32_t kMaxFusedGrid = 1024;  // workgroups; sizes the flag words of the workspace
 constexpr uint32_t kFlag = 0x80000000u;
-// Spin limit of the waits inside a workgroup (workers for their
-// coordinator, coordinator for its workers), in ticks of the 100 MHz
+// Spin limit of the waits inside a workgroup (key waves for their
+// coordinator, coordinator for its key waves), in ticks of the 100 MHz
 // constant clock: 0.5 s. These waits depend only on the workgroup's own
 // waves, so the limit is a guard against a hang, never expected to trip.
 constexpr uint64_t kWaitTicks = 50000000ull;
@@ -448,15 +454,15 @@ __device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t L, uint3
 
 template <int D>
 struct FusedLds {
-    static constexpr int kBpw = 128 / D;  // blocks per worker wave per round: 4 KiB of keys
-    uint4 hold[kHoldRounds][kFusedWorkers][kBpw][D / 32][kWave];  // [round % 3][wave][block][chunk][lane]
-    EncodeStage<D> stage[kFusedWorkers];
-    // By round % 3: a worker reaches round r only after its wait in round
+    static constexpr int kBpw = 128 / D;  // blocks per slot and round: 4 KiB of keys
+    uint4 hold[kHoldRounds][kFusedSlots][kBpw][D / 32][kWave];  // [round % 3][slot][block][chunk][lane]
+    EncodeStage<D> stage[kFusedSlots];  // per slot: .v by its value wave, .k by its key wave
+    // By round % 3: a key wave reaches round r only after its wait in round
     // r-1 saw the maxima of round r-3 ready, i.e. after the coordinator has
     // consumed and cleared the round-(r-3) entries that round r reuses.
     uint32_t wg_max[kHoldRounds][kMaxRoundLayers];     // this workgroup's key maxima
     uint32_t layer_max[kHoldRounds][kMaxRoundLayers];  // every workgroup's, per layer
-    uint32_t done[kHoldRounds];                        // workers done with the round
+    uint32_t done[kHoldRounds];                        // key waves done with the round
     uint32_t ready;                                    // rounds whose maxima are in layer_max
 };
 
@@ -532,66 +538,107 @@ __device__ __forceinline__ void note_timeout(const EncodeParams& p) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Block j of slot gw in round r (clamped: a block past the round's end, or
+// a round past the last, is block 0 of layer 0, loaded and never used).
 template <int D>
-struct FusedRaw {
-    uint4 k[FusedLds<D>::kBpw][D / 32];
+__device__ __forceinline__ BlockPos fused_block(const EncodeParams& p, uint32_t r, uint32_t nrounds, uint32_t gw,
+                                                uint32_t j, uint32_t NW, uint32_t lane) {
+    const bool live_round = r < nrounds;
+    const Round q = round_of(p, live_round ? r : 0);
+    const uint32_t bi = gw + j * NW;
+    const bool live = live_round && bi < q.nblk;
+    return block_pos<D>(p, live ? q.l0 + bi / p.blocks_per_layer : 0u, live ? bi % p.blocks_per_layer : 0u, lane);
+}
+
+template <int D>
+struct ValueRaw {
     uint4 v[FusedLds<D>::kBpw][D / 32];
 };
 
-// Loads of a worker wave's round-r block(s). Always issued, the same number
-// every time (a block past the round's end, or a round past the last, loads
-// block 0 of layer 0 and is never used): the waits for a round's data then
-// count exactly the loads issued after it, and never drain the prefetch.
 template <int D>
-__device__ __forceinline__ void fused_load(const EncodeParams& p, uint32_t r, uint32_t nrounds, uint32_t gw,
-                                           uint32_t NW, uint32_t lane, FusedRaw<D>& raw) {
-    const bool live_round = r < nrounds;
-    const Round q = round_of(p, live_round ? r : 0);
+struct KeyRaw {
+    uint4 k[kSlotsPerKeyWave][FusedLds<D>::kBpw][D / 32];
+};
+
+// Value wave: slot vw's values, round after round, one round of loads in
+// flight; no wait on any other wave.
+template <int D>
+__device__ __forceinline__ void value_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t vw, uint32_t lane,
+                                            uint32_t r, uint32_t nrounds, ValueRaw<D>& cur, ValueRaw<D>& fill) {
+    const uint32_t NW = gridDim.x * kFusedSlots;
+    const uint32_t gw = blockIdx.x * kFusedSlots + vw;
+#pragma unroll
+    for (int j = 0; j < FusedLds<D>::kBpw; ++j)
+        load_lane<D>(p.v, fused_block<D>(p, r + 1, nrounds, gw, j, NW, lane).elem, fill.v[j]);
+    const Round q = round_of(p, r);
 #pragma unroll
     for (int j = 0; j < FusedLds<D>::kBpw; ++j) {
         const uint32_t bi = gw + (uint32_t)j * NW;
-        const bool live = live_round && bi < q.nblk;
-        const BlockPos b = block_pos<D>(p, live ? q.l0 + bi / p.blocks_per_layer : 0u,
-                                        live ? bi % p.blocks_per_layer : 0u, lane);
-        load_lane<D>(p.k, b.elem, raw.k[j]);
-        load_lane<D>(p.v, b.elem, raw.v[j]);
+        if (bi < q.nblk) {
+            const BlockPos b = block_pos<D>(p, q.l0 + bi / p.blocks_per_layer, bi % p.blocks_per_layer, lane);
+            encode_values<D>(p, b, cur.v[j], sm.stage[vw], lane);
+        }
     }
 }
 
-// Worker iteration r: round r+1's loads go out first (into `fill`), then
-// round r (in `cur`, loaded one iteration earlier) is encoded, then round
-// r-2's keys are quantised: a round of work separates the workers' count
-// for a round from their wait for that round's maxima.
 template <int D>
-__device__ __forceinline__ void fused_worker_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t w, uint32_t lane,
-                                                   uint32_t r, uint32_t nrounds, FusedRaw<D>& cur,
-                                                   FusedRaw<D>& fill) {
+__device__ __forceinline__ void fused_value_wave(const EncodeParams& p, FusedLds<D>& sm, uint32_t vw, uint32_t lane,
+                                                 uint32_t nrounds) {
+    const uint32_t NW = gridDim.x * kFusedSlots;
+    const uint32_t gw = blockIdx.x * kFusedSlots + vw;
+    ValueRaw<D> a, b;
+#pragma unroll
+    for (int j = 0; j < FusedLds<D>::kBpw; ++j)
+        load_lane<D>(p.v, fused_block<D>(p, 0, nrounds, gw, j, NW, lane).elem, a.v[j]);
+    for (uint32_t r = 0; r < nrounds; r += 2) {
+        value_round<D>(p, sm, vw, lane, r, nrounds, a, b);
+        if (r + 1 < nrounds) value_round<D>(p, sm, vw, lane, r + 1, nrounds, b, a);
+    }
+}
+
+// Key wave kw, iteration r: round r+1's key loads go out first, then
+// round r's keys are parked and their maxima folded in, then round r-2's
+// keys are quantised: a round of work separates the wave's count for a
+// round from its wait for that round's maxima.
+template <int D>
+__device__ __forceinline__ void key_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t kw, uint32_t lane,
+                                          uint32_t r, uint32_t nrounds, KeyRaw<D>& cur, KeyRaw<D>& fill) {
     constexpr int BPW = FusedLds<D>::kBpw;
-    const uint32_t NW = gridDim.x * kFusedWorkers;  // worker waves in the grid
-    const uint32_t gw = blockIdx.x * kFusedWorkers + w;
-    fused_load<D>(p, r + 1, nrounds, gw, NW, lane, fill);
-    // round r's values and keys
+    const uint32_t NW = gridDim.x * kFusedSlots;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerKeyWave; ++i)
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+            load_lane<D>(p.k,
+                         fused_block<D>(p, r + 1, nrounds, blockIdx.x * kFusedSlots + kw * kSlotsPerKeyWave + i, j,
+                                        NW, lane)
+                             .elem,
+                         fill.k[i][j]);
     if (r < nrounds) {
         const Round q = round_of(p, r);
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-            const uint32_t bi = gw + (uint32_t)j * NW;
-            if (bi < q.nblk) {
-                const uint32_t lr = bi / p.blocks_per_layer;
-                const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
-                encode_values<D>(p, b, cur.v[j], sm.stage[w], lane);
-                const uint32_t m = wave_max_u32(b.valid ? lane_absmax_bits<D / 32>(cur.k[j]) : 0u);
+        for (int i = 0; i < kSlotsPerKeyWave; ++i) {
+            const uint32_t slot = kw * kSlotsPerKeyWave + i;
+            const uint32_t gw = blockIdx.x * kFusedSlots + slot;
 #pragma unroll
-                for (int i = 0; i < D / 32; ++i) sm.hold[r % kHoldRounds][w][j][i][lane] = cur.k[j][i];
-                if (lane == 0)
-                    __hip_atomic_fetch_max(&sm.wg_max[r % kHoldRounds][lr], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            for (int j = 0; j < BPW; ++j) {
+                const uint32_t bi = gw + (uint32_t)j * NW;
+                if (bi < q.nblk) {
+                    const uint32_t lr = bi / p.blocks_per_layer;
+                    const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                    const uint32_t m = wave_max_u32(b.valid ? lane_absmax_bits<D / 32>(cur.k[i][j]) : 0u);
+#pragma unroll
+                    for (int c = 0; c < D / 32; ++c) sm.hold[r % kHoldRounds][slot][j][c][lane] = cur.k[i][j][c];
+                    if (lane == 0)
+                        __hip_atomic_fetch_max(&sm.wg_max[r % kHoldRounds][lr], m, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
             }
         }
         // LDS operations of a wave complete in order: the maxima above land
         // before the count
         if (lane == 0) __hip_atomic_fetch_add(&sm.done[r % kHoldRounds], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // round r-2's keys
     if (r >= 2) {
         const uint32_t rq = r - 2;
         const uint64_t start = wall_clock64();
@@ -604,31 +651,44 @@ __device__ __forceinline__ void fused_worker_round(const EncodeParams& p, FusedL
         }
         const Round q = round_of(p, rq);
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-            const uint32_t bi = gw + (uint32_t)j * NW;
-            if (bi < q.nblk) {
-                const uint32_t lr = bi / p.blocks_per_layer;
-                const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
-                uint4 kr[D / 32];
+        for (int i = 0; i < kSlotsPerKeyWave; ++i) {
+            const uint32_t slot = kw * kSlotsPerKeyWave + i;
+            const uint32_t gw = blockIdx.x * kFusedSlots + slot;
 #pragma unroll
-                for (int i = 0; i < D / 32; ++i) kr[i] = sm.hold[rq % kHoldRounds][w][j][i][lane];
-                quantize_keys<D>(p, b, kr, lds_load(&sm.layer_max[rq % kHoldRounds][lr]), sm.stage[w], lane);
+            for (int j = 0; j < BPW; ++j) {
+                const uint32_t bi = gw + (uint32_t)j * NW;
+                if (bi < q.nblk) {
+                    const uint32_t lr = bi / p.blocks_per_layer;
+                    const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                    uint4 kr[D / 32];
+#pragma unroll
+                    for (int c = 0; c < D / 32; ++c) kr[c] = sm.hold[rq % kHoldRounds][slot][j][c][lane];
+                    quantize_keys<D>(p, b, kr, lds_load(&sm.layer_max[rq % kHoldRounds][lr]), sm.stage[slot], lane);
+                }
             }
         }
     }
 }
 
 template <int D>
-__device__ __forceinline__ void fused_worker(const EncodeParams& p, FusedLds<D>& sm, uint32_t w, uint32_t lane,
-                                             uint32_t nrounds) {
+__device__ __forceinline__ void fused_key_wave(const EncodeParams& p, FusedLds<D>& sm, uint32_t kw, uint32_t lane,
+                                               uint32_t nrounds) {
     // two register sets, alternating, one round of loads in flight (the loop
     // is unrolled by two so that both stay in registers)
-    FusedRaw<D> a, b;
-    const uint32_t gw = blockIdx.x * kFusedWorkers + w, NW = gridDim.x * kFusedWorkers;
-    fused_load<D>(p, 0, nrounds, gw, NW, lane, a);
+    KeyRaw<D> a, b;
+    const uint32_t NW = gridDim.x * kFusedSlots;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerKeyWave; ++i)
+#pragma unroll
+        for (int j = 0; j < FusedLds<D>::kBpw; ++j)
+            load_lane<D>(p.k,
+                         fused_block<D>(p, 0, nrounds, blockIdx.x * kFusedSlots + kw * kSlotsPerKeyWave + i, j, NW,
+                                        lane)
+                             .elem,
+                         a.k[i][j]);
     for (uint32_t r = 0; r < nrounds + 2; r += 2) {
-        fused_worker_round<D>(p, sm, w, lane, r, nrounds, a, b);
-        if (r + 1 < nrounds + 2) fused_worker_round<D>(p, sm, w, lane, r + 1, nrounds, b, a);
+        key_round<D>(p, sm, kw, lane, r, nrounds, a, b);
+        if (r + 1 < nrounds + 2) key_round<D>(p, sm, kw, lane, r + 1, nrounds, b, a);
     }
 }
 
@@ -638,10 +698,10 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
     const uint32_t G = gridDim.x;
     for (uint32_t r = 0; r <= nrounds; ++r) {
         if (r < nrounds) {
-            // the workers' round r, then this workgroup's maxima of it, published
+            // the key waves' round r, then this workgroup's maxima of it, published
             const Round q = round_of(p, r);
             const uint64_t start = wall_clock64();
-            while (lds_load(&sm.done[r % kHoldRounds]) < (uint32_t)kFusedWorkers) {
+            while (lds_load(&sm.done[r % kHoldRounds]) < (uint32_t)kFusedKeyWaves) {
                 if (wall_clock64() - start > kWaitTicks) {
                     note_timeout(p);
                     break;
@@ -720,8 +780,10 @@ __global__ __launch_bounds__(kFusedThreads) void pool_encode_fused_kernel(Encode
     if (threadIdx.x < kHoldRounds) sm.done[threadIdx.x] = 0;
     if (threadIdx.x == 0) sm.ready = 0;
     __syncthreads();
-    if (w < (uint32_t)kFusedWorkers)
-        fused_worker<D>(p, sm, w, lane, nrounds);
+    if (w < (uint32_t)kFusedSlots)
+        fused_value_wave<D>(p, sm, w, lane, nrounds);
+    else if (w < (uint32_t)(kFusedSlots + kFusedKeyWaves))
+        fused_key_wave<D>(p, sm, w - kFusedSlots, lane, nrounds);
     else
         fused_coordinator<D>(p, sm, lane, nrounds);
     // Header and padding last, by workgroup 0. A wait that gave up anywhere
@@ -984,7 +1046,7 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, kFusedThreads, 0) == hipSuccess && per_cu > 0 &&
         (uint64_t)cus * (uint64_t)per_cu <= kMaxFusedGrid) {
         const uint64_t grid = (uint64_t)cus * (uint64_t)per_cu;
-        const uint64_t per_round = grid * kFusedWorkers * (128u / s.d);  // blocks a round can hold
+        const uint64_t per_round = grid * kFusedSlots * (128u / s.d);  // blocks a round can hold
         uint64_t lpr = per_round / p.blocks_per_layer;
         if (lpr > kMaxRoundLayers) lpr = kMaxRoundLayers;
         if (lpr > s.L) lpr = s.L;

@@ -1,11 +1,12 @@
 """Model check of the single-pass encode's in-workgroup handshake (host
 logic, no GPU).
 
-The kernel's worker waves and its coordinator wave exchange, through LDS,
-each round's key maxima (wg_max), a count of workers done with the round
-(done) and the number of rounds whose layer maxima are ready (ready). The
-workers encode round r, then quantise round r-2 once ready > r-2; the
-coordinator waits until every worker is done with round r, takes and clears
+The kernel's key waves (the "workers" below) and its coordinator wave
+exchange, through LDS, each round's key maxima (wg_max), a count of key
+waves done with the round (done) and the number of rounds whose layer
+maxima are ready (ready). The key waves park round r, then quantise round
+r-2 once ready > r-2; the coordinator waits until every key wave is done
+with round r, takes and clears
 its entries, publishes, and marks round r-1 ready. This model runs those
 steps under random interleavings and checks that no count or maximum is
 lost and every round is quantised with its own maxima. With the entries
@@ -15,6 +16,8 @@ round r, and the count it adds is lost (the kernel's bounded wait would
 then give up and mark the pool invalid)."""
 
 import random
+
+import pytest
 
 
 def run(buffers, rounds, seed, workers=8):
@@ -74,11 +77,15 @@ def run(buffers, rounds, seed, workers=8):
             cstep = next(cg, None)
 
 
-def test_entries_by_round_mod_3_survive_every_schedule():
+@pytest.mark.parametrize("workers", [4, 8])
+def test_entries_by_round_mod_3_survive_every_schedule(workers):
+    """4: the kernel's key waves; 8: one wave per slot (the protocol does
+    not depend on the count)."""
     for seed in range(400):
-        assert run(3, 7, seed) == [], seed
+        assert run(3, 7, seed, workers) == [], seed
 
 
-def test_entries_by_round_parity_lose_counts():
-    failures = sum(1 for seed in range(200) if run(2, 7, seed))
+@pytest.mark.parametrize("workers", [4, 8])
+def test_entries_by_round_parity_lose_counts(workers):
+    failures = sum(1 for seed in range(200) if run(2, 7, seed, workers))
     assert failures > 0
