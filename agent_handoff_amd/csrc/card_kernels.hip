@@ -416,25 +416,30 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     const uint32_t lane = lane_id();
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
-    if (p.info[2] != 0) return;
-    const uint64_t S = p.info[0];
     const uint64_t s = wave / p.nbk;
     const uint32_t b = (uint32_t)(wave % p.nbk);
     const uint32_t t0 = b * TPW;
     const uint32_t tok = t0 + lane / G;
     const uint32_t g = lane % G;
     const bool valid = tok < p.T;
+    const uint32_t tc = valid ? tok : t0;
     const uint32_t nv = (p.T - t0 < TPW) ? p.T - t0 : TPW;
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
+    // Everything the scan wrote that this wave needs, in one round of loads
+    // (none depends on another), before the status check: a short-lived
+    // wave pays each dependent round trip in full.
+    const uint64_t flags = p.info[2], S = p.info[0];
+    const uint64_t span0 = p.off[t0], span1 = p.off[t0 + nv], my_off = p.off[tc];
+    const uint32_t width = p.widths[tc];
+    if (flags != 0) return;
     // The wave's records are one contiguous span of the stream: load it with
     // 16-byte coalesced loads into LDS, then decode each group from there.
     __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
     uint4* st = stage[threadIdx.x / kWave];
     {
-        const uint64_t span0 = p.off[t0];
-        const uint32_t n16 = (uint32_t)((p.off[t0 + nv] - span0) / 16);
+        const uint32_t n16 = (uint32_t)((span1 - span0) / 16);
         const uint4* src = reinterpret_cast<const uint4*>(p.card_in + p.payload + s * S + span0);
         uint4 c[kSpanChunks / kWave];
 #pragma unroll
@@ -449,8 +454,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = 0;
     if (valid) {
-        const uint32_t width = p.widths[tok];
-        const uint8_t* rec = reinterpret_cast<const uint8_t*>(st) + (uint32_t)(p.off[tok] - p.off[t0]);
+        const uint8_t* rec = reinterpret_cast<const uint8_t*>(st) + (uint32_t)(my_off - span0);
         if (width == 16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
