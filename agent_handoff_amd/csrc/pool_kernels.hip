@@ -418,7 +418,9 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
 //   b. park round r's keys in LDS, fold their maxima into the workgroup's
 //      (LDS atomics) and count itself done;
 //   c. wait (in LDS) until the coordinator has the layer maxima of round
-//      r-2, then quantise the keys parked in round r-2.
+//      r-3, then quantise the keys parked in round r-3 (kQuantLag rounds of
+//      work between a workgroup's publication and its need of everyone's:
+//      a lag of 2 measured 3-4 us slower on the Llama 4K pool).
 // Coordinator wave, round r: when the key waves are done with r, publish
 // the workgroup's maxima of r as flag|max words (one per layer and
 // workgroup; one plain device-scope store each, no returning atomic), then
@@ -438,7 +440,8 @@ constexpr int kFusedSlots = 8;     // block slots per workgroup and round
 constexpr int kFusedKeyWaves = 4;    // key waves, kSlotsPerKeyWave slots each
 constexpr int kSlotsPerKeyWave = kFusedSlots / kFusedKeyWaves;
 constexpr int kFusedThreads = (kFusedSlots + kFusedKeyWaves + 1) * kWave;
-constexpr int kHoldRounds = 3;
+constexpr int kQuantLag = 3;                // rounds between parking keys and quantising them
+constexpr int kHoldRounds = kQuantLag + 1;  // LDS key buffers and handshake entries
 constexpr uint32_t kMaxRoundLayers = 32;
 constexpr uint32_t kMaxFusedGrid = 1024;  // workgroups; sizes the flag words of the workspace
 constexpr uint32_t kFlag = 0x80000000u;
@@ -455,11 +458,11 @@ __device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t L, uint3
 template <int D>
 struct FusedLds {
     static constexpr int kBpw = 128 / D;  // blocks per slot and round: 4 KiB of keys
-    uint4 hold[kHoldRounds][kFusedSlots][kBpw][D / 32][kWave];  // [round % 3][slot][block][chunk][lane]
+    uint4 hold[kHoldRounds][kFusedSlots][kBpw][D / 32][kWave];  // [round % 4][slot][block][chunk][lane]
     EncodeStage<D> stage[kFusedSlots];  // per slot: .v by its value wave, .k by its key wave
-    // By round % 3: a key wave reaches round r only after its wait in round
-    // r-1 saw the maxima of round r-3 ready, i.e. after the coordinator has
-    // consumed and cleared the round-(r-3) entries that round r reuses.
+    // By round % 4: a key wave reaches round r only after its wait in round
+    // r-1 saw the maxima of round r-4 ready, i.e. after the coordinator has
+    // consumed and cleared the round-(r-4) entries that round r reuses.
     uint32_t wg_max[kHoldRounds][kMaxRoundLayers];     // this workgroup's key maxima
     uint32_t layer_max[kHoldRounds][kMaxRoundLayers];  // every workgroup's, per layer
     uint32_t done[kHoldRounds];                        // key waves done with the round
@@ -597,7 +600,7 @@ __device__ __forceinline__ void fused_value_wave(const EncodeParams& p, FusedLds
 }
 
 // Key wave kw, iteration r: round r+1's key loads go out first, then
-// round r's keys are parked and their maxima folded in, then round r-2's
+// round r's keys are parked and their maxima folded in, then round r-3's
 // keys are quantised: a round of work separates the wave's count for a
 // round from its wait for that round's maxima.
 template <int D>
@@ -639,8 +642,8 @@ __device__ __forceinline__ void key_round(const EncodeParams& p, FusedLds<D>& sm
         // before the count
         if (lane == 0) __hip_atomic_fetch_add(&sm.done[r % kHoldRounds], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    if (r >= 2) {
-        const uint32_t rq = r - 2;
+    if (r >= (uint32_t)kQuantLag) {
+        const uint32_t rq = r - kQuantLag;
         const uint64_t start = wall_clock64();
         while (lds_load(&sm.ready) < rq + 1) {
             if (wall_clock64() - start > kWaitTicks) {
@@ -686,9 +689,9 @@ __device__ __forceinline__ void fused_key_wave(const EncodeParams& p, FusedLds<D
                                         lane)
                              .elem,
                          a.k[i][j]);
-    for (uint32_t r = 0; r < nrounds + 2; r += 2) {
+    for (uint32_t r = 0; r < nrounds + kQuantLag; r += 2) {
         key_round<D>(p, sm, kw, lane, r, nrounds, a, b);
-        if (r + 1 < nrounds + 2) key_round<D>(p, sm, kw, lane, r + 1, nrounds, b, a);
+        if (r + 1 < nrounds + kQuantLag) key_round<D>(p, sm, kw, lane, r + 1, nrounds, b, a);
     }
 }
 
@@ -710,7 +713,7 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
             }
             uint32_t m = 0;
             if (lane < q.nl) m = lds_load(&sm.wg_max[r % kHoldRounds][lane]);
-            if (lane < kMaxRoundLayers) sm.wg_max[r % kHoldRounds][lane] = 0;  // reused in round r + 3
+            if (lane < kMaxRoundLayers) sm.wg_max[r % kHoldRounds][lane] = 0;  // reused in round r + 4
             if (lane == 0) sm.done[r % kHoldRounds] = 0;
             if (lane < q.nl)
                 __hip_atomic_store(round_flags(p.ws, p.L, q.l0 + lane) + blockIdx.x, kFlag | m, __ATOMIC_RELAXED,

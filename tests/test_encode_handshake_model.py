@@ -5,22 +5,22 @@ The kernel's key waves (the "workers" below) and its coordinator wave
 exchange, through LDS, each round's key maxima (wg_max), a count of key
 waves done with the round (done) and the number of rounds whose layer
 maxima are ready (ready). The key waves park round r, then quantise round
-r-2 once ready > r-2; the coordinator waits until every key wave is done
-with round r, takes and clears
+r-lag once ready > r-lag (the kernel's lag is 3); the coordinator waits
+until every key wave is done with round r, takes and clears
 its entries, publishes, and marks round r-1 ready. This model runs those
 steps under random interleavings and checks that no count or maximum is
 lost and every round is quantised with its own maxima. With the entries
-indexed by round % 3 (as in the kernel) every schedule passes; indexed by
-round % 2, a worker can reach round r+2 before the coordinator has cleared
-round r, and the count it adds is lost (the kernel's bounded wait would
-then give up and mark the pool invalid)."""
+indexed by round % (lag + 1) (as in the kernel: % 4) every schedule
+passes; indexed by round % lag, a worker can reach round r+lag before the
+coordinator has cleared round r, and the count it adds is lost (the
+kernel's bounded wait would then give up and mark the pool invalid)."""
 
 import random
 
 import pytest
 
 
-def run(buffers, rounds, seed, workers=8):
+def run(buffers, rounds, seed, workers=8, lag=2):
     rng = random.Random(seed)
     done = [0] * buffers
     wg_max = [[] for _ in range(buffers)]
@@ -28,11 +28,11 @@ def run(buffers, rounds, seed, workers=8):
     ready = 0
 
     def worker():
-        for r in range(rounds + 2):
+        for r in range(rounds + lag):
             if r < rounds:
                 yield ("encode", r)
-            if r >= 2:
-                yield ("quantise", r - 2)
+            if r >= lag:
+                yield ("quantise", r - lag)
 
     def coordinator():
         for k in range(rounds + 1):
@@ -78,14 +78,18 @@ def run(buffers, rounds, seed, workers=8):
 
 
 @pytest.mark.parametrize("workers", [4, 8])
-def test_entries_by_round_mod_3_survive_every_schedule(workers):
-    """4: the kernel's key waves; 8: one wave per slot (the protocol does
-    not depend on the count)."""
+@pytest.mark.parametrize("lag", [2, 3])
+def test_entries_by_round_mod_lag_plus_1_survive_every_schedule(workers, lag):
+    """Entries indexed by round % (lag + 1): the kernel quantises round r-3
+    with 4 buffers and 4 key waves (lag 2 with 3 buffers is the earlier
+    build's, kept as a case); 8 workers: the count does not matter."""
     for seed in range(400):
-        assert run(3, 7, seed, workers) == [], seed
+        assert run(lag + 1, 9, seed, workers, lag) == [], seed
 
 
 @pytest.mark.parametrize("workers", [4, 8])
-def test_entries_by_round_parity_lose_counts(workers):
-    failures = sum(1 for seed in range(200) if run(2, 7, seed, workers))
+@pytest.mark.parametrize("lag", [2, 3])
+def test_entries_by_round_mod_lag_lose_counts(workers, lag):
+    """One buffer fewer than lag + 1 and some schedule loses a count."""
+    failures = sum(1 for seed in range(200) if run(lag, 9, seed, workers, lag))
     assert failures > 0
