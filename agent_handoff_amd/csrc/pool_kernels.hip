@@ -60,9 +60,11 @@ struct EncodeParams {
 };
 
 // Encode workspace (u32 words): [2] the single-pass encode's timeout flag,
-// up to 64 reserved words; then per layer kSlots partial key maxima of the
-// two-pass encode, each on its own 128-byte line so that concurrent atomics
-// spread over addresses; then the single-pass encode's flag words.
+// up to 64 reserved words; then one region that a call uses in one of two
+// ways: the two-pass encode's kSlots partial key maxima per layer, each on
+// its own 128-byte line so that concurrent atomics spread over addresses,
+// or the single-pass encode's flag words, one per (layer, workgroup). Each
+// call zeroes the head and the part of the region its path uses.
 constexpr uint32_t kSlots = 16;
 constexpr uint32_t kSlotStride = 32;  // words
 constexpr uint32_t kWsHead = 64;      // words
@@ -157,9 +159,10 @@ __device__ void pool_header_and_padding(const EncodeParams& p, uint32_t d, uint3
 
 // ---------------------------------------------------------------- kernels
 
-__global__ void fill_zero_kernel(uint32_t* p, uint32_t n) {
+// Zeroes n4 16-byte chunks (the encode workspace is 16-byte aligned).
+__global__ void fill_zero_kernel(uint4* p, uint32_t n4) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+    if (i < n4) p[i] = make_uint4(0, 0, 0, 0);
 }
 
 // Per-layer max |K| (PolyKV 2.B item 1: one linear scale per tensor). For
@@ -451,8 +454,9 @@ constexpr uint32_t kFlag = 0x80000000u;
 // waves, so the limit is a guard against a hang, never expected to trip.
 constexpr uint64_t kWaitTicks = 50000000ull;
 
-__device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t L, uint32_t l) {
-    return ws + kWsHead + L * kSlots * kSlotStride + l * kMaxFusedGrid;
+// Flag words of layer l, one per workgroup of a G-workgroup grid.
+__device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t G, uint32_t l) {
+    return ws + kWsHead + (uint64_t)l * G;
 }
 
 template <int D>
@@ -716,7 +720,7 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
             if (lane < kMaxRoundLayers) sm.wg_max[r % kHoldRounds][lane] = 0;  // reused in round r + 4
             if (lane == 0) sm.done[r % kHoldRounds] = 0;
             if (lane < q.nl)
-                __hip_atomic_store(round_flags(p.ws, p.L, q.l0 + lane) + blockIdx.x, kFlag | m, __ATOMIC_RELAXED,
+                __hip_atomic_store(round_flags(p.ws, gridDim.x, q.l0 + lane) + blockIdx.x, kFlag | m, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         if (r >= 1) {
@@ -724,7 +728,7 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
             const uint32_t rq = r - 1;
             const Round q = round_of(p, rq);
             for (uint32_t lr = 0; lr < q.nl; ++lr) {
-                const uint32_t* f = round_flags(p.ws, p.L, q.l0 + lr);
+                const uint32_t* f = round_flags(p.ws, gridDim.x, q.l0 + lr);
                 // all of the layer's words at once (lane + 64 i), then again
                 // for those not yet flagged
                 constexpr int kPer = kMaxFusedGrid / kWave;
@@ -1033,9 +1037,14 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.poll_ticks = encode_poll_ticks();
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
-    const uint32_t ws_words = (uint32_t)encode_workspace_words(s.L);
-    hipError_t e = launch_kernel(fill_zero_kernel, dim3((ws_words + 255) / 256), dim3(256), stream, ws, ws_words);
-    if (e != hipSuccess) return e;
+    // Zero the workspace head and the part of its region the chosen path
+    // uses (a whole number of 16-byte chunks; encode_workspace_words covers
+    // the largest of them).
+    auto zero_words = [&](uint64_t words) {
+        const uint32_t n4 = (uint32_t)((words + 3) / 4);
+        return launch_kernel(fill_zero_kernel, dim3((n4 + 255) / 256), dim3(256), stream, reinterpret_cast<uint4*>(ws),
+                             n4);
+    };
 
     // Single pass when a round of whole layers fits the LDS of a grid of one
     // workgroup per CU; otherwise two passes (the per-layer key maxima, then
@@ -1055,11 +1064,15 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
         if (lpr > s.L) lpr = s.L;
         if (lpr >= 1) {
             p.layers_per_round = (uint32_t)lpr;
+            const hipError_t ez = zero_words(kWsHead + (uint64_t)s.L * grid);
+            if (ez != hipSuccess) return ez;
             void* argv[] = {&p};
             return report_launch(hipLaunchKernel(fused, dim3((uint32_t)grid), dim3(kFusedThreads), argv, 0, stream),
                                  "pool_encode_fused_kernel");
         }
     }
+    hipError_t e = zero_words(kWsHead + (uint64_t)s.L * kSlots * kSlotStride);
+    if (e != hipSuccess) return e;
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
     uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
     if (gx > 64) gx = 64;
