@@ -114,6 +114,15 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape);
  * Keys: m_l = max |K[l]| over the layer; codes clamp(rint(x*(127/m_l))).
  * Values: per vector, s = fp16(sqrt(sum x^2 / d)), y = H x (Sylvester
  * order), z = y / (sqrt(d) s), code = number of Lloyd-Max thresholds <= z.
+ * Execution: where a round of whole layers fits the LDS of one workgroup per
+ * CU, one kernel reads K once (keys wait in LDS for their layer's maximum);
+ * otherwise a key-maximum pass runs first. The single pass is an ordinary
+ * launch: a workgroup that has not received every other workgroup's key
+ * maximum for a layer within a bound (200 us by default; environment
+ * variable KVC_ENCODE_POLL_US, read at each call, 0 = always) reads the
+ * layer's keys itself. The pool is the same either way; only the time
+ * differs. A pool whose encode hit an internal wait limit (never expected)
+ * has a zero magic word and is refused by decode.
  * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
  * KVC_E_HIP. */
 int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool,
