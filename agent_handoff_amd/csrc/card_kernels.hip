@@ -27,6 +27,32 @@ namespace kvc {
 namespace {
 
 constexpr uint32_t kFlagBadHeader = 1, kFlagBadWidth = 2, kFlagCapacity = 4;
+
+// Workgroups are dealt to the 8 XCDs in turn, so consecutive token blocks
+// of a stream would land on different XCDs (their L2s each fetching the
+// cache lines that neighbouring spans share, their writes scattered). The
+// pack and unpack grids are instead read in an order that gives each XCD
+// runs of C consecutive logical workgroups: XCD x's r-th workgroup is
+// logical workgroup ((r / C) * 8 + x) * C + r % C, a bijection onto
+// [0, gridDim) for a grid padded to a multiple of 8 C (workgroups past the
+// work exit). Measured on the Llama 4K card with the configs' width mix:
+// unpack 151 -> 132 us with C = 64 (one stream of 4096 tokens per run; 16:
+// 134, 128: 136), pack 144 -> 135 us with C = 16.
+constexpr uint32_t kXcdCount = 8;
+constexpr uint32_t kUnpackXcdRun = 64;
+constexpr uint32_t kPackXcdRun = 16;
+
+template <uint32_t C>
+__device__ __forceinline__ uint64_t xcd_run_block(uint32_t b) {
+    const uint32_t r = b / kXcdCount;
+    return ((uint64_t)(r / C) * kXcdCount + b % kXcdCount) * C + r % C;
+}
+
+template <uint32_t C>
+inline uint32_t xcd_run_grid(uint64_t workgroups) {
+    const uint64_t pad = (uint64_t)kXcdCount * C;
+    return (uint32_t)((workgroups + pad - 1) / pad * pad);
+}
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 8;
 
@@ -286,7 +312,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
     constexpr uint32_t TPW = kWave / G;     // tokens per wave
     static_assert(TPW * 2 * D <= 16 * kSpanChunks, "span exceeds the stage");
     const uint32_t lane = lane_id();
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    const uint64_t wave = xcd_run_block<kPackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
     const uint64_t s = wave / p.nbk;
     const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     constexpr uint32_t G = D / kCardGroup;
     constexpr uint32_t TPW = kWave / G;  // the wave's tokens: 4 KiB of bf16 output
     const uint32_t lane = lane_id();
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    const uint64_t wave = xcd_run_block<kUnpackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
     const uint64_t s = wave / p.nbk;
     const uint32_t b = (uint32_t)(wave % p.nbk);
@@ -631,7 +657,7 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
     p.v = static_cast<const uint16_t*>(v);
     p.widths = widths;
     p.card = static_cast<uint8_t*>(card);
-    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    const uint32_t nblocks = xcd_run_grid<kPackXcdRun>((p.n_waves + 3) / 4);
     return launch_kernel(s.d == 64 ? card_pack_kernel<64> : card_pack_kernel<128>, dim3(nblocks),
                          dim3(kBlockThreads), stream, p);
 }
@@ -658,7 +684,7 @@ hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_by
     p.v_out = static_cast<uint16_t*>(v_out);
     p.widths = sp.widths;
     p.card_in = static_cast<const uint8_t*>(card);
-    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    const uint32_t nblocks = xcd_run_grid<kUnpackXcdRun>((p.n_waves + 3) / 4);
     return launch_kernel(s.d == 64 ? card_unpack_kernel<64> : card_unpack_kernel<128>, dim3(nblocks),
                          dim3(kBlockThreads), stream, p);
 }
