@@ -37,10 +37,12 @@ constexpr uint32_t kFlagBadHeader = 1, kFlagBadWidth = 2, kFlagCapacity = 4;
 // [0, gridDim) for a grid padded to a multiple of 8 C (workgroups past the
 // work exit). Measured on the Llama 4K card with the configs' width mix:
 // unpack 151 -> 132 us with C = 64 (one stream of 4096 tokens per run; 16:
-// 134, 128: 136), pack 144 -> 135 us with C = 16.
+// 134, 128: 136), pack 144 -> 135 us with C = 16, transcode 130 -> 126 us
+// with C = 64.
 constexpr uint32_t kXcdCount = 8;
 constexpr uint32_t kUnpackXcdRun = 64;
 constexpr uint32_t kPackXcdRun = 16;
+constexpr uint32_t kTranscodeXcdRun = 64;
 
 template <uint32_t C>
 __device__ __forceinline__ uint64_t xcd_run_block(uint32_t b) {
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
     constexpr uint32_t G = D / kCardGroup;  // lanes per token
     constexpr uint32_t TPW = kWave / G;     // tokens per wave
     const uint32_t lane = lane_id();
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    const uint64_t wave = xcd_run_block<kTranscodeXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
     const uint64_t s = wave / p.nbk;
     const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
@@ -741,7 +743,7 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
     p.nbk = cp.nbk;
     p.payload = cp.payload;
     p.n_waves = cp.n_waves;
-    const uint32_t nblocks = (uint32_t)((p.n_waves + 3) / 4);
+    const uint32_t nblocks = xcd_run_grid<kTranscodeXcdRun>((p.n_waves + 3) / 4);
     return launch_kernel(s.d == 64 ? card_transcode_kernel<64> : card_transcode_kernel<128>, dim3(nblocks),
                          dim3(kBlockThreads), stream, p);
 }
