@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--agents", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-configs", action="store_true",
+                    help="instead of the step: one JSON line per op for the tiny, SmolLM2 2K, 8K card and 32K "
+                         "workloads (reported, not the benchmark line)")
     ap.add_argument("--cpu-layers", type=int, default=32, help="layers of the workload in the CPU oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per dispatch (from rocprofv3 counters)")
@@ -69,6 +72,9 @@ def main():
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this codec is measured on "
               "one GPU's share; the multi-GPU handoff is a design note, not a benchmark)", file=sys.stderr)
         sys.exit(2)
+    if args.other_configs:
+        other_configs(args)
+        return
 
     import numpy as np
     import torch
@@ -354,6 +360,91 @@ def _counter_rows(folder, counter):
                 rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
     rows.sort()
     return [(n, v) for _, n, v in rows]
+
+
+def other_configs(args):
+    """Encode / decode (or pack / unpack) of the workloads other than the
+    headline one, each timed alone (median of HIP events over repeated calls
+    on one stream, inputs resident): the tiny pool, the SmolLM2-1.7B 2K pool
+    (decode into one agent), the Llama-3-8B 32K pool (encode of the whole
+    pool in one call, then the decode streamed one layer per call, the 32
+    calls timed as one sequence) and the Llama-3.1-8B 8K card."""
+    import torch
+
+    from agent_handoff_amd import kvcodec as kv
+    from agent_handoff_amd import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return t[len(t) // 2]
+
+    def emit(w, op, t, nbytes, **extra):
+        gbs = nbytes / t / 1e9
+        print(json.dumps({"workload": w.name, "op": op, "us": round(t * 1e6, 2), "bytes": int(nbytes),
+                          "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), **extra}), flush=True)
+
+    for cfg in (1, 2, 5):
+        w = synth.WORKLOADS[cfg]
+        L, H, T, d = shape = w.shape
+        log(f"generating {w.name} inputs on the GPU")
+        k, v = synth.kv_tensors_torch(w, args.seed, dev)
+        kv_bytes = L * H * T * d * 2
+        pool_b = pool_payload_bytes(*shape)
+        pool = torch.empty(kv.kvpool_bytes(shape), dtype=torch.uint8, device=dev)
+        ws = torch.empty(kv.kvpool_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        reps = 20 if cfg != 5 else 8
+        te = timed(lambda: kv.kvpool_encode(shape, k, v, pool, ws, stream=stream), reps)
+        emit(w, "encode", te, 2 * kv_bytes + pool_b,
+             path="single pass" if cfg != 5 else "two passes (a layer exceeds one round)")
+        if cfg == 5:
+            ko = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
+            vo = torch.empty_like(ko)
+
+            def dec():
+                for l in range(L):
+                    kv.kvpool_decode(shape, pool, l, l + 1, [ko], [vo], status, stream=stream)
+            td = timed(dec, reps)
+            emit(w, "decode, one layer per call (32 calls)", td, pool_b + 2 * kv_bytes)
+            del ko, vo
+        else:
+            ko, vo = torch.empty_like(k), torch.empty_like(v)
+            td = timed(lambda: kv.kvpool_decode(shape, pool, 0, L, [ko], [vo], status, stream=stream), reps)
+            emit(w, "decode, one agent", td, pool_b + 2 * kv_bytes)
+            del ko, vo
+        del k, v, pool, ws
+        torch.cuda.empty_cache()
+
+    w = synth.WORKLOADS[4]
+    L, H, T, d = shape = w.shape
+    log(f"generating {w.name} inputs on the GPU")
+    k, v = synth.kv_tensors_torch(w, args.seed, dev)
+    kv_bytes = L * H * T * d * 2
+    widths_np = synth.card_widths(w, args.seed, T=T)
+    widths = torch.from_numpy(widths_np).to(dev)
+    card_n = kv.cachecard_bytes_host(shape, widths_np)
+    card = torch.empty(card_n, dtype=torch.uint8, device=dev)
+    cws = torch.empty(kv.cachecard_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+    tp = timed(lambda: kv.cachecard_pack(shape, k, v, widths, card, cws, b"llama-3.1-8b", 0, None, status,
+                                         stream=stream), 20)
+    emit(w, "card pack", tp, 2 * kv_bytes + card_n, card_bytes=card_n)
+    tu = timed(lambda: kv.cachecard_unpack(shape, card, ko, vo, cws, card_n, status, stream=stream), 20)
+    emit(w, "card unpack", tu, card_n + 2 * kv_bytes, card_bytes=card_n)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set"
 
 
 def traffic_from_counters(fetch_dir, write_dir, out_path, agents):
