@@ -545,16 +545,48 @@ __device__ __forceinline__ void note_timeout(const EncodeParams& p) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-// Block j of slot gw in round r (clamped: a block past the round's end, or
-// a round past the last, is block 0 of layer 0, loaded and never used).
+// Block bi of every round: its layer within the round, its block within the
+// layer, head and first token. The same in every round (only the layer,
+// l0 + lr, moves), so a wave works it out once, not at every use.
+struct SlotBlock {
+    uint32_t lr, bidx, h, t0;
+};
+
+__device__ __forceinline__ SlotBlock slot_block(const EncodeParams& p, uint32_t bi) {
+    SlotBlock g;
+    g.lr = bi / p.blocks_per_layer;
+    g.bidx = bi % p.blocks_per_layer;
+    g.h = g.bidx / p.nb;
+    g.t0 = (g.bidx % p.nb) * kBlockTokens;
+    return g;
+}
+
+// block_pos for a block whose head and first token are known
 template <int D>
-__device__ __forceinline__ BlockPos fused_block(const EncodeParams& p, uint32_t r, uint32_t nrounds, uint32_t gw,
-                                                uint32_t j, uint32_t NW, uint32_t lane) {
+__device__ __forceinline__ BlockPos block_pos_at(const EncodeParams& p, uint32_t l, const SlotBlock& g, uint32_t lane) {
+    BlockPos b;
+    b.l = l;
+    b.bidx = g.bidx;
+    b.m = lane & 3u;
+    b.nv = (p.T - g.t0 < kBlockTokens) ? p.T - g.t0 : kBlockTokens;
+    b.vec0 = ((uint64_t)l * p.H + g.h) * p.T + g.t0;
+    b.vec = b.vec0 + (lane >> 2);
+    b.valid = g.t0 + (lane >> 2) < p.T;
+    b.elem = (b.valid ? b.vec : b.vec0) * D + (uint64_t)b.m * (D / 4);
+    return b;
+}
+
+// Block g in round r (clamped: a block past the round's end, or a round past
+// the last, is block 0 of layer 0, loaded and never used). Block bi is in
+// round r's range exactly when its layer lr is below the round's layers.
+template <int D>
+__device__ __forceinline__ BlockPos fused_block(const EncodeParams& p, uint32_t r, uint32_t nrounds, const SlotBlock& g,
+                                                uint32_t lane) {
     const bool live_round = r < nrounds;
     const Round q = round_of(p, live_round ? r : 0);
-    const uint32_t bi = gw + j * NW;
-    const bool live = live_round && bi < q.nblk;
-    return block_pos<D>(p, live ? q.l0 + bi / p.blocks_per_layer : 0u, live ? bi % p.blocks_per_layer : 0u, lane);
+    const bool live = live_round && g.lr < q.nl;
+    const SlotBlock z = {0u, 0u, 0u, 0u};
+    return block_pos_at<D>(p, live ? q.l0 + g.lr : 0u, live ? g : z, lane);
 }
 
 // Logical workgroup of the single-pass encode's block mapping. Workgroups
@@ -580,18 +612,16 @@ struct KeyRaw {
 // flight; no wait on any other wave.
 template <int D>
 __device__ __forceinline__ void value_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t vw, uint32_t lane,
-                                            uint32_t r, uint32_t nrounds, ValueRaw<D>& cur, ValueRaw<D>& fill) {
-    const uint32_t NW = gridDim.x * kFusedSlots;
-    const uint32_t gw = fused_wg() * kFusedSlots + vw;
+                                            uint32_t r, uint32_t nrounds, const SlotBlock (&g)[FusedLds<D>::kBpw],
+                                            ValueRaw<D>& cur, ValueRaw<D>& fill) {
 #pragma unroll
     for (int j = 0; j < FusedLds<D>::kBpw; ++j)
-        load_lane<D>(p.v, fused_block<D>(p, r + 1, nrounds, gw, j, NW, lane).elem, fill.v[j]);
+        load_lane<D>(p.v, fused_block<D>(p, r + 1, nrounds, g[j], lane).elem, fill.v[j]);
     const Round q = round_of(p, r);
 #pragma unroll
     for (int j = 0; j < FusedLds<D>::kBpw; ++j) {
-        const uint32_t bi = gw + (uint32_t)j * NW;
-        if (bi < q.nblk) {
-            const BlockPos b = block_pos<D>(p, q.l0 + bi / p.blocks_per_layer, bi % p.blocks_per_layer, lane);
+        if (g[j].lr < q.nl) {
+            const BlockPos b = block_pos_at<D>(p, q.l0 + g[j].lr, g[j], lane);
             encode_values<D>(p, b, cur.v[j], sm.stage[vw], lane);
         }
     }
@@ -602,13 +632,16 @@ __device__ __forceinline__ void fused_value_wave(const EncodeParams& p, FusedLds
                                                  uint32_t nrounds) {
     const uint32_t NW = gridDim.x * kFusedSlots;
     const uint32_t gw = fused_wg() * kFusedSlots + vw;
+    SlotBlock g[FusedLds<D>::kBpw];
+#pragma unroll
+    for (int j = 0; j < FusedLds<D>::kBpw; ++j) g[j] = slot_block(p, gw + (uint32_t)j * NW);
     ValueRaw<D> a, b;
 #pragma unroll
     for (int j = 0; j < FusedLds<D>::kBpw; ++j)
-        load_lane<D>(p.v, fused_block<D>(p, 0, nrounds, gw, j, NW, lane).elem, a.v[j]);
+        load_lane<D>(p.v, fused_block<D>(p, 0, nrounds, g[j], lane).elem, a.v[j]);
     for (uint32_t r = 0; r < nrounds; r += 2) {
-        value_round<D>(p, sm, vw, lane, r, nrounds, a, b);
-        if (r + 1 < nrounds) value_round<D>(p, sm, vw, lane, r + 1, nrounds, b, a);
+        value_round<D>(p, sm, vw, lane, r, nrounds, g, a, b);
+        if (r + 1 < nrounds) value_round<D>(p, sm, vw, lane, r + 1, nrounds, g, b, a);
     }
 }
 
@@ -618,30 +651,24 @@ __device__ __forceinline__ void fused_value_wave(const EncodeParams& p, FusedLds
 // round from its wait for that round's maxima.
 template <int D>
 __device__ __forceinline__ void key_round(const EncodeParams& p, FusedLds<D>& sm, uint32_t kw, uint32_t lane,
-                                          uint32_t r, uint32_t nrounds, KeyRaw<D>& cur, KeyRaw<D>& fill) {
+                                          uint32_t r, uint32_t nrounds,
+                                          const SlotBlock (&g)[kSlotsPerKeyWave][FusedLds<D>::kBpw], KeyRaw<D>& cur,
+                                          KeyRaw<D>& fill) {
     constexpr int BPW = FusedLds<D>::kBpw;
-    const uint32_t NW = gridDim.x * kFusedSlots;
 #pragma unroll
     for (int i = 0; i < kSlotsPerKeyWave; ++i)
 #pragma unroll
-        for (int j = 0; j < BPW; ++j)
-            load_lane<D>(p.k,
-                         fused_block<D>(p, r + 1, nrounds, fused_wg() * kFusedSlots + kw * kSlotsPerKeyWave + i, j,
-                                        NW, lane)
-                             .elem,
-                         fill.k[i][j]);
+        for (int j = 0; j < BPW; ++j) load_lane<D>(p.k, fused_block<D>(p, r + 1, nrounds, g[i][j], lane).elem, fill.k[i][j]);
     if (r < nrounds) {
         const Round q = round_of(p, r);
 #pragma unroll
         for (int i = 0; i < kSlotsPerKeyWave; ++i) {
             const uint32_t slot = kw * kSlotsPerKeyWave + i;
-            const uint32_t gw = fused_wg() * kFusedSlots + slot;
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
-                const uint32_t bi = gw + (uint32_t)j * NW;
-                if (bi < q.nblk) {
-                    const uint32_t lr = bi / p.blocks_per_layer;
-                    const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                if (g[i][j].lr < q.nl) {
+                    const uint32_t lr = g[i][j].lr;
+                    const BlockPos b = block_pos_at<D>(p, q.l0 + lr, g[i][j], lane);
                     const uint32_t m = wave_max_u32(b.valid ? lane_absmax_bits<D / 32>(cur.k[i][j]) : 0u);
 #pragma unroll
                     for (int c = 0; c < D / 32; ++c) sm.hold[r % kHoldRounds][slot][j][c][lane] = cur.k[i][j][c];
@@ -669,13 +696,11 @@ __device__ __forceinline__ void key_round(const EncodeParams& p, FusedLds<D>& sm
 #pragma unroll
         for (int i = 0; i < kSlotsPerKeyWave; ++i) {
             const uint32_t slot = kw * kSlotsPerKeyWave + i;
-            const uint32_t gw = fused_wg() * kFusedSlots + slot;
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
-                const uint32_t bi = gw + (uint32_t)j * NW;
-                if (bi < q.nblk) {
-                    const uint32_t lr = bi / p.blocks_per_layer;
-                    const BlockPos b = block_pos<D>(p, q.l0 + lr, bi % p.blocks_per_layer, lane);
+                if (g[i][j].lr < q.nl) {
+                    const uint32_t lr = g[i][j].lr;
+                    const BlockPos b = block_pos_at<D>(p, q.l0 + lr, g[i][j], lane);
                     uint4 kr[D / 32];
 #pragma unroll
                     for (int c = 0; c < D / 32; ++c) kr[c] = sm.hold[rq % kHoldRounds][slot][j][c][lane];
@@ -691,20 +716,21 @@ __device__ __forceinline__ void fused_key_wave(const EncodeParams& p, FusedLds<D
                                                uint32_t nrounds) {
     // two register sets, alternating, one round of loads in flight (the loop
     // is unrolled by two so that both stay in registers)
-    KeyRaw<D> a, b;
     const uint32_t NW = gridDim.x * kFusedSlots;
+    SlotBlock g[kSlotsPerKeyWave][FusedLds<D>::kBpw];
 #pragma unroll
     for (int i = 0; i < kSlotsPerKeyWave; ++i)
 #pragma unroll
         for (int j = 0; j < FusedLds<D>::kBpw; ++j)
-            load_lane<D>(p.k,
-                         fused_block<D>(p, 0, nrounds, fused_wg() * kFusedSlots + kw * kSlotsPerKeyWave + i, j, NW,
-                                        lane)
-                             .elem,
-                         a.k[i][j]);
+            g[i][j] = slot_block(p, fused_wg() * kFusedSlots + kw * kSlotsPerKeyWave + i + (uint32_t)j * NW);
+    KeyRaw<D> a, b;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerKeyWave; ++i)
+#pragma unroll
+        for (int j = 0; j < FusedLds<D>::kBpw; ++j) load_lane<D>(p.k, fused_block<D>(p, 0, nrounds, g[i][j], lane).elem, a.k[i][j]);
     for (uint32_t r = 0; r < nrounds + kQuantLag; r += 2) {
-        key_round<D>(p, sm, kw, lane, r, nrounds, a, b);
-        if (r + 1 < nrounds + kQuantLag) key_round<D>(p, sm, kw, lane, r + 1, nrounds, b, a);
+        key_round<D>(p, sm, kw, lane, r, nrounds, g, a, b);
+        if (r + 1 < nrounds + kQuantLag) key_round<D>(p, sm, kw, lane, r + 1, nrounds, g, b, a);
     }
 }
 
