@@ -95,7 +95,24 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid % kWave, w = tid / kWave;
     if (tid == 0) bad = 0;
+    // The input card's header words (unpack and transcode), loaded before the
+    // scan so that their trip to memory overlaps the widths' rather than
+    // following it.
+    uint32_t hw[7] = {};
+    uint64_t hq[4] = {};
+    if (!p.card_out && tid == 0) {
+        const uint32_t* h = reinterpret_cast<const uint32_t*>(p.card_in);
+        const uint64_t* h64 = reinterpret_cast<const uint64_t*>(p.card_in);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) hw[i] = h[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hq[i] = h64[5 + i];
+    }
     __syncthreads();
+    // With at most one chunk of tokens (the common case) each thread keeps
+    // its widths, which the pack then copies into the card from registers.
+    const bool one_chunk = p.T <= (uint64_t)kScanThreads * kScanItems;
+    uint8_t wv[kScanItems] = {};
     // Chunks of kScanThreads * kScanItems tokens: each thread sums its
     // tokens' record sizes, the wave scans the sums with lane shifts, and the
     // waves' totals go through LDS (two barriers per chunk). A chunk's bytes
@@ -108,8 +125,10 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) {
             uint32_t r = 0;
+            wv[i] = 0;
             if (t0 + i < p.T) {
-                r = card_record_bytes(p.d, p.widths[t0 + i]);
+                wv[i] = p.widths[t0 + i];
+                r = card_record_bytes(p.d, wv[i]);
                 if (r == 0) bad = 1;
             }
             rs[i] = r;
@@ -149,11 +168,9 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
             if (total > p.limit) flags |= kFlagCapacity;
             if (p.dev_card_bytes) *p.dev_card_bytes = total;
         } else {
-            const uint32_t* h = reinterpret_cast<const uint32_t*>(p.card_in);
-            const uint64_t* h64 = reinterpret_cast<const uint64_t*>(p.card_in);
-            const bool ok = h[0] == kCardMagic && h[1] == (1u | (2u << 16)) && h[2] == p.L && h[3] == p.H &&
-                            h[4] == p.T && h[5] == p.d && h[6] == kCardGroup && h64[5] == kCardHeaderBytes &&
-                            h64[6] == payload && h64[7] == S && h64[8] == total && total <= p.limit;
+            const bool ok = hw[0] == kCardMagic && hw[1] == (1u | (2u << 16)) && hw[2] == p.L && hw[3] == p.H &&
+                            hw[4] == p.T && hw[5] == p.d && hw[6] == kCardGroup && hq[0] == kCardHeaderBytes &&
+                            hq[1] == payload && hq[2] == S && hq[3] == total && total <= p.limit;
             if (!ok) flags |= kFlagBadHeader;
         }
         p.info[0] = S;
@@ -199,8 +216,17 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
         }
         hdr[tid] = val;
     }
-    for (uint64_t i = tid; i < payload - kCardHeaderBytes; i += kScanThreads)
-        p.card_out[kCardHeaderBytes + i] = i < p.T ? p.widths[i] : 0;
+    if (one_chunk) {
+        const uint64_t t0 = (uint64_t)tid * kScanItems;
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i)
+            if (t0 + i < p.T) p.card_out[kCardHeaderBytes + t0 + i] = wv[i];
+        for (uint64_t i = p.T + tid; i < payload - kCardHeaderBytes; i += kScanThreads)
+            p.card_out[kCardHeaderBytes + i] = 0;
+    } else {
+        for (uint64_t i = tid; i < payload - kCardHeaderBytes; i += kScanThreads)
+            p.card_out[kCardHeaderBytes + i] = i < p.T ? p.widths[i] : 0;
+    }
 }
 
 // One 32-channel group at a per-lane width b (2, 4 or 8): the codes as

@@ -147,4 +147,16 @@ __device__ __forceinline__ void st_stream(uint4* p, const uint4& x) {
 }
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t x) { __builtin_nontemporal_store(x, p); }
 
+// q = x / d and r = x % d for a wave-uniform x: 32-bit arithmetic when x
+// fits (the case in practice), 64-bit otherwise.
+__device__ __forceinline__ void divmod_u64(uint64_t x, uint32_t d, uint64_t& q, uint32_t& r) {
+    if (x <= 0xFFFFFFFFull) {
+        q = (uint32_t)x / d;
+        r = (uint32_t)x % d;
+    } else {
+        q = x / d;
+        r = (uint32_t)(x % d);
+    }
+}
+
 }  // namespace kvc

@@ -871,10 +871,12 @@ __global__ __launch_bounds__(kBlockThreads) void pool_decode_kernel(DecodeParams
     const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
 
-    const uint32_t blk = (uint32_t)(wave % p.nb);
-    const uint64_t lh_rel = wave / p.nb;
+    uint64_t lh_rel, lq;
+    uint32_t blk, hr;
+    divmod_u64(wave, p.nb, lh_rel, blk);
     const uint64_t lh = (uint64_t)p.l0 * p.H + lh_rel;
-    const uint32_t l = (uint32_t)(lh / p.H);
+    divmod_u64(lh, p.H, lq, hr);
+    const uint32_t l = (uint32_t)lq;
     const uint32_t t0 = blk * kBlockTokens;
     const uint32_t m = lane & 3u;
     // lanes past the head's last token read the block's first vector (their
