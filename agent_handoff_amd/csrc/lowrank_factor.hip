@@ -32,6 +32,11 @@ constexpr int kFR = 32;              // rank
 constexpr int kFChunk = 256;         // tokens per partial product of Z^T Q
 constexpr int kFThreads = 256;
 constexpr int kFSweeps = 16;         // Jacobi sweep limit
+// The small eigenproblem's workgroup: a Jacobi step is a chain of two
+// barriers and 1728 independent updates (576 2 x 2 blocks of A, 1152 rows of
+// V), so more threads shorten every step of the chain; its 32 workgroups do
+// not fill the chip in any case.
+constexpr int kSvdThreads = 1024;
 
 // Y[m](t, :) = Z[m](t, :) X[m]; X is D x 48 row-major binary32, x_stride
 // elements apart per matrix (0: one X for all). Block: 64 tokens x 4 waves
@@ -204,9 +209,10 @@ __global__ __launch_bounds__(kFThreads) void fac_gram_partial_kernel(const float
 }
 
 // g = sum of the chunks' partial Gram matrices, chunks in order
+template <int NT>
 __device__ __forceinline__ void sum_gram(const double* gpart, uint32_t m, uint32_t nchunks, double* g) {
     const double* gp = gpart + (uint64_t)m * nchunks * kFK * kFK;
-    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) {
+    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += NT) {
         double s = 0.0;
         for (uint32_t c = 0; c < nchunks; ++c) s += gp[(uint64_t)c * kFK * kFK + i];
         g[i] = s;
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kFThreads) void fac_chol_kernel(const double* gpart
     __shared__ double g[kFK * kFK];
     __shared__ double L[kFK * kFK];
     const uint32_t m = blockIdx.x;
-    sum_gram(gpart, m, nchunks, g);
+    sum_gram<kFThreads>(gpart, m, nchunks, g);
     for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) L[i] = 0.0;
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -303,21 +309,21 @@ __global__ __launch_bounds__(kFThreads) void fac_apply_rinv_kernel(float* y, uin
 // below 1e-12 of the diagonal (in norm); writes ua = U_r diag(sigma),
 // ur = U_r diag(1/sigma) (0 where sigma = 0), both 48 x 32 binary32, and
 // sigma (descending).
-__global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const double* gpart, uint32_t nchunks, float* ua,
+__global__ __launch_bounds__(kSvdThreads) void fac_small_svd_kernel(const double* gpart, uint32_t nchunks, float* ua,
                                                                   float* ur, float* sigma) {
     __shared__ double a[kFK * kFK];
     __shared__ double v[kFK * kFK];
     __shared__ double rc[kFK / 2], rs[kFK / 2];
     __shared__ uint32_t rp[kFK / 2], rq[kFK / 2];
-    __shared__ double red[2][kFThreads / kWave];
+    __shared__ double red[2][kSvdThreads / kWave];
     __shared__ uint32_t order[kFK];
     const uint32_t m = blockIdx.x;
-    sum_gram(gpart, m, nchunks, a);
-    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) v[i] = (i / kFK == i % kFK) ? 1.0 : 0.0;
+    sum_gram<kSvdThreads>(gpart, m, nchunks, a);
+    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kSvdThreads) v[i] = (i / kFK == i % kFK) ? 1.0 : 0.0;
     __syncthreads();
     for (int sweep = 0; sweep < kFSweeps; ++sweep) {
         double off = 0.0, dia = 0.0;
-        for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) {
+        for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kSvdThreads) {
             const double x = a[i];
             if (i / kFK == i % kFK) dia += x * x;
             else off += x * x;
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const double* 
         }
         __syncthreads();
         double so = 0.0, sd = 0.0;
-        for (int k = 0; k < kFThreads / kWave; ++k) {
+        for (int k = 0; k < kSvdThreads / kWave; ++k) {
             so += red[0][k];
             sd += red[1][k];
         }
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const double* 
             // A <- J^T A J on 2 x 2 blocks (pair P rows, pair Q columns), and
             // V <- V J on rows j, pair Q
             constexpr uint32_t NP = kFK / 2;
-            for (uint32_t k = threadIdx.x; k < NP * NP + kFK * NP; k += kFThreads) {
+            for (uint32_t k = threadIdx.x; k < NP * NP + kFK * NP; k += kSvdThreads) {
                 if (k < NP * NP) {
                     const uint32_t P = k / NP, Q = k % NP;
                     const uint32_t p0 = rp[P], p1 = rq[P], q0 = rp[Q], q1 = rq[Q];
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(kFThreads) void fac_small_svd_kernel(const double* 
         order[rank] = i;
     }
     __syncthreads();
-    for (uint32_t k = threadIdx.x; k < (uint32_t)kFK * kFR; k += kFThreads) {
+    for (uint32_t k = threadIdx.x; k < (uint32_t)kFK * kFR; k += kSvdThreads) {
         const uint32_t j = k / kFR, col = k % kFR;
         const uint32_t e = order[col];
         const double lam = a[e * kFK + e];
@@ -546,7 +552,7 @@ hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d,
     {
         const uint32_t nc = gram(W, Dt);
         if (e == hipSuccess)
-            e = launch_kernel(fac_small_svd_kernel, dim3(M), blk, stream, (const double*)Gp, nc, UA, UR, sig);
+            e = launch_kernel(fac_small_svd_kernel, dim3(M), dim3(kSvdThreads), stream, (const double*)Gp, nc, UA, UR, sig);
     }
     if (e == hipSuccess)
         e = launch_kernel(fac_finalize_kernel, dim3((T + kFThreads - 1) / kFThreads, M), blk, stream, (const float*)Y,
