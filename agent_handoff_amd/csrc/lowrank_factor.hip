@@ -235,17 +235,21 @@ __global__ __launch_bounds__(kFThreads) void fac_chol_kernel(const double* gpart
         double maxdiag = 0.0;
         for (int k = 0; k < kFK; ++k) maxdiag = fmax(maxdiag, g[k * kFK + k]);
         const double tol = 1e-12 * maxdiag;
+        const uint32_t ri = i < (uint32_t)kFK ? i : 0u;
         for (uint32_t j = 0; j < (uint32_t)kFK; ++j) {
+            // the pivot's sum and this row's sum in one loop: two independent
+            // chains of subtractions, each in its own order of k
             double s = g[j * kFK + j];
-            for (uint32_t k = 0; k < j; ++k) s -= L[j * kFK + k] * L[j * kFK + k];
+            double v = g[ri * kFK + j];
+            for (uint32_t k = 0; k < j; ++k) {
+                const double ljk = L[j * kFK + k];
+                s -= ljk * ljk;
+                v -= L[ri * kFK + k] * ljk;
+            }
             const bool keep = s > tol;
             const double ljj = keep ? sqrt(s) : 0.0;
-            double v = 0.0;
-            if (keep && i > j && i < (uint32_t)kFK) {
-                v = g[i * kFK + j];
-                for (uint32_t k = 0; k < j; ++k) v -= L[i * kFK + k] * L[j * kFK + k];
-                v /= ljj;
-            }
+            if (keep && i > j && i < (uint32_t)kFK) v /= ljj;
+            else v = 0.0;
             __builtin_amdgcn_wave_barrier();
             if (i == j) L[j * kFK + j] = ljj;
             if (i > j && i < (uint32_t)kFK) L[i * kFK + j] = v;
