@@ -212,10 +212,26 @@ __global__ __launch_bounds__(kFThreads) void fac_gram_partial_kernel(const float
 template <int NT>
 __device__ __forceinline__ void sum_gram(const double* gpart, uint32_t m, uint32_t nchunks, double* g) {
     const double* gp = gpart + (uint64_t)m * nchunks * kFK * kFK;
-    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += NT) {
-        double s = 0.0;
-        for (uint32_t c = 0; c < nchunks; ++c) s += gp[(uint64_t)c * kFK * kFK + i];
-        g[i] = s;
+    // a thread's elements side by side, chunk after chunk: each element is
+    // still summed in chunk order, while the loads of several chunks and
+    // elements are in flight together
+    constexpr int kPer = (kFK * kFK + NT - 1) / NT;
+    double acc[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc[e] = 0.0;
+#pragma unroll 4
+    for (uint32_t c = 0; c < nchunks; ++c) {
+        const double* gc = gp + (uint64_t)c * kFK * kFK;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const uint32_t i = threadIdx.x + (uint32_t)e * NT;
+            if (i < (uint32_t)(kFK * kFK)) acc[e] += gc[i];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const uint32_t i = threadIdx.x + (uint32_t)e * NT;
+        if (i < (uint32_t)(kFK * kFK)) g[i] = acc[e];
     }
     __syncthreads();
 }
