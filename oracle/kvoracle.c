@@ -489,7 +489,6 @@ static void card_pack_record(const uint16_t* x, uint32_t d, uint32_t b, uint8_t*
     }
 }
 
-/* out = bf16(q * s + mn) in binary64; width 16 copies the stored bf16. */
 /* One dequantised card value (QKVShare method item 3, the receiver
  * rebuilding full-width values from a group's scale and minimum): q*s + mn
  * computed in binary32 with one rounding (fmaf; q*s alone is exact, at most
@@ -499,6 +498,9 @@ uint16_t or_card_dequant(uint32_t q, uint16_t scale_f16, uint16_t min_bf16) {
     return or_f64_to_bf16((double)r);
 }
 
+/* One record back to d bf16 values: width 16 copies the stored bf16, other
+ * widths read each code LSB-first and dequantise it with its group's scale
+ * and minimum. */
 static void card_unpack_record(const uint8_t* rec, uint32_t d, uint32_t b, uint16_t* out) {
     if (b == 16) {
         for (uint32_t i = 0; i < d; ++i) out[i] = get_u16(rec + 2 * i);

@@ -16,8 +16,12 @@ where a bf16 is stored.
 
 import numpy as np
 
-from agent_handoff_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
 from . import f64_to_bf16
+
+
+def bf16_bits_to_f32(b):
+    """bf16 bit patterns -> float32 (exact: the bits become the top half)."""
+    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
 def round_bf16(x):

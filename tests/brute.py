@@ -162,19 +162,3 @@ def card_record_size(d, b):
         return 2 * d
     raw = 4 * (d // 32) + d * b // 8
     return -(-raw // 16) * 16
-
-
-def card_quant_brute(x_bits, b):
-    """One group of 32 bf16 values: (scale fp16 bits, min bf16 bits, codes)
-    following the min-max definition with numpy float32 scalars."""
-    x = bf16_bits_to_f32(x_bits)
-    mn, mx = np.float32(x.min()), np.float32(x.max())
-    mn = np.float32(mn + np.float32(0.0))
-    mx = np.float32(mx + np.float32(0.0))
-    qmax = np.float32(2 ** b - 1)
-    s = np.float32(np.float32(mx - mn) / qmax)
-    s16 = np.float16(min(s, np.float32(65504.0)))
-    sf = np.float32(s16)
-    inv = np.float32(0.0) if sf == 0 else np.float32(np.float32(1.0) / sf)
-    q = np.minimum(np.rint((x - mn) * inv), qmax).astype(np.uint8)
-    return int(s16.view(np.uint16)), int(np.float32(mn).view(np.uint32) >> np.uint32(16)), q
