@@ -76,6 +76,22 @@ int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* po
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
+int kvpool_encode_noalloc(const kvc_shape* shape, const void* k, const void* v, void* pool, size_t pool_bytes,
+                          hipStream_t stream) {
+    if (!shape || !k || !v || !pool) return KVC_E_NULL;
+    if (!pool_shape(shape)) return KVC_E_SHAPE;
+    const uint64_t need = kvpool_bytes(shape);
+    if (pool_bytes < need) return KVC_E_SIZE;
+    if (kvpool_workspace_bytes(shape) > kvc::kNoAllocScratchBytes) return KVC_E_SCRATCH;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pool, 256)) return KVC_E_ALIGN;
+    const uint64_t kvb = kv_bytes(shape);
+    if (overlap(pool, need, k, kvb) || overlap(pool, need, v, kvb)) return KVC_E_ALIAS;
+    uint32_t* ws = nullptr;
+    if (kvc::noalloc_scratch(&ws) != hipSuccess) return KVC_E_HIP;
+    const hipError_t e = kvc::launch_pool_encode(to_shape(shape), k, v, pool, ws, stream);
+    return e == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
 int kvpool_decode(const kvc_shape* shape, const void* pool, size_t pool_bytes, uint32_t layer_begin,
                   uint32_t layer_end, void* const* k_out, void* const* v_out, uint32_t n_out,
                   int32_t* dev_status, hipStream_t stream) {
@@ -338,6 +354,7 @@ const char* kvc_strerror(int code) {
         case KVC_E_FORMAT: return "malformed pool or card header";
         case KVC_E_RANGE: return "argument out of range (layer range, agent count, pairing, rank or anchors)";
         case KVC_E_HIP: return "kernel launch failed";
+        case KVC_E_SCRATCH: return "the shape needs more workspace than the library's allocation-free scratch holds";
         default: return "unknown error";
     }
 }

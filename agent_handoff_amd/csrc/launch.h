@@ -16,6 +16,12 @@ constexpr int kMaxAgents = 64;
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
                               hipStream_t stream);
 
+// kvpool_encode_noalloc: the library's per-GPU encode workspace (1 MiB,
+// enough for kvpool_workspace_bytes of up to 255 layers) and its device
+// address on the current device.
+constexpr uint64_t kNoAllocScratchBytes = 1ull << 20;
+hipError_t noalloc_scratch(uint32_t** out);
+
 hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,
                               void* const* k_out, void* const* v_out, uint32_t n_out,
                               int32_t* dev_status, hipStream_t stream);

@@ -34,8 +34,15 @@
 #include "launch.h"
 #include "layout.h"
 
+#include <atomic>
 #include <cstdlib>
+#include <mutex>
 #include <utility>
+
+// Encode workspace held by the library for kvpool_encode_noalloc (callers
+// that cannot allocate). A module variable exists once per GPU, at its own
+// address on each; it starts zeroed and keeps what the last call left.
+static __device__ __align__(256) uint32_t scratch[kvc::kNoAllocScratchBytes / 4];
 
 namespace kvc {
 namespace {
@@ -1058,6 +1065,33 @@ uint64_t encode_poll_ticks() {
 }
 
 }  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (in host code the array's name is only a
+// stand-in for the symbol, not a device address).
+hipError_t noalloc_scratch(uint32_t** out) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<uint32_t*> ptrs[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    uint32_t* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = ptrs[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            p = static_cast<uint32_t*>(addr);
+            ptrs[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
                               hipStream_t stream) {

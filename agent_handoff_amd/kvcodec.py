@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvcodec.so")
 
 KVC_OK = 0
 KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN = -1, -2, -3, -4
-KVC_E_ALIAS, KVC_E_FORMAT, KVC_E_RANGE, KVC_E_HIP = -5, -6, -7, -8
+KVC_E_ALIAS, KVC_E_FORMAT, KVC_E_RANGE, KVC_E_HIP, KVC_E_SCRATCH = -5, -6, -7, -8, -9
 KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY = 1, 2, 4
 KVC_MAX_AGENTS = 64
 
@@ -54,6 +54,7 @@ def _load():
         "kvpool_bytes": (sz, [sp]),
         "kvpool_workspace_bytes": (sz, [sp]),
         "kvpool_encode": (i32, [sp, p, p, p, sz, p, sz, p]),
+        "kvpool_encode_noalloc": (i32, [sp, p, p, p, sz, p]),
         "kvpool_decode": (i32, [sp, p, sz, u32, u32, ctypes.POINTER(p), ctypes.POINTER(p), u32, p, p]),
         "cachecard_record_bytes": (sz, [u32, u32]),
         "cachecard_max_bytes": (sz, [sp]),
@@ -79,7 +80,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_decode",
+EXPORTED = ("kvpool_bytes", "kvpool_workspace_bytes", "kvpool_encode", "kvpool_encode_noalloc", "kvpool_decode",
             "cachecard_record_bytes", "cachecard_max_bytes", "cachecard_bytes_host",
             "cachecard_workspace_bytes", "cachecard_pack", "cachecard_unpack",
             "cachecard_transcode_workspace_bytes", "cachecard_transcode", "kvc_realign_keys",
@@ -146,6 +147,13 @@ def kvpool_encode(shape, k, v, pool, ws, stream=None):
     """k, v: bf16 [L, H, T, d]; pool, ws: uint8 device buffers."""
     _check(_lib.kvpool_encode(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(pool), _nbytes(pool),
                               _ptr(ws), _nbytes(ws), _stream(stream)), "kvpool_encode")
+
+
+def kvpool_encode_noalloc(shape, k, v, pool, stream=None):
+    """kvpool_encode with the library's own per-GPU scratch as workspace
+    (no allocation anywhere in the call)."""
+    _check(_lib.kvpool_encode_noalloc(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(pool), _nbytes(pool),
+                                      _stream(stream)), "kvpool_encode_noalloc")
 
 
 def kvpool_decode(shape, pool, layer_begin, layer_end, k_outs, v_outs, dev_status=None, stream=None):

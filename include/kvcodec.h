@@ -75,7 +75,8 @@ enum {
     KVC_E_ALIAS = -5,  /* an output overlaps an input or another output */
     KVC_E_FORMAT = -6, /* malformed header bytes */
     KVC_E_RANGE = -7,  /* argument out of range (layer range, agent count, ...) */
-    KVC_E_HIP = -8     /* a kernel launch failed */
+    KVC_E_HIP = -8,    /* a kernel launch failed */
+    KVC_E_SCRATCH = -9 /* needs more workspace than kvpool_encode_noalloc's scratch */
 };
 
 /* Bits set in *dev_status by device-side checks. */
@@ -127,6 +128,22 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape);
  * KVC_E_HIP. */
 int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool,
                   size_t pool_bytes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* kvpool_encode without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * workspace is a 1 MiB array inside the library, one per GPU (the current
+ * device's is used; `stream` must belong to that device), which each GPU
+ * holds until the process ends: shapes whose kvpool_workspace_bytes exceeds
+ * 1 MiB (more than 255 layers) are refused with KVC_E_SCRATCH. Every call on
+ * a GPU uses that GPU's one array, so calls that overlap in time on one GPU
+ * (other streams, other threads) race and must not be issued; calls in
+ * sequence on one stream are fine. Each call clears the part of the array
+ * it uses before its encode kernel. Arguments, output and the remaining
+ * errors are those of kvpool_encode (without the workspace checks); the
+ * pool is byte-identical to kvpool_encode's. */
+int kvpool_encode_noalloc(const kvc_shape* shape, const void* k, const void* v, void* pool,
+                          size_t pool_bytes, hipStream_t stream);
 
 /* Decompress layers [layer_begin, layer_end) of `pool` into the caches of
  * n_out agents (PolyKV 2.A, PooledAgent: layer-wise injection into each

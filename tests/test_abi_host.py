@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -88,7 +88,7 @@ def test_parse_header_of_oracle_pool_and_card():
 
 
 def test_strerror_covers_every_code():
-    for c in range(-8, 1):
+    for c in range(-9, 1):
         assert kv.kvc_strerror(c) != "unknown error"
     assert kv.kvc_strerror(-99) == "unknown error"
 
@@ -130,6 +130,29 @@ def test_encode_argument_errors():
     assert _enc(pool=3 * A + 16) == kv.KVC_E_ALIGN
     assert _enc(pool=A + KVB - 256) == kv.KVC_E_ALIAS       # pool overlaps k
     assert _enc(ws=3 * A + 256) == kv.KVC_E_ALIAS            # ws inside pool
+
+
+def _enc_noalloc(shape=S, k=A, v=2 * A, pool=3 * A, pool_bytes=None):
+    pb = kv.kvpool_bytes(shape or S) if pool_bytes is None else pool_bytes
+    return L.kvpool_encode_noalloc(ctypes.byref(shape) if shape is not None else None, k, v, pool, pb, None)
+
+
+@fake_addresses
+def test_encode_noalloc_argument_errors():
+    """The allocation-free encode refuses bad arguments, and any shape whose
+    workspace exceeds the library's 1 MiB scratch (more than 255 layers),
+    before touching the GPU."""
+    assert _enc_noalloc(shape=None) == kv.KVC_E_NULL
+    assert _enc_noalloc(pool=None) == kv.KVC_E_NULL
+    assert _enc_noalloc(shape=kv.kvc_shape(2, 2, 32, 96)) == kv.KVC_E_SHAPE
+    assert _enc_noalloc(pool_bytes=kv.kvpool_bytes(S) - 1) == kv.KVC_E_SIZE
+    assert kv.kvpool_workspace_bytes(kv.kvc_shape(255, 1, 16, 64)) <= 1 << 20
+    assert kv.kvpool_workspace_bytes(kv.kvc_shape(256, 1, 16, 64)) > 1 << 20
+    big = kv.kvc_shape(256, 1, 16, 64)
+    assert _enc_noalloc(shape=big, v=A + (1 << 30), pool=3 * A) == kv.KVC_E_SCRATCH
+    assert _enc_noalloc(k=A + 8) == kv.KVC_E_ALIGN
+    assert _enc_noalloc(pool=3 * A + 16) == kv.KVC_E_ALIGN
+    assert _enc_noalloc(pool=A + KVB - 256) == kv.KVC_E_ALIAS   # pool overlaps k
 
 
 def _dec(l0=0, l1=2, n=2, outs=None, pool=3 * A, pool_bytes=None, status=None):
