@@ -57,6 +57,8 @@ def lib():
         L.or_v_encode_vector.argtypes = [p, u32, p, p, p]
         L.or_v_decode_vector.restype = None
         L.or_v_decode_vector.argtypes = [p, ctypes.c_uint16, u32, p, p]
+        L.or_pool_near_boundary.restype = ctypes.c_int
+        L.or_pool_near_boundary.argtypes = [u32] * 4 + [p, p, p, ctypes.c_double, p]
         L.or_k_layer_absmax.restype = ctypes.c_float
         L.or_k_layer_absmax.argtypes = [p, u64]
         L.or_card_record_bytes.restype = u32
@@ -180,6 +182,20 @@ def v_decode_vector(codes, scale_bits):
     out = np.zeros(codes.size, np.uint16)
     lib().or_v_decode_vector(_ptr(codes), int(scale_bits), codes.size, _ptr(levels), _ptr(out))
     return out
+
+
+def pool_near_boundary(k, v, eps=1e-5):
+    """(keys, value coordinates) whose encoding decision lies within eps:
+    x * 127 / m within eps of a half-integer, z within eps of a threshold."""
+    L, H, T, d = k.shape
+    k = _check_bf16(k, (L, H, T, d))
+    v = _check_bf16(v, (L, H, T, d))
+    _, thr = _table()
+    out = np.zeros(2, np.uint64)
+    rc = lib().or_pool_near_boundary(L, H, T, d, _ptr(k), _ptr(v), _ptr(thr), float(eps), _ptr(out))
+    if rc:
+        raise ValueError(f"or_pool_near_boundary failed: {rc}")
+    return int(out[0]), int(out[1])
 
 
 def k_layer_absmax(k_layer):

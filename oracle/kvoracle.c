@@ -219,8 +219,7 @@ static float inv_sqrt_d(uint32_t d) { return (float)(1.0 / sqrt((double)d)); }
  *   z_i  = y_i * (d^-1/2 / s)              (r = 0 when s = 0)
  *   code = number of thresholds b_k with z_i >= b_k
  * Since H / sqrt(d) is orthonormal, z has unit mean square when s = rms. */
-void or_v_encode_vector(const uint16_t* v, uint32_t d, const float thr[7],
-                        uint16_t* scale_bits, uint8_t* codes) {
+static void v_normalised(const uint16_t* v, uint32_t d, float* z, uint16_t* scale_bits) {
     float x[128], y[128];
     for (uint32_t i = 0; i < d; ++i) x[i] = y[i] = or_bf16_to_f32(v[i]);
     float ss = pairwise_sum_of_squares(x, (int)d);
@@ -229,14 +228,20 @@ void or_v_encode_vector(const uint16_t* v, uint32_t d, const float thr[7],
     float s = or_f16_to_f32(sh);
     fwht_f32(y, (int)d);
     float r = (s == 0.0f) ? 0.0f : inv_sqrt_d(d) / s;
+    for (uint32_t i = 0; i < d; ++i) z[i] = y[i] * r;
+    *scale_bits = sh;
+}
+
+void or_v_encode_vector(const uint16_t* v, uint32_t d, const float thr[7],
+                        uint16_t* scale_bits, uint8_t* codes) {
+    float z[128];
+    v_normalised(v, d, z, scale_bits);
     for (uint32_t i = 0; i < d; ++i) {
-        float z = y[i] * r;
         uint8_t c = 0;
         for (int k = 0; k < 7; ++k)
-            if (z >= thr[k]) c++;
+            if (z[i] >= thr[k]) c++;
         codes[i] = c;
     }
-    *scale_bits = sh;
 }
 
 /* Reconstruction of one value vector, binary64:
@@ -251,14 +256,19 @@ void or_v_decode_vector(const uint8_t* codes, uint16_t scale_bits, uint32_t d,
 }
 
 /* Per-layer key scale (PolyKV 2.B item 1, one linear scale per tensor; the
- * tensor is one layer's K, all heads, tokens and channels). */
+ * tensor is one layer's K, all heads, tokens and channels). The maximum
+ * magnitude is taken on the bf16 bit patterns with the sign cleared, as
+ * unsigned integers: for finite values that is the order of |x|; an
+ * infinity ranks above every finite value and a NaN above an infinity (the
+ * pages define the codec on finite values only; this fixes what a layer
+ * holding Inf or NaN gives, see or_pool_encode). */
 float or_k_layer_absmax(const uint16_t* k_layer, uint64_t n) {
-    float m = 0.0f;
+    uint16_t m = 0;
     for (uint64_t i = 0; i < n; ++i) {
-        float a = fabsf(or_bf16_to_f32(k_layer[i]));
+        uint16_t a = (uint16_t)(k_layer[i] & 0x7FFFu);
         if (a > m) m = a;
     }
-    return m;
+    return or_bf16_to_f32(m);
 }
 
 /* q = clamp(rint(x * (127 / m)), -127, 127); scale = m / 127 (binary32). */
@@ -285,6 +295,44 @@ static void v_unpack_planes(const uint8_t* in, uint32_t d, uint8_t* codes) {
     }
 }
 
+/* How many values sit near a decision of the encoder, for the tolerance
+ * report: out[0] counts keys whose x * (127 / m) (binary32) lies within eps
+ * of a half-integer (the rounding decision), out[1] value coordinates whose
+ * normalised rotated value z lies within eps of one of the 7 thresholds.
+ * Same operations and order as or_pool_encode. */
+int or_pool_near_boundary(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uint16_t* k,
+                          const uint16_t* v, const float thr[7], double eps, uint64_t out[2]) {
+    if (d != 64 && d != 128) return OR_E_ARG;
+    uint64_t per_layer = (uint64_t)H * T * d, nk = 0, nv = 0;
+    for (uint32_t l = 0; l < L; ++l) {
+        const uint16_t* kl = k + l * per_layer;
+        float m = or_k_layer_absmax(kl, per_layer);
+        if (!isfinite(m) || m == 0.0f) continue;
+        float inv = 127.0f / m;
+        #pragma omp parallel for schedule(static) reduction(+ : nk)
+        for (int64_t i = 0; i < (int64_t)per_layer; ++i) {
+            double u = fabs((double)(or_bf16_to_f32(kl[i]) * inv));
+            if (fabs(u - floor(u) - 0.5) < eps) nk++;
+        }
+    }
+    int64_t n_vec = (int64_t)L * H * T;
+    #pragma omp parallel for schedule(static) reduction(+ : nv)
+    for (int64_t vec = 0; vec < n_vec; ++vec) {
+        float z[128];
+        uint16_t sh;
+        v_normalised(v + (uint64_t)vec * d, d, z, &sh);
+        for (uint32_t i = 0; i < d; ++i) {
+            int near = 0;
+            for (int t = 0; t < 7; ++t)
+                if (fabs((double)z[i] - (double)thr[t]) < eps) near = 1;
+            nv += (uint64_t)near;
+        }
+    }
+    out[0] = nk;
+    out[1] = nv;
+    return OR_OK;
+}
+
 /* Encode K and V (bf16 [L][H][T][d], raw bits) into a pool (PolyKV 2.A/2.B). */
 int or_pool_encode(uint32_t L, uint32_t H, uint32_t T, uint32_t d,
                    const uint16_t* k, const uint16_t* v, const float thr[7], uint8_t* pool) {
@@ -304,10 +352,17 @@ int or_pool_encode(uint32_t L, uint32_t H, uint32_t T, uint32_t d,
     for (uint32_t l = 0; l < L; ++l) {
         const uint16_t* kl = k + l * per_layer;
         float m = or_k_layer_absmax(kl, per_layer);
+        int8_t* kc = (int8_t*)(pool + off[1]) + l * per_layer;
+        if (!isfinite(m)) {
+            /* a layer holding Inf or NaN keys: scale NaN (bits 0x7FC00000),
+             * every code 0, so its keys decode to NaN */
+            put_u32(pool + off[0] + 4ull * l, 0x7FC00000u);
+            memset(kc, 0, per_layer);
+            continue;
+        }
         float scale = (m == 0.0f) ? 0.0f : m / 127.0f;
         float inv = (m == 0.0f) ? 0.0f : 127.0f / m;
         put_f32(pool + off[0] + 4ull * l, scale);
-        int8_t* kc = (int8_t*)(pool + off[1]) + l * per_layer;
         #pragma omp parallel for schedule(static)
         for (int64_t i = 0; i < (int64_t)per_layer; ++i)
             kc[i] = k_quantize(or_bf16_to_f32(kl[i]), inv);

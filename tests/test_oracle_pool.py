@@ -308,3 +308,57 @@ def test_rotation_gaussianises_heavy_tailed_vectors():
     z = (x @ hadamard(64).T) / (8.0 * rms)
     kx, kz = np.mean((x / rms) ** 4), np.mean(z ** 4)
     assert kx > 10 and abs(kz - 3) < abs(kx - 3) / 5
+
+
+def test_non_finite_inputs_follow_the_stated_rule():
+    """Inputs are expected finite; the rule for the rest: a layer's key
+    maximum is taken on the sign-cleared bit patterns (NaN above Inf), so a
+    layer holding Inf or NaN gets a NaN scale and zero codes (keys decode to
+    NaN) while the other layers are as if encoded alone; a value vector with
+    Inf or NaN gets the saturated scale 65504, and a NaN coordinate code 0."""
+    shape = (3, 1, 16, 64)
+    k, v = _random_kv(shape, 4)
+    k[0, 0, 3, 7] = 0x7FC1   # NaN
+    k[1, 0, 9, 2] = 0xFF80   # -Inf
+    v[2, 0, 5, 0] = 0x7F80   # +Inf
+    v[2, 0, 6, 1] = 0xFFC0   # NaN
+    pool = oracle.pool_encode(k, v)
+    k_scale, k_codes, v_scale, _ = _sections(pool, shape)
+    for l in (0, 1):
+        assert k_scale[l:l + 1].view(np.uint32)[0] == 0x7FC00000
+        assert np.all(k_codes[l] == 0)
+    alone = oracle.pool_encode(k[2:3].copy(), v[2:3].copy())
+    s2, c2, _, _ = _sections(alone, (1, 1, 16, 64))
+    assert k_scale[2] == s2[0] and np.array_equal(k_codes[2], c2[0])
+    ko, vo = oracle.pool_decode(pool, shape)
+    assert np.all(np.isnan(bf16_bits_to_f32(ko[:2])))
+    assert v_scale[2, 0, 5] == np.float16(65504).view(np.uint16)
+    assert v_scale[2, 0, 6] == np.float16(65504).view(np.uint16)
+    codes = oracle.pool_v_codes(pool, shape)
+    assert np.all(codes[2, 0, 6] == 0)          # every rotated coordinate NaN
+    assert not np.any(np.isnan(bf16_bits_to_f32(vo[2, 0, 5])))
+
+
+def test_near_boundary_counts_against_brute_force():
+    """The tolerance report's counts: keys within eps of a rounding tie and
+    value coordinates within eps of a threshold, against the float64 brute
+    force (which differs from the binary32 pipeline only within a few ulps,
+    so a generous eps on random data gives the same counts up to a few)."""
+    shape = (2, 3, 64, 128)
+    k, v = _random_kv(shape, 13)
+    nk, nv = oracle.pool_near_boundary(k, v, eps=1e-3)
+    _, _, tie = k_codes_brute(k)   # float64 |frac - 0.5| < 1e-5
+    x = bf16_bits_to_f32(k).astype(np.float64)
+    m = np.max(np.abs(x.reshape(2, -1)), axis=1)[:, None, None, None]
+    u = np.abs(x * 127.0 / m)
+    ref_k = int(np.count_nonzero(np.abs(u - np.floor(u) - 0.5) < 1e-3))
+    assert abs(nk - ref_k) <= 2 and nk >= int(np.count_nonzero(tie))
+    xv = bf16_bits_to_f32(v).astype(np.float64).reshape(-1, 128)
+    s = np.minimum(np.sqrt(np.mean(xv * xv, axis=1)), 65504.0).astype(np.float16).astype(np.float64)
+    z = (xv @ hadamard(128).T) / (math.sqrt(128) * s[:, None])
+    ref_v = int(np.count_nonzero(np.min(np.abs(z[:, :, None] - np.asarray(THRESH, np.float64)), axis=2) < 1e-3))
+    assert abs(nv - ref_v) <= 2
+    assert 0 < nv < 0.01 * v.size
+    # with eps = 0 nothing is counted; the counts grow with eps
+    assert oracle.pool_near_boundary(k, v, eps=0.0) == (0, 0)
+    assert oracle.pool_near_boundary(k, v, eps=1e-2)[1] > nv
