@@ -27,10 +27,15 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose=False, extra=()):
+# streaming bandwidth probes of the benchmark (not part of the codec ABI)
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libkvprobe.so")
+
+
+def _hipcc(srcs, out, verbose, extra=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + sources() + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + list(srcs) + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,7 +46,14 @@ def build(verbose=False, extra=()):
         raise RuntimeError(f"hipcc failed ({res.returncode})")
     if verbose and errs:
         print(errs)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False, extra=()):
+    """libkvcodec.so (the codec) and libkvprobe.so (the benchmark's probes)."""
+    _hipcc(sources(), LIB_PATH, verbose, extra)
+    _hipcc([PROBE_SRC], PROBE_LIB, verbose)
     return LIB_PATH
 
 

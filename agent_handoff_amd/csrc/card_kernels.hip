@@ -27,6 +27,9 @@ namespace kvc {
 namespace {
 
 constexpr uint32_t kFlagBadHeader = 1, kFlagBadWidth = 2, kFlagCapacity = 4;
+// internal: the input card of a transcode was refused (already reported)
+constexpr uint32_t kFlagInputRefused = 256;
+constexpr uint32_t kStatusBits = kFlagBadHeader | kFlagBadWidth | kFlagCapacity;
 
 // Workgroups are dealt to the 8 XCDs in turn, so consecutive token blocks
 // of a stream would land on different XCDs (their L2s each fetching the
@@ -70,6 +73,7 @@ struct ScanParams {
     uint32_t L, H, T, d;
     CardMetaDev meta;
     const uint8_t* meta_src;   // transcode: card whose model ID and position offset are carried over
+    const uint64_t* prior_info;  // transcode, output scan: the input scan's info (its flags refuse the output)
 };
 
 struct CardParams {
@@ -166,7 +170,12 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
         p.off[p.T] = carry;
         if (p.card_out) {
             if (total > p.limit) flags |= kFlagCapacity;
+            if (p.prior_info && p.prior_info[2] != 0) flags |= kFlagInputRefused;
             if (p.dev_card_bytes) *p.dev_card_bytes = total;
+            // a card that will not be written gets a zero magic word (the
+            // buffer holds at least a header), so that nothing it held before
+            // can pass for this call's output
+            if (flags) reinterpret_cast<uint32_t*>(p.card_out)[0] = 0;
         } else {
             const bool ok = hw[0] == kCardMagic && hw[1] == (1u | (2u << 16)) && hw[2] == p.L && hw[3] == p.H &&
                             hw[4] == p.T && hw[5] == p.d && hw[6] == kCardGroup && hq[0] == kCardHeaderBytes &&
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
         p.info[0] = S;
         p.info[1] = total;
         p.info[2] = flags;
-        if (flags && p.status) atomicOr(p.status, (int)flags);
+        if ((flags & kStatusBits) && p.status) atomicOr(p.status, (int)(flags & kStatusBits));
         flags_sh = flags;
     }
     __syncthreads();
@@ -751,6 +760,7 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
     b.T = s.T;
     b.d = s.d;
     b.meta_src = static_cast<const uint8_t*>(card_in);
+    b.prior_info = a.info;
     e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, b);
     if (e != hipSuccess) return e;
     const CardParams cp = card_params(s, ws);

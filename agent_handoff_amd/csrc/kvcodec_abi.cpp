@@ -62,33 +62,47 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape) {
 }
 
 int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool, size_t pool_bytes,
-                  void* ws, size_t ws_bytes, hipStream_t stream) {
+                  void* ws, size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
     if (!shape || !k || !v || !pool || !ws) return KVC_E_NULL;
     if (!pool_shape(shape)) return KVC_E_SHAPE;
     const uint64_t need = kvpool_bytes(shape), ws_need = kvpool_workspace_bytes(shape);
     if (pool_bytes < need || ws_bytes < ws_need) return KVC_E_SIZE;
-    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pool, 256) || !aligned(ws, 16)) return KVC_E_ALIGN;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pool, 256) || !aligned(ws, 16) ||
+        (dev_status && !aligned(dev_status, 4)))
+        return KVC_E_ALIGN;
     const uint64_t kvb = kv_bytes(shape);
-    if (overlap(pool, need, k, kvb) || overlap(pool, need, v, kvb) || overlap(ws, ws_need, k, kvb) ||
-        overlap(ws, ws_need, v, kvb) || overlap(ws, ws_need, pool, need))
-        return KVC_E_ALIAS;
-    const hipError_t e = kvc::launch_pool_encode(to_shape(shape), k, v, pool, static_cast<uint32_t*>(ws), stream);
+    const void* outs[3] = {pool, ws, dev_status};
+    const uint64_t outn[3] = {need, ws_need, dev_status ? 4u : 0u};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], outn[i], k, kvb) || overlap(outs[i], outn[i], v, kvb)) return KVC_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return KVC_E_ALIAS;
+    }
+    const hipError_t e = kvc::launch_pool_encode(to_shape(shape), k, v, pool, static_cast<uint32_t*>(ws), dev_status,
+                                                 stream);
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
 int kvpool_encode_noalloc(const kvc_shape* shape, const void* k, const void* v, void* pool, size_t pool_bytes,
-                          hipStream_t stream) {
+                          int32_t* dev_status, hipStream_t stream) {
     if (!shape || !k || !v || !pool) return KVC_E_NULL;
     if (!pool_shape(shape)) return KVC_E_SHAPE;
     const uint64_t need = kvpool_bytes(shape);
     if (pool_bytes < need) return KVC_E_SIZE;
     if (kvpool_workspace_bytes(shape) > kvc::kNoAllocScratchBytes) return KVC_E_SCRATCH;
-    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pool, 256)) return KVC_E_ALIGN;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(pool, 256) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_E_ALIGN;
     const uint64_t kvb = kv_bytes(shape);
     if (overlap(pool, need, k, kvb) || overlap(pool, need, v, kvb)) return KVC_E_ALIAS;
+    if (dev_status && (overlap(dev_status, 4, k, kvb) || overlap(dev_status, 4, v, kvb) ||
+                       overlap(dev_status, 4, pool, need)))
+        return KVC_E_ALIAS;
     uint32_t* ws = nullptr;
     if (kvc::noalloc_scratch(&ws) != hipSuccess) return KVC_E_HIP;
-    const hipError_t e = kvc::launch_pool_encode(to_shape(shape), k, v, pool, ws, stream);
+    // the scratch starts zeroed when the library is loaded; each call tags
+    // the words it writes with its own call number, so nothing an earlier
+    // call left there is taken for this call's
+    const hipError_t e = kvc::launch_pool_encode(to_shape(shape), k, v, pool, ws, dev_status, stream);
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 

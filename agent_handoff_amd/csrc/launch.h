@@ -12,9 +12,11 @@ struct Shape {
 
 constexpr int kMaxAgents = 64;
 
-// Pool encode: ws holds L u32 per-layer absmax words (bf16 magnitude bits).
+// Pool encode: ws is the encode workspace (encode_workspace_words(L) u32
+// words, zero before its first use, written by each call with words tagged
+// by that call's number).
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
-                              hipStream_t stream);
+                              int32_t* dev_status, hipStream_t stream);
 
 // kvpool_encode_noalloc: the library's per-GPU encode workspace (1 MiB,
 // enough for kvpool_workspace_bytes of up to 255 layers) and its device

@@ -58,28 +58,45 @@ struct EncodeParams {
     const uint16_t* v;
     uint8_t* pool;
     uint32_t* ws;           // workspace, see the slot helpers below
+    int32_t* status;        // device status word or nullptr
     uint32_t L, H, T, nb;   // nb = 16-token blocks per head
     uint32_t blocks_per_layer;  // H * nb
     uint32_t layers_per_round;  // single-pass encode: whole layers per round
     uint64_t n_waves;           // L * H * nb
     uint64_t poll_ticks;        // single-pass encode: bound on the wait for other workgroups' maxima
+    uint32_t absmax_groups;     // two-pass encode: key-maximum workgroups per layer
+    uint64_t call;              // single-pass encode: this call's number (tags its exchange words)
     PoolLayout lay;
 };
 
-// Encode workspace (u32 words): [2] the single-pass encode's timeout flag,
-// up to 64 reserved words; then one region that a call uses in one of two
-// ways: the two-pass encode's kSlots partial key maxima per layer, each on
-// its own 128-byte line so that concurrent atomics spread over addresses,
-// or the single-pass encode's flag words, one per (layer, workgroup). Each
-// call zeroes the head and the part of the region its path uses.
-constexpr uint32_t kSlots = 16;
-constexpr uint32_t kSlotStride = 32;  // words
-constexpr uint32_t kWsHead = 64;      // words
-constexpr uint32_t kWsTimeout = 2;
+// Encode workspace (u32 words): 64 head words, then kWsWordsPerLayer words
+// per layer, used by one of two paths per call.
+//  - Single pass: one 64-bit exchange word per (layer, workgroup) that its
+//    workgroup publishes and every workgroup reads, some before it is
+//    written. Each call tags the words it writes with a call number of its
+//    own (48 bits, from a per-process counter on the host, never reused): a
+//    word counts only if it carries this call's number, so words left by
+//    earlier calls (or zeros) are never taken for this call's, and nothing
+//    needs clearing between calls. Head words [2..3]: the number of a call
+//    whose wait gave up (64 bits).
+//  - Two passes: the key-maximum pass stores each workgroup's partial
+//    maximum of a layer in a word of its own, at the end of the region
+//    (kMaxAbsmaxGroups words per layer), and the encode pass reads them:
+//    every word read is written earlier in the same call.
+// A single-pass word is (call << 16) | 0x8000 | maximum bits (15 bits): a
+// pair of two-pass words (each below 0x8000) never has bit 15 set, so it
+// cannot pass for one. The workspace must hold zeros before its first
+// single-pass encode (zero never matches a call number, which starts at 1).
+constexpr uint32_t kMaxAbsmaxGroups = 64;
+constexpr uint32_t kWsHead = 64;              // words
+constexpr uint32_t kWsWordsPerLayer = 1024;  // = encode_workspace_words(L) / L, less the head
+constexpr uint32_t kWsGaveUp = 2;             // u64 at words 2..3
+constexpr int32_t kDevTimeout = 8;            // KVC_DEV_ENCODE_TIMEOUT
 
-__device__ __forceinline__ uint32_t* absmax_slot(uint32_t* ws, uint32_t l, uint32_t s) {
-    return ws + kWsHead + (l * kSlots + s) * kSlotStride;
+__device__ __forceinline__ uint32_t* absmax_slot(uint32_t* ws, uint32_t L, uint32_t l, uint32_t s) {
+    return ws + kWsHead + (uint64_t)L * (kWsWordsPerLayer - kMaxAbsmaxGroups) + (uint64_t)l * kMaxAbsmaxGroups + s;
 }
+
 
 struct DecodeParams {
     const uint8_t* pool;
@@ -133,6 +150,16 @@ __device__ __forceinline__ float fwht_quad_sign(uint32_t m) {
     return (__builtin_popcount(m & 3u) & 1) ? -1.0f : 1.0f;
 }
 
+// Maximum of r over the wave.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
+        r = t > r ? t : r;
+    }
+    return r;
+}
+
 // Header (64 B) and every padding byte of the pool; run by workgroup 0.
 __device__ void pool_header_and_padding(const EncodeParams& p, uint32_t d, uint32_t tid) {
     uint8_t* pool = p.pool;
@@ -175,9 +202,10 @@ __global__ void fill_zero_kernel(uint4* p, uint32_t n4) {
 // Per-layer max |K| (PolyKV 2.B item 1: one linear scale per tensor). For
 // bf16, |x| ordering equals integer ordering of the bits with the sign
 // cleared, so the maximum is taken on 16-bit integers (packed max, two
-// values per instruction).
+// values per instruction). Workgroup x of layer l (gridDim.x <=
+// kMaxAbsmaxGroups) stores its partial maximum in word x of the layer.
 __global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* __restrict__ k,
-                                                                  uint64_t per_layer_u4,
+                                                                  uint64_t per_layer_u4, uint32_t L,
                                                                   uint32_t* __restrict__ ws) {
     typedef unsigned short us2 __attribute__((ext_vector_type(2)));
     const uint32_t l = blockIdx.y;
@@ -216,7 +244,7 @@ __global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* 
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kBlockThreads / kWave; ++w) r = red[w] > r ? red[w] : r;
-        atomicMax(absmax_slot(ws, l, blockIdx.x % kSlots), r);
+        *absmax_slot(ws, L, l, blockIdx.x) = r;
     }
 }
 
@@ -351,17 +379,24 @@ __device__ __forceinline__ void encode_values(const EncodeParams& p, const Block
 // Keys of one block given the layer's max m (as bf16 magnitude bits)
 // (PolyKV 2.B item 1): q = rint(x * (127 / m)). |x * inv| <= 127 (1 + 2^-23),
 // so q never leaves [-127, 127]. Rounding adds 1.5*2^23: the low byte of the
-// sum is the two's-complement integer (ties to even).
+// sum is the two's-complement integer (ties to even). The maximum is taken
+// on the sign-cleared bit patterns, so an Inf or NaN key makes it
+// non-finite; such a layer gets a NaN scale and all-zero codes.
 template <int D>
 __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const BlockPos& b, const uint4 (&kraw)[D / 32],
                                               uint32_t mbits, EncodeStage<D>& stg, uint32_t lane) {
     constexpr int C = D / 4;
     const float mk = __uint_as_float(mbits << 16);
+    const bool finite = mbits < 0x7F80u;
     const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
     uint32_t out[C / 4];
 #pragma unroll
     for (int j = 0; j < C / 4; ++j) {
+        if (!finite) {
+            out[j] = 0;
+            continue;
+        }
         const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
         const float q0 = bf16_lo(w0) * inv + 12582912.0f;
         const float q1 = bf16_hi(w0) * inv + 12582912.0f;
@@ -382,7 +417,8 @@ __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const Block
         if ((64 * j + lane) / (D / 16) < b.nv) st_stream(dst + 64 * j + lane, chunk16);
     }
     if (b.bidx == 0 && lane == 0)
-        reinterpret_cast<float*>(p.pool + p.lay.k_scale)[b.l] = (mk == 0.0f) ? 0.0f : mk / 127.0f;
+        reinterpret_cast<uint32_t*>(p.pool + p.lay.k_scale)[b.l] =
+            finite ? __float_as_uint((mk == 0.0f) ? 0.0f : mk / 127.0f) : 0x7FC00000u;
 }
 
 // Two passes: the per-layer key maxima were reduced by key_absmax_kernel;
@@ -402,12 +438,10 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams
     load_lane<D>(p.k, b.elem, kraw);
     load_lane<D>(p.v, b.elem, vraw);
     encode_values<D>(p, b, vraw, stage_all[wib], lane);
-    uint32_t mbits = 0;
-#pragma unroll
-    for (uint32_t s = 0; s < kSlots; ++s) {
-        const uint32_t v = *absmax_slot(p.ws, b.l, s);
-        mbits = v > mbits ? v : mbits;
-    }
+    // the layer's partial maxima, one per key-maximum workgroup (lane i reads
+    // word i), reduced across the wave
+    const uint32_t part = lane < p.absmax_groups ? *absmax_slot(p.ws, p.L, b.l, lane) : 0u;
+    const uint32_t mbits = wave_max_u32(part);
     quantize_keys<D>(p, b, kraw, mbits, stage_all[wib], lane);
 }
 
@@ -453,8 +487,8 @@ constexpr int kFusedThreads = (kFusedSlots + kFusedKeyWaves + 1) * kWave;
 constexpr int kQuantLag = 3;                // rounds between parking keys and quantising them
 constexpr int kHoldRounds = kQuantLag + 1;  // LDS key buffers and handshake entries
 constexpr uint32_t kMaxRoundLayers = 32;
-constexpr uint32_t kMaxFusedGrid = 1024;  // workgroups; sizes the flag words of the workspace
-constexpr uint32_t kFlag = 0x80000000u;
+constexpr uint32_t kMaxFusedGrid = 1024;  // bound on the grid (the launch keeps it below 960); sizes the poll registers
+constexpr uint64_t kWordFlag = 0x8000u;
 // Spin limit of the waits inside a workgroup (key waves for their
 // coordinator, coordinator for its key waves), in ticks of the 100 MHz
 // constant clock: 0.5 s. These waits depend only on the workgroup's own
@@ -462,8 +496,8 @@ constexpr uint32_t kFlag = 0x80000000u;
 constexpr uint64_t kWaitTicks = 50000000ull;
 
 // Flag words of layer l, one per workgroup of a G-workgroup grid.
-__device__ __forceinline__ uint32_t* round_flags(uint32_t* ws, uint32_t G, uint32_t l) {
-    return ws + kWsHead + (uint64_t)l * G;
+__device__ __forceinline__ uint64_t* round_flags(uint32_t* ws, uint32_t G, uint32_t l) {
+    return reinterpret_cast<uint64_t*>(ws + kWsHead) + (uint64_t)l * G;
 }
 
 template <int D>
@@ -478,6 +512,7 @@ struct FusedLds {
     uint32_t layer_max[kHoldRounds][kMaxRoundLayers];  // every workgroup's, per layer
     uint32_t done[kHoldRounds];                        // key waves done with the round
     uint32_t ready;                                    // rounds whose maxima are in layer_max
+    uint32_t gave_up;                                  // a wave of this workgroup recorded a wait that gave up
 };
 
 // Largest bf16 magnitude (as bits) among a lane's raw words.
@@ -493,15 +528,6 @@ __device__ __forceinline__ uint32_t lane_absmax_bits(const uint4 (&raw)[N]) {
         mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, raw[i].w & 0x7FFF7FFFu));
     }
     return mx.x > mx.y ? mx.x : mx.y;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
-        r = t > r ? t : r;
-    }
-    return r;
 }
 
 // Largest key magnitude (bf16 bits) of layer l, read from the keys in HBM
@@ -547,9 +573,12 @@ __device__ __forceinline__ uint32_t lds_load(const uint32_t* a) {
 // (Waiting here, inside the rare branch, rather than on a returned value
 // keeps the common path free of a full wait that would drain the
 // prefetched loads.)
-__device__ __forceinline__ void note_timeout(const EncodeParams& p) {
-    __hip_atomic_fetch_or(p.ws + kWsTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void note_gave_up(const EncodeParams& p, uint32_t* lds_gave_up) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p.ws + kWsGaveUp), p.call, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (p.status) atomicOr(p.status, kDevTimeout);
     __builtin_amdgcn_s_waitcnt(0);
+    *lds_gave_up = 1;
 }
 
 // Block bi of every round: its layer within the round, its block within the
@@ -694,7 +723,7 @@ __device__ __forceinline__ void key_round(const EncodeParams& p, FusedLds<D>& sm
         const uint64_t start = wall_clock64();
         while (lds_load(&sm.ready) < rq + 1) {
             if (wall_clock64() - start > kWaitTicks) {
-                note_timeout(p);
+                note_gave_up(p, &sm.gave_up);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -752,7 +781,7 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
             const uint64_t start = wall_clock64();
             while (lds_load(&sm.done[r % kHoldRounds]) < (uint32_t)kFusedKeyWaves) {
                 if (wall_clock64() - start > kWaitTicks) {
-                    note_timeout(p);
+                    note_gave_up(p, &sm.gave_up);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -762,30 +791,31 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
             if (lane < kMaxRoundLayers) sm.wg_max[r % kHoldRounds][lane] = 0;  // reused in round r + 4
             if (lane == 0) sm.done[r % kHoldRounds] = 0;
             if (lane < q.nl)
-                __hip_atomic_store(round_flags(p.ws, gridDim.x, q.l0 + lane) + blockIdx.x, kFlag | m, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(round_flags(p.ws, gridDim.x, q.l0 + lane) + blockIdx.x,
+                                   (p.call << 16) | kWordFlag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (r >= 1) {
             // every workgroup's maxima of round r-1, reduced per layer
             const uint32_t rq = r - 1;
             const Round q = round_of(p, rq);
             for (uint32_t lr = 0; lr < q.nl; ++lr) {
-                const uint32_t* f = round_flags(p.ws, gridDim.x, q.l0 + lr);
+                const uint64_t* f = round_flags(p.ws, gridDim.x, q.l0 + lr);
+                const uint64_t tag = (p.call << 16) | kWordFlag;  // this call's words: (word & ~0x7FFF) == tag
                 // all of the layer's words at once (lane + 64 i), then again
                 // for those not yet flagged
                 constexpr int kPer = kMaxFusedGrid / kWave;
-                uint32_t v[kPer];
+                uint64_t v[kPer];
 #pragma unroll
                 for (int i = 0; i < kPer; ++i) {
                     const uint32_t g = lane + (uint32_t)i * kWave;
-                    v[i] = g < G ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlag;
+                    v[i] = g < G ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
                 }
                 const uint64_t start = wall_clock64();
                 bool all_flagged = false;
                 for (;;) {
                     bool all = true;
 #pragma unroll
-                    for (int i = 0; i < kPer; ++i) all = all && (v[i] & kFlag);
+                    for (int i = 0; i < kPer; ++i) all = all && ((v[i] & ~0x7FFFull) == tag);
                     if (p.poll_ticks != 0 && __builtin_amdgcn_ballot_w64(!all) == 0) {
                         all_flagged = true;
                         break;
@@ -795,14 +825,15 @@ __device__ __forceinline__ void fused_coordinator(const EncodeParams& p, FusedLd
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) {
                         const uint32_t g = lane + (uint32_t)i * kWave;
-                        if (!(v[i] & kFlag)) v[i] = __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if ((v[i] & ~0x7FFFull) != tag)
+                            v[i] = __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
                 uint32_t mx = 0;
                 if (all_flagged) {
 #pragma unroll
                     for (int i = 0; i < kPer; ++i) {
-                        const uint32_t x = v[i] & ~kFlag;
+                        const uint32_t x = (uint32_t)(v[i] & 0x7FFFu);
                         mx = x > mx ? x : mx;
                     }
                     mx = wave_max_u32(mx);
@@ -828,6 +859,7 @@ __global__ __launch_bounds__(kFusedThreads) void pool_encode_fused_kernel(Encode
     if (threadIdx.x < kHoldRounds * kMaxRoundLayers) (&sm.wg_max[0][0])[threadIdx.x] = 0;
     if (threadIdx.x < kHoldRounds) sm.done[threadIdx.x] = 0;
     if (threadIdx.x == 0) sm.ready = 0;
+    if (threadIdx.x == 0) sm.gave_up = 0;
     __syncthreads();
     if (w < (uint32_t)kFusedSlots)
         fused_value_wave<D>(p, sm, w, lane, nrounds);
@@ -836,25 +868,24 @@ __global__ __launch_bounds__(kFusedThreads) void pool_encode_fused_kernel(Encode
     else
         fused_coordinator<D>(p, sm, lane, nrounds);
     // Header and padding last, by workgroup 0. A wait that gave up anywhere
-    // leaves the header's magic word zero (decode then refuses the pool):
-    // workgroup 0 checks the timeout flag before and again after writing the
-    // header, and a workgroup whose own wait gave up clears the word when it
-    // ends. Whatever the order of those events, one of the three sees the flag
-    // after the header is written or writes zero after it.
+    // leaves the header's magic word zero (decode then refuses the pool): a
+    // workgroup whose wait gave up records this call's number in the head
+    // and zeroes the magic at its end, after a device-scope fence;
+    // workgroup 0 reads the head after writing the header and a fence.
+    // Either workgroup 0 sees the record, or the other workgroup's zero
+    // lands after the header. (Other workgroups that see the record zero
+    // the magic too; only these two sides need the fences.)
     __syncthreads();
-    uint32_t* magic = reinterpret_cast<uint32_t*>(p.pool);
-    if (blockIdx.x == 0) {
-        if (threadIdx.x < kBlockThreads) pool_header_and_padding(p, D, threadIdx.x);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __threadfence();
-            if (__hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-                __hip_atomic_store(magic, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else if (threadIdx.x == 0 &&
-               __hip_atomic_load(p.ws + kWsTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-        __hip_atomic_store(magic, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x < kBlockThreads) {
+        pool_header_and_padding(p, D, threadIdx.x);
+        __threadfence();
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (blockIdx.x == 0 || sm.gave_up) __threadfence();
+        if (__hip_atomic_load(reinterpret_cast<const uint64_t*>(p.ws + kWsGaveUp), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT) == p.call)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(p.pool), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1054,12 +1085,24 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
 // publishes a round within a few microseconds, so the bound trips only for
 // a workgroup that is not running. KVC_ENCODE_POLL_US overrides it; 0 makes
 // every coordinator compute each layer's maximum itself (tests use it).
+// Values above kMaxPollUs are ignored: a round of up to kMaxRoundLayers
+// layers, each waited for this long and then read directly (a few hundred
+// microseconds), must stay well inside the 0.5 s guard of the key waves'
+// wait for their coordinator.
+constexpr uint64_t kMaxPollUs = 5000;
+
+// Call numbers of the single-pass encode: unique within the process, from
+// 1 (a zeroed workspace word never matches), 48 bits (never wrap).
+uint64_t next_call_number() {
+    static std::atomic<uint64_t> counter{1};
+    return counter.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+}
 uint64_t encode_poll_ticks() {
     uint64_t us = 200;
     if (const char* e = std::getenv("KVC_ENCODE_POLL_US")) {
         char* end = nullptr;
         const unsigned long long v = std::strtoull(e, &end, 10);
-        if (end != e && *end == '\0' && v <= 10000000ull) us = v;
+        if (end != e && *end == '\0' && v <= kMaxPollUs) us = v;
     }
     return us * 100;
 }
@@ -1094,12 +1137,13 @@ hipError_t noalloc_scratch(uint32_t** out) {
 }
 
 hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void* pool, uint32_t* ws,
-                              hipStream_t stream) {
+                              int32_t* dev_status, hipStream_t stream) {
     EncodeParams p;
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
     p.pool = static_cast<uint8_t*>(pool);
     p.ws = ws;
+    p.status = dev_status;
     p.L = s.L;
     p.H = s.H;
     p.T = s.T;
@@ -1108,27 +1152,23 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.layers_per_round = 0;
     p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
     p.poll_ticks = encode_poll_ticks();
+    p.absmax_groups = 0;
+    p.call = next_call_number();
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
-
-    // Zero the workspace head and the part of its region the chosen path
-    // uses (a whole number of 16-byte chunks; encode_workspace_words covers
-    // the largest of them).
-    auto zero_words = [&](uint64_t words) {
-        const uint32_t n4 = (uint32_t)((words + 3) / 4);
-        return launch_kernel(fill_zero_kernel, dim3((n4 + 255) / 256), dim3(256), stream, reinterpret_cast<uint4*>(ws),
-                             n4);
-    };
 
     // Single pass when a round of whole layers fits the LDS of a grid of one
     // workgroup per CU; otherwise two passes (the per-layer key maxima, then
     // the encode proper). The single pass is an ordinary launch: its waits
-    // never depend on every workgroup being resident (see the kernel).
+    // never depend on every workgroup being resident (see the kernel). Its
+    // exchange words (two u32 words per layer and workgroup) must leave the
+    // two-pass words at the end of each layer's share free.
     const void* fused = s.d == 64 ? reinterpret_cast<const void*>(pool_encode_fused_kernel<64>)
                                   : reinterpret_cast<const void*>(pool_encode_fused_kernel<128>);
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, kFusedThreads, 0) == hipSuccess && per_cu > 0 &&
+        2 * (uint64_t)cus * (uint64_t)per_cu <= kWsWordsPerLayer - kMaxAbsmaxGroups &&
         (uint64_t)cus * (uint64_t)per_cu <= kMaxFusedGrid) {
         const uint64_t grid = (uint64_t)cus * (uint64_t)per_cu;
         const uint64_t per_round = grid * kFusedSlots * (128u / s.d);  // blocks a round can hold
@@ -1137,24 +1177,21 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
         if (lpr > s.L) lpr = s.L;
         if (lpr >= 1) {
             p.layers_per_round = (uint32_t)lpr;
-            const hipError_t ez = zero_words(kWsHead + (uint64_t)s.L * grid);
-            if (ez != hipSuccess) return ez;
             void* argv[] = {&p};
             return report_launch(hipLaunchKernel(fused, dim3((uint32_t)grid), dim3(kFusedThreads), argv, 0, stream),
                                  "pool_encode_fused_kernel");
         }
     }
-    hipError_t e = zero_words(kWsHead + (uint64_t)s.L * kSlots * kSlotStride);
-    if (e != hipSuccess) return e;
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
     uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
-    if (gx > 64) gx = 64;
-    e = launch_kernel(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), stream,
-                      static_cast<const uint4*>(k), per_layer_u4, ws);
+    if (gx > kMaxAbsmaxGroups) gx = kMaxAbsmaxGroups;
+    p.absmax_groups = (uint32_t)gx;
+    hipError_t e = launch_kernel(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), stream,
+                                 static_cast<const uint4*>(k), per_layer_u4, s.L, ws);
     if (e != hipSuccess) return e;
     const uint64_t nblocks = (p.n_waves + 3) / 4;
-    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>,
-                         dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
+    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>, dim3((uint32_t)nblocks),
+                         dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,

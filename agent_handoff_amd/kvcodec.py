@@ -25,6 +25,7 @@ KVC_OK = 0
 KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN = -1, -2, -3, -4
 KVC_E_ALIAS, KVC_E_FORMAT, KVC_E_RANGE, KVC_E_HIP, KVC_E_SCRATCH = -5, -6, -7, -8, -9
 KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY = 1, 2, 4
+KVC_DEV_ENCODE_TIMEOUT = 8
 KVC_MAX_AGENTS = 64
 
 
@@ -53,8 +54,8 @@ def _load():
     sig = {
         "kvpool_bytes": (sz, [sp]),
         "kvpool_workspace_bytes": (sz, [sp]),
-        "kvpool_encode": (i32, [sp, p, p, p, sz, p, sz, p]),
-        "kvpool_encode_noalloc": (i32, [sp, p, p, p, sz, p]),
+        "kvpool_encode": (i32, [sp, p, p, p, sz, p, sz, p, p]),
+        "kvpool_encode_noalloc": (i32, [sp, p, p, p, sz, p, p]),
         "kvpool_decode": (i32, [sp, p, sz, u32, u32, ctypes.POINTER(p), ctypes.POINTER(p), u32, p, p]),
         "cachecard_record_bytes": (sz, [u32, u32]),
         "cachecard_max_bytes": (sz, [sp]),
@@ -115,6 +116,27 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _want(t, dtype, numel, what):
+    """Argument check before any device work: a GPU tensor of this dtype
+    and element count (numel None: any count), contiguous."""
+    if t is None:
+        raise ValueError(f"{what}: tensor required")
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
+    return _ptr(t)
+
+
+def _kv_numel(shape, layers=None):
+    L, H, T, d = (int(x) for x in shape)
+    return (L if layers is None else layers) * H * T * d
+
+
+def _opt(t, dtype, numel, what):
+    return None if t is None else _want(t, dtype, numel, what)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -143,17 +165,27 @@ def kvpool_workspace_bytes(shape):
     return int(_lib.kvpool_workspace_bytes(ctypes.byref(_shape(shape))))
 
 
-def kvpool_encode(shape, k, v, pool, ws, stream=None):
-    """k, v: bf16 [L, H, T, d]; pool, ws: uint8 device buffers."""
-    _check(_lib.kvpool_encode(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(pool), _nbytes(pool),
-                              _ptr(ws), _nbytes(ws), _stream(stream)), "kvpool_encode")
+def kvpool_encode(shape, k, v, pool, ws, dev_status=None, stream=None):
+    """k, v: bf16 [L, H, T, d]; pool, ws: uint8 device buffers (ws zeroed
+    before its first use, e.g. torch.zeros); dev_status: int32 device
+    tensor of 1 element or None."""
+    n = _kv_numel(shape)
+    args = (_want(k, torch.bfloat16, n, "k"), _want(v, torch.bfloat16, n, "v"),
+            _want(pool, torch.uint8, None, "pool"))
+    wsp, st = _want(ws, torch.uint8, None, "ws"), _opt(dev_status, torch.int32, 1, "dev_status")
+    _check(_lib.kvpool_encode(ctypes.byref(_shape(shape)), *args, _nbytes(pool), wsp, _nbytes(ws), st,
+                              _stream(stream)), "kvpool_encode")
 
 
-def kvpool_encode_noalloc(shape, k, v, pool, stream=None):
+def kvpool_encode_noalloc(shape, k, v, pool, dev_status=None, stream=None):
     """kvpool_encode with the library's own per-GPU scratch as workspace
     (no allocation anywhere in the call)."""
-    _check(_lib.kvpool_encode_noalloc(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(pool), _nbytes(pool),
-                                      _stream(stream)), "kvpool_encode_noalloc")
+    n = _kv_numel(shape)
+    args = (_want(k, torch.bfloat16, n, "k"), _want(v, torch.bfloat16, n, "v"),
+            _want(pool, torch.uint8, None, "pool"))
+    _check(_lib.kvpool_encode_noalloc(ctypes.byref(_shape(shape)), *args, _nbytes(pool),
+                                      _opt(dev_status, torch.int32, 1, "dev_status"), _stream(stream)),
+           "kvpool_encode_noalloc")
 
 
 def kvpool_decode(shape, pool, layer_begin, layer_end, k_outs, v_outs, dev_status=None, stream=None):
@@ -162,12 +194,14 @@ def kvpool_decode(shape, pool, layer_begin, layer_end, k_outs, v_outs, dev_statu
     n = len(k_outs)
     if len(v_outs) != n:
         raise ValueError("k_outs and v_outs must have the same length")
+    m = _kv_numel(shape, max(int(layer_end) - int(layer_begin), 0))
+    for i, t in enumerate(list(k_outs) + list(v_outs)):
+        _want(t, torch.bfloat16, m, f"decode output {i}")
     karr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in k_outs])
     varr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in v_outs])
-    for t in list(k_outs) + list(v_outs):
-        _ptr(t)
-    _check(_lib.kvpool_decode(ctypes.byref(_shape(shape)), _ptr(pool), _nbytes(pool), int(layer_begin),
-                              int(layer_end), karr, varr, n, _ptr(dev_status), _stream(stream)),
+    _check(_lib.kvpool_decode(ctypes.byref(_shape(shape)), _want(pool, torch.uint8, None, "pool"), _nbytes(pool),
+                              int(layer_begin), int(layer_end), karr, varr, n,
+                              _opt(dev_status, torch.int32, 1, "dev_status"), _stream(stream)),
            "kvpool_decode")
 
 
@@ -198,15 +232,25 @@ def cachecard_pack(shape, k, v, widths, card, ws, model_id=b"", position_offset=
     mid = model_id.encode() if isinstance(model_id, str) else bytes(model_id)
     meta.model_id = mid[:63]
     meta.position_offset = int(position_offset)
-    _check(_lib.cachecard_pack(ctypes.byref(_shape(shape)), _ptr(k), _ptr(v), _ptr(widths), ctypes.byref(meta),
-                               _ptr(card), _nbytes(card), _ptr(dev_card_bytes), _ptr(dev_status), _ptr(ws),
+    n = _kv_numel(shape)
+    args = (_want(k, torch.bfloat16, n, "k"), _want(v, torch.bfloat16, n, "v"),
+            _want(widths, torch.uint8, int(shape[2]), "widths"))
+    _check(_lib.cachecard_pack(ctypes.byref(_shape(shape)), *args, ctypes.byref(meta),
+                               _want(card, torch.uint8, None, "card"), _nbytes(card),
+                               _opt(dev_card_bytes, torch.int64, 1, "dev_card_bytes"),
+                               _opt(dev_status, torch.int32, 1, "dev_status"), _want(ws, torch.uint8, None, "ws"),
                                _nbytes(ws), _stream(stream)), "cachecard_pack")
 
 
 def cachecard_unpack(shape, card, k_out, v_out, ws, card_bytes=None, dev_status=None, stream=None):
     n = _nbytes(card) if card_bytes is None else int(card_bytes)
-    _check(_lib.cachecard_unpack(ctypes.byref(_shape(shape)), _ptr(card), n, _ptr(k_out), _ptr(v_out),
-                                 _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_unpack")
+    if n > _nbytes(card):
+        raise ValueError("card_bytes exceeds the card tensor")
+    m = _kv_numel(shape)
+    _check(_lib.cachecard_unpack(ctypes.byref(_shape(shape)), _want(card, torch.uint8, None, "card"), n,
+                                 _want(k_out, torch.bfloat16, m, "k_out"), _want(v_out, torch.bfloat16, m, "v_out"),
+                                 _opt(dev_status, torch.int32, 1, "dev_status"), _want(ws, torch.uint8, None, "ws"),
+                                 _nbytes(ws), _stream(stream)), "cachecard_unpack")
 
 
 def cachecard_transcode_workspace_bytes(shape):
@@ -218,9 +262,15 @@ def cachecard_transcode(shape, card_in, new_widths, card_out, ws, card_in_bytes=
     """card_in, card_out, ws: uint8 device buffers; new_widths: uint8 [T]
     device tensor; dev_card_bytes: int64 device tensor of 1 element or None."""
     n = _nbytes(card_in) if card_in_bytes is None else int(card_in_bytes)
-    _check(_lib.cachecard_transcode(ctypes.byref(_shape(shape)), _ptr(card_in), n, _ptr(new_widths),
-                                    _ptr(card_out), _nbytes(card_out), _ptr(dev_card_bytes), _ptr(dev_status),
-                                    _ptr(ws), _nbytes(ws), _stream(stream)), "cachecard_transcode")
+    if n > _nbytes(card_in):
+        raise ValueError("card_in_bytes exceeds the card_in tensor")
+    _check(_lib.cachecard_transcode(ctypes.byref(_shape(shape)), _want(card_in, torch.uint8, None, "card_in"), n,
+                                    _want(new_widths, torch.uint8, int(shape[2]), "new_widths"),
+                                    _want(card_out, torch.uint8, None, "card_out"), _nbytes(card_out),
+                                    _opt(dev_card_bytes, torch.int64, 1, "dev_card_bytes"),
+                                    _opt(dev_status, torch.int32, 1, "dev_status"),
+                                    _want(ws, torch.uint8, None, "ws"), _nbytes(ws), _stream(stream)),
+           "cachecard_transcode")
 
 
 KVC_ROPE_HALVES, KVC_ROPE_ADJACENT = 0, 1
@@ -232,6 +282,9 @@ def kvc_realign_keys(shape, k_in, k_out, delta, inv_freq, pairing=KVC_ROPE_HALVE
     f = np.ascontiguousarray(inv_freq, np.float32)
     if f.size != shape[3] // 2:
         raise ValueError("inv_freq must hold d/2 values")
+    n = _kv_numel(shape)
+    _want(k_in, torch.bfloat16, n, "k_in")
+    _want(k_out, torch.bfloat16, n, "k_out")
     _check(_lib.kvc_realign_keys(ctypes.byref(_shape(shape)), _ptr(k_in), _ptr(k_out), int(delta),
                                  f.ctypes.data_as(ctypes.c_void_p), int(pairing), _stream(stream)),
            "kvc_realign_keys")
@@ -241,6 +294,13 @@ def kvc_lowrank_materialize(shape, rank, n_anchors, src, a, r, weights, out, str
     """src, out: bf16 device tensors [L, H, T, d] (the same tensor for in
     place); a: bf16 [L, V, T, rank]; r: bf16 [L, V, H*d, rank]; weights:
     float32 device tensor [L, V]."""
+    L, H, T, d = (int(x) for x in shape)
+    V, r_ = int(n_anchors), int(rank)
+    _want(src, torch.bfloat16, _kv_numel(shape), "src")
+    _want(out, torch.bfloat16, _kv_numel(shape), "out")
+    _want(a, torch.bfloat16, L * V * T * r_, "a")
+    _want(r, torch.bfloat16, L * V * H * d * r_, "r")
+    _want(weights, torch.float32, L * V, "weights")
     _check(_lib.kvc_lowrank_materialize(ctypes.byref(_shape(shape)), int(rank), int(n_anchors), _ptr(src),
                                         _ptr(a), _ptr(r), _ptr(weights), _ptr(out), _stream(stream)),
            "kvc_lowrank_materialize")
@@ -274,6 +334,12 @@ def kvc_lowrank_factor(shape, rank, z, omega, a_out, r_out, ws, a_stride=None, r
             raise ValueError("expected a [L, rows, rank] view with contiguous rows")
         return ctypes.c_void_p(t.data_ptr())
 
+    _want(z, torch.bfloat16, _kv_numel(shape), "z")
+    _want(omega, torch.float32, H * d * LOWRANK_SKETCH, "omega")
+    _want(ws, torch.uint8, None, "ws")
+    _opt(sigma_out, torch.float32, L * rank, "sigma_out")
+    if a_out.dtype != torch.bfloat16 or r_out.dtype != torch.bfloat16:
+        raise ValueError("a_out and r_out must be bfloat16")
     a_ptr, r_ptr = base(a_out, T), base(r_out, H * d)
     if L > 1 and (a_out.stride(0) != a_stride or r_out.stride(0) != r_stride):
         raise ValueError("layer strides of the views differ from a_stride / r_stride")

@@ -83,7 +83,8 @@ enum {
 enum {
     KVC_DEV_BAD_HEADER = 1, /* pool/card header does not match the shape */
     KVC_DEV_BAD_WIDTH = 2,  /* a token width is not 2, 4, 8 or 16 */
-    KVC_DEV_CAPACITY = 4    /* the card does not fit card_capacity */
+    KVC_DEV_CAPACITY = 4,   /* the card does not fit card_capacity */
+    KVC_DEV_ENCODE_TIMEOUT = 8 /* an internal wait of the encode gave up */
 };
 
 #define KVC_MAX_AGENTS 64
@@ -103,7 +104,12 @@ enum {
  * Payload ratio against bf16 K+V: 16 / 5.5 (PolyKV 2.B, compression ratio). */
 size_t kvpool_bytes(const kvc_shape* shape);
 
-/* Workspace bytes needed by kvpool_encode (per-layer reductions). */
+/* Workspace bytes needed by kvpool_encode (per-layer reductions). The
+ * workspace must hold zeros before its first encode (e.g. one hipMemset
+ * after allocation) and must not be written by anything else afterwards;
+ * it then serves any number of encodes in sequence, of any shapes, with no
+ * clearing in between (each call tags the words it writes with a number of
+ * its own, and ignores words that carry another). */
 size_t kvpool_workspace_bytes(const kvc_shape* shape);
 
 /* Compress bf16 K and V ([L][H][T][d]) into `pool` (PolyKV 2.B items 1-2).
@@ -111,8 +117,16 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape);
  *   pool       device, >= kvpool_bytes(shape), 256-byte aligned; fully written
  *              (header, sections and zero padding)
  *   ws         device workspace of >= kvpool_workspace_bytes(shape) bytes,
- *              16-byte aligned; clobbered
+ *              16-byte aligned, zeroed before its first use (see above)
+ *   dev_status device int32 or NULL: KVC_DEV_ENCODE_TIMEOUT if an internal
+ *              wait gave up (never expected); the pool's magic word is then
+ *              zero and decode refuses it
  * Keys: m_l = max |K[l]| over the layer; codes clamp(rint(x*(127/m_l))).
+ * Inputs are expected finite. The maximum is taken on the bf16 bit patterns
+ * with the sign cleared (NaN ranks above Inf), so a layer holding an Inf or
+ * NaN key gets a NaN scale and all-zero codes (its keys decode to NaN); a
+ * value vector holding Inf or NaN gets the scale 65504 and codes from the
+ * comparisons of its (non-finite) rotated coordinates (NaN: code 0).
  * Values: per vector, s = fp16(sqrt(sum x^2 / d)), y = H x (Sylvester
  * order), z = y / (sqrt(d) s), code = number of Lloyd-Max thresholds <= z.
  * Execution: where a round of whole layers fits the LDS of one workgroup per
@@ -121,13 +135,13 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape);
  * launch: a workgroup that has not received every other workgroup's key
  * maximum for a layer within a bound (200 us by default; environment
  * variable KVC_ENCODE_POLL_US, read at each call, 0 = always) reads the
- * layer's keys itself. The pool is the same either way; only the time
- * differs. A pool whose encode hit an internal wait limit (never expected)
- * has a zero magic word and is refused by decode.
+ * layer's keys itself (values above 5000 are ignored). The pool is the
+ * same either way; only the time differs.
  * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
  * KVC_E_HIP. */
 int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* pool,
-                  size_t pool_bytes, void* ws, size_t ws_bytes, hipStream_t stream);
+                  size_t pool_bytes, void* ws, size_t ws_bytes, int32_t* dev_status,
+                  hipStream_t stream);
 
 /* kvpool_encode without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory (code under HIP graph
@@ -138,12 +152,12 @@ int kvpool_encode(const kvc_shape* shape, const void* k, const void* v, void* po
  * 1 MiB (more than 255 layers) are refused with KVC_E_SCRATCH. Every call on
  * a GPU uses that GPU's one array, so calls that overlap in time on one GPU
  * (other streams, other threads) race and must not be issued; calls in
- * sequence on one stream are fine. Each call clears the part of the array
- * it uses before its encode kernel. Arguments, output and the remaining
- * errors are those of kvpool_encode (without the workspace checks); the
- * pool is byte-identical to kvpool_encode's. */
+ * sequence on one stream are fine. The array is zero when the library is
+ * loaded and needs no clearing between calls. Arguments, output, status bits and the
+ * remaining errors are those of kvpool_encode (without the workspace
+ * checks); the pool is byte-identical to kvpool_encode's. */
 int kvpool_encode_noalloc(const kvc_shape* shape, const void* k, const void* v, void* pool,
-                          size_t pool_bytes, hipStream_t stream);
+                          size_t pool_bytes, int32_t* dev_status, hipStream_t stream);
 
 /* Decompress layers [layer_begin, layer_end) of `pool` into the caches of
  * n_out agents (PolyKV 2.A, PooledAgent: layer-wise injection into each
@@ -196,6 +210,7 @@ size_t cachecard_workspace_bytes(const kvc_shape* shape);
  *   card            device, card_capacity bytes, 256-byte aligned
  *   dev_card_bytes  device u64 or NULL; receives the card's exact size
  *   dev_status      device int32 or NULL; KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY
+ *                   (then the card's magic word is zero and unpack refuses it)
  *   ws              device workspace, >= cachecard_workspace_bytes(shape)
  * Per group of 32 channels at width b < 16: mn, mx = group min and max,
  * s = fp16((mx - mn) / (2^b - 1)), q = min(rint((x - mn) / s), 2^b - 1).
@@ -237,7 +252,8 @@ size_t cachecard_transcode_workspace_bytes(const kvc_shape* shape);
  *   dev_card_bytes  device u64 or NULL; receives card_out's exact size
  *   dev_status      device int32 or NULL; KVC_DEV_BAD_HEADER (card_in),
  *                   KVC_DEV_BAD_WIDTH (either card), KVC_DEV_CAPACITY; on a
- *                   nonzero status card_out's payload is unspecified
+ *                   nonzero status card_out's magic word is zero (unpack and
+ *                   later hops refuse it) and the rest is unspecified
  *   ws              device workspace, >= cachecard_transcode_workspace_bytes
  * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
  * KVC_E_HIP. */

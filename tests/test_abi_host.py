@@ -111,10 +111,10 @@ A = 1 << 40  # fake, 256-aligned addresses far apart
 KVB = 2 * 2 * 32 * 128 * 2
 
 
-def _enc(shape=S, k=A, v=2 * A, pool=3 * A, pool_bytes=None, ws=4 * A, ws_bytes=None):
+def _enc(shape=S, k=A, v=2 * A, pool=3 * A, pool_bytes=None, ws=4 * A, ws_bytes=None, status=None):
     pb = kv.kvpool_bytes(shape or S) if pool_bytes is None else pool_bytes
     wb = kv.kvpool_workspace_bytes(shape or S) if ws_bytes is None else ws_bytes
-    return L.kvpool_encode(ctypes.byref(shape) if shape is not None else None, k, v, pool, pb, ws, wb, None)
+    return L.kvpool_encode(ctypes.byref(shape) if shape is not None else None, k, v, pool, pb, ws, wb, status, None)
 
 
 @fake_addresses
@@ -130,11 +130,15 @@ def test_encode_argument_errors():
     assert _enc(pool=3 * A + 16) == kv.KVC_E_ALIGN
     assert _enc(pool=A + KVB - 256) == kv.KVC_E_ALIAS       # pool overlaps k
     assert _enc(ws=3 * A + 256) == kv.KVC_E_ALIAS            # ws inside pool
+    assert _enc(status=4 * A + 2) == kv.KVC_E_ALIGN
+    assert _enc(status=4 * A + 64) == kv.KVC_E_ALIAS         # status inside ws
+    assert _enc(status=A + 64) == kv.KVC_E_ALIAS             # status inside k
 
 
-def _enc_noalloc(shape=S, k=A, v=2 * A, pool=3 * A, pool_bytes=None):
+def _enc_noalloc(shape=S, k=A, v=2 * A, pool=3 * A, pool_bytes=None, status=None):
     pb = kv.kvpool_bytes(shape or S) if pool_bytes is None else pool_bytes
-    return L.kvpool_encode_noalloc(ctypes.byref(shape) if shape is not None else None, k, v, pool, pb, None)
+    return L.kvpool_encode_noalloc(ctypes.byref(shape) if shape is not None else None, k, v, pool, pb, status,
+                                   None)
 
 
 @fake_addresses
@@ -153,6 +157,8 @@ def test_encode_noalloc_argument_errors():
     assert _enc_noalloc(k=A + 8) == kv.KVC_E_ALIGN
     assert _enc_noalloc(pool=3 * A + 16) == kv.KVC_E_ALIGN
     assert _enc_noalloc(pool=A + KVB - 256) == kv.KVC_E_ALIAS   # pool overlaps k
+    assert _enc_noalloc(status=5 * A + 1) == kv.KVC_E_ALIGN
+    assert _enc_noalloc(status=3 * A + 512) == kv.KVC_E_ALIAS   # status inside the pool
 
 
 def _dec(l0=0, l1=2, n=2, outs=None, pool=3 * A, pool_bytes=None, status=None):

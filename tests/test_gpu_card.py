@@ -104,7 +104,8 @@ def test_bad_width_is_reported():
     widths[7] = 5
     card, n, st = gpu_pack(shape, k, v, widths)
     assert st & kv.KVC_DEV_BAD_WIDTH
-    assert torch.all(card == 0xA5)     # nothing written
+    # nothing written but a zero magic word (a stale card cannot pass)
+    assert int(card[:4].view(torch.int32).item()) == 0 and torch.all(card[4:] == 0xA5)
 
 
 def test_small_capacity_is_reported_with_needed_size():
@@ -114,7 +115,7 @@ def test_small_capacity_is_reported_with_needed_size():
     need = kv.cachecard_bytes_host(shape, widths)
     card, n, st = gpu_pack(shape, k, v, widths, capacity=need - 256)
     assert st == kv.KVC_DEV_CAPACITY and n == need
-    assert torch.all(card == 0xA5)
+    assert int(card[:4].view(torch.int32).item()) == 0 and torch.all(card[4:] == 0xA5)
 
 
 def test_unpack_rejects_bad_header_and_widths():
@@ -209,13 +210,47 @@ def test_transcode_reports_errors():
     good = np.full(20, 8, np.uint8)
     bad = src.copy()
     bad[0] = 0
-    _, _, st = gpu_transcode(shape, torch.from_numpy(bad).to(DEV), src.size, good)
+    out, n, st = gpu_transcode(shape, torch.from_numpy(bad).to(DEV), src.size, good)
     assert st & kv.KVC_DEV_BAD_HEADER
+    _assert_refused_by_unpack(shape, out, n)
     w = good.copy()
     w[5] = 3
-    _, _, st = gpu_transcode(shape, torch.from_numpy(src).to(DEV), src.size, w)
+    out, n, st = gpu_transcode(shape, torch.from_numpy(src).to(DEV), src.size, w)
     assert st & kv.KVC_DEV_BAD_WIDTH
+    assert int(out[:4].view(torch.int32).item()) == 0
     need = kv.cachecard_bytes_host(shape, good)
     out, n, st = gpu_transcode(shape, torch.from_numpy(src).to(DEV), src.size, good, capacity=need - 256)
     assert st == kv.KVC_DEV_CAPACITY and n == need
-    assert torch.all(out == 0xA5)
+    assert int(out[:4].view(torch.int32).item()) == 0 and torch.all(out[4:] == 0xA5)
+
+
+def _assert_refused_by_unpack(shape, card, n):
+    """unpack refuses a card whose transcode was refused (zero magic word)."""
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ko = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    vo = torch.empty_like(ko)
+    ws = dev_bytes(kv.cachecard_workspace_bytes(shape))
+    kv.cachecard_unpack(shape, card, ko, vo, ws, card_bytes=min(n, card.numel()), dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & kv.KVC_DEV_BAD_HEADER
+
+
+def test_transcode_output_after_refused_input_is_refused():
+    """A card_out that held a valid card before: a transcode whose input is
+    refused must not leave it looking valid."""
+    shape = (1, 2, 20, 64)
+    k, v = synth.kv_bits(synth.WORKLOADS[4], 0, shape=shape)
+    widths = np.full(20, 8, np.uint8)
+    src = oracle.card_pack(k, v, np.full(20, 4, np.uint8))
+    prev = oracle.card_pack(k, v, widths)
+    bad = src.copy()
+    bad[8] ^= 1  # layer count
+    card_in = torch.from_numpy(bad).to(DEV)
+    out = torch.from_numpy(prev.copy()).to(DEV)
+    ws = dev_bytes(kv.cachecard_transcode_workspace_bytes(shape))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.cachecard_transcode(shape, card_in, torch.from_numpy(widths).to(DEV), out, ws, card_in_bytes=bad.size,
+                           dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & kv.KVC_DEV_BAD_HEADER
+    _assert_refused_by_unpack(shape, out, prev.size)

@@ -23,11 +23,13 @@ def _pool_both_ways(shape, cfg, seed):
     k, v = synth.kv_bits(synth.WORKLOADS[cfg], seed, shape=shape)
     kd, vd = to_dev(k), to_dev(v)
     ref = dev_bytes(kv.kvpool_bytes(shape), fill=0xA5)
-    ws = dev_bytes(kv.kvpool_workspace_bytes(shape), fill=0x5A)
+    ws = dev_bytes(kv.kvpool_workspace_bytes(shape), fill=0)
     kv.kvpool_encode(shape, kd, vd, ref, ws)
     got = dev_bytes(kv.kvpool_bytes(shape), fill=0x3C)
-    kv.kvpool_encode_noalloc(shape, kd, vd, got)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kvpool_encode_noalloc(shape, kd, vd, got, status)
     torch.cuda.synchronize()
+    assert int(status.item()) == 0
     return got.cpu().numpy(), ref.cpu().numpy()
 
 
