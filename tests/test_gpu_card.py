@@ -81,11 +81,14 @@ def assert_bits_equal(got, want, what):
                              f"got {got.flat[idx[0]]:#06x} want {want.flat[idx[0]]:#06x}")
 
 
-def test_full_size_cachecard_workload():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_full_size_cachecard_workload(seed):
+    """The Llama-3.1-8B 8K card (seeds 0-2: values and width runs): pack
+    byte-exact, unpack bit-exact against the oracle."""
     w = synth.WORKLOADS[4]
-    say("full-size card workload", w.name)
-    k, v = synth.kv_bits(w, 0)
-    widths = synth.card_widths(w, 0)
+    say("full-size card workload", w.name, "seed", seed)
+    k, v = synth.kv_bits(w, seed)
+    widths = synth.card_widths(w, seed)
     card, n, st = gpu_pack(w.shape, k, v, widths, pos=4096)
     ref = oracle.card_pack(k, v, widths, b"llama-3.1-8b", 4096)
     assert st == 0 and n == ref.size == kv.cachecard_bytes_host(w.shape, widths)

@@ -5,9 +5,9 @@ The GPU runs the randomized range finder with one power iteration on a
 48-column Gaussian sketch, so it reaches the exact truncated SVD only up to
 the sketch's approximation error, which is small where the spectrum has a
 gap at 32. Bounds used (from the algorithm and the bf16 storage of the
-factors; the sketch error is checked empirically by a float64 mirror of the
-algorithm on the same inputs, and is below 1e-4 relative wherever
-sigma_32 / sigma_33 >= 3):
+factors; the float64 mirror of the algorithm in
+tests/test_lowrank_factor_bounds.py runs on the same inputs and meets the
+gapped bounds with a factor of 4 or more to spare):
   - residual: ||Z - A R^T||_F <= 1.02 ||Z - A_o R_o^T||_F (+ 2^-12 ||Z||_F
     for the rounding of binary32 products), for every input;
   - with a gap: every singular value within 2e-3 sigma_1 of the exact one,
