@@ -15,9 +15,11 @@
 //
 // orth() is CholeskyQR (Gram matrix and Cholesky factor in binary64, a
 // pivot at or below 1e-12 of the largest diagonal drops its column), once
-// inside the power iteration and twice for the final Q, the products with Z run in binary32 on the vector units (Z is
-// bf16, exact in binary32), and the 48 x 48 eigenproblem is solved by
-// parallel cyclic Jacobi in binary64. A and R are rounded once to bf16.
+// inside the power iteration and twice for the final Q; the products with Z
+// run on the matrix cores (Z is bf16; the binary32 operand enters as two
+// bf16 parts, binary32 accumulation), and the 48 x 48 eigenproblem is
+// solved by parallel cyclic Jacobi in binary64. A and R are rounded once to
+// bf16.
 //
 // Z is a matrix view of the cache layout: row t, column h*d + c of matrix m
 // is element [m][h][t][c] of a bf16 [M][H][T][d] tensor.
@@ -29,7 +31,7 @@ namespace {
 
 constexpr int kFK = kLowrankSketch;  // 48 sketch columns
 constexpr int kFR = 32;              // rank
-constexpr int kFChunk = 256;         // tokens per partial product of Z^T Q
+constexpr int kFChunk = 1024;        // tokens per partial product of Z^T Q
 constexpr int kFThreads = 256;
 constexpr int kFSweeps = 16;         // Jacobi sweep limit
 // The small eigenproblem's workgroup: a Jacobi step is a chain of two
@@ -38,107 +40,215 @@ constexpr int kFSweeps = 16;         // Jacobi sweep limit
 // not fill the chip in any case.
 constexpr int kSvdThreads = 1024;
 
-// Y[m](t, :) = Z[m](t, :) X[m]; X is D x 48 row-major binary32, x_stride
-// elements apart per matrix (0: one X for all). Block: 64 tokens x 4 waves
-// of 12 columns; the rows of X for one head at a time pass through LDS.
+typedef __bf16 fbf16x8 __attribute__((ext_vector_type(8)));
+typedef float ff32x4 __attribute__((ext_vector_type(4)));
+
+// A binary32 operand of the matrix-core products as two bf16 parts: hi =
+// bf16(x) (nearest, ties to even) and lo = bf16(x - hi) (x - hi is exact),
+// so hi + lo is within 2^-17 |x| of x; a product Z (hi + lo) is two matrix
+// instructions accumulating in binary32. Z itself is bf16 and exact.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ ff32x4 mfma_bf16(const uint4& a, const uint4& b, ff32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fbf16x8, a), __builtin_bit_cast(fbf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row l % 16 of A
+// and column l % 16 of B, each with k = 8 (l / 16) .. 8 (l / 16) + 7, and
+// receives rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16 of the result.
+
+// Y[m](t, :) = Z[m](t, :) X[m] on the matrix cores; X is D x 48 row-major
+// binary32, x_stride elements apart per matrix (0: one X for all). Block:
+// 256 tokens, wave w rows 64 w .. 64 w + 63 (four 16-row tiles) by all 48
+// columns (three tiles). The contraction runs over the channels, which are
+// contiguous in Z: A fragments are 16-byte loads straight from memory. The
+// rows of X for one head pass through LDS as bf16 B fragments (hi and lo).
 template <int D>
 __global__ __launch_bounds__(kFThreads) void fac_zx_kernel(const uint16_t* z, const float* x, uint64_t x_stride,
                                                            float* y, uint32_t H, uint32_t T) {
-    __shared__ float4 xs[D * kFK / 4];
+    constexpr int KS = D / 32;  // k-steps per head
+    __shared__ uint4 xb[2][KS][3][kWave];
     const uint32_t m = blockIdx.y;
-    const uint32_t t = blockIdx.x * 64 + threadIdx.x % 64;
-    const uint32_t cg = wave_uniform(threadIdx.x / 64);  // columns 12 cg .. 12 cg + 11
-    const uint32_t tc = t < T ? t : T - 1;
+    const uint32_t lane = lane_id(), w = wave_uniform(threadIdx.x / kWave);
+    const uint32_t tb = blockIdx.x * 256 + w * 64;
     const uint16_t* zm = z + (uint64_t)m * H * T * D;
     const float* xm = x + (uint64_t)m * x_stride;
-    float acc[12];
+    ff32x4 acc[4][3];
 #pragma unroll
-    for (int j = 0; j < 12; ++j) acc[j] = 0.0f;
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct) acc[rt][ct] = ff32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's A fragments of head h: rows tb + 16 rt + lane % 16
+    // (clamped to the last token), channels 32 ks + 8 (lane / 16) ..
+    auto load_a = [&](uint32_t h, uint4 (&a)[KS][4]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                uint32_t t = tb + rt * 16 + lane % 16;
+                t = t < T ? t : T - 1;
+                a[ks][rt] = *reinterpret_cast<const uint4*>(zm + ((uint64_t)h * T + t) * D + ks * 32 + 8 * (lane / 16));
+            }
+    };
+    uint4 a[KS][4], an[KS][4];
+    load_a(0, an);
     for (uint32_t h = 0; h < H; ++h) {
-        __syncthreads();
-        const float4* xh = reinterpret_cast<const float4*>(xm + (uint64_t)h * D * kFK);
-        for (uint32_t i = threadIdx.x; i < D * kFK / 4; i += kFThreads) xs[i] = xh[i];
-        __syncthreads();
-        const uint4* zr = reinterpret_cast<const uint4*>(zm + ((uint64_t)h * T + tc) * D);
-        for (int q = 0; q < D / 8; ++q) {
-            const uint4 w = zr[q];
-            const float zz[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                                 bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float4* xr = xs + ((q * 8 + e) * kFK + cg * 12) / 4;
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int v = 0; v < 3; ++v) {
-                    const float4 xv = xr[v];
-                    acc[4 * v] = fmaf(zz[e], xv.x, acc[4 * v]);
-                    acc[4 * v + 1] = fmaf(zz[e], xv.y, acc[4 * v + 1]);
-                    acc[4 * v + 2] = fmaf(zz[e], xv.z, acc[4 * v + 2]);
-                    acc[4 * v + 3] = fmaf(zz[e], xv.w, acc[4 * v + 3]);
+            for (int rt = 0; rt < 4; ++rt) a[ks][rt] = an[ks][rt];
+        __syncthreads();
+        for (uint32_t f = threadIdx.x; f < (uint32_t)KS * 3 * kWave; f += kFThreads) {
+            const uint32_t ks = f / (3 * kWave), ct = (f / kWave) % 3, l = f % kWave;
+            const float* xr = xm + ((uint64_t)h * D + ks * 32 + 8 * (l / 16)) * kFK + ct * 16 + l % 16;
+            __bf16 hi[8], lo[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) split_bf16(xr[i * kFK], hi[i], lo[i]);
+            xb[0][ks][ct][l] = __builtin_bit_cast(uint4, hi);
+            xb[1][ks][ct][l] = __builtin_bit_cast(uint4, lo);
+        }
+        __syncthreads();
+        if (h + 1 < H) load_a(h + 1, an);  // the next head's rows, in flight during this head's products
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 bh[3], bl[3];
+#pragma unroll
+            for (int ct = 0; ct < 3; ++ct) {
+                bh[ct] = xb[0][ks][ct][lane];
+                bl[ct] = xb[1][ks][ct][lane];
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 3; ++ct) {
+                    acc[rt][ct] = mfma_bf16(a[ks][rt], bh[ct], acc[rt][ct]);
+                    acc[rt][ct] = mfma_bf16(a[ks][rt], bl[ct], acc[rt][ct]);
+                }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t t = tb + rt * 16 + 4 * (lane / 16) + e;
+            if (t < T) {
+                float* yr = y + ((uint64_t)m * T + t) * kFK + lane % 16;
+#pragma unroll
+                for (int ct = 0; ct < 3; ++ct) yr[ct * 16] = acc[rt][ct][e];
+            }
+        }
+}
+
+// Partial products P[m][chunk](h*d + c, :) = sum over the chunk's tokens t
+// of Z[m](t, h*d + c) Q[m](t, :), on the matrix cores. The contraction runs
+// over tokens, which are not contiguous in Z: a 128-token tile of the head
+// is staged in LDS as it lies ([t][c], coalesced) and each lane gathers its
+// A fragment (8 tokens of one channel) with 2-byte reads; the tile's rows of
+// Q pass through LDS as bf16 B fragments (hi and lo). Block: one chunk of
+// tokens of one head; wave w owns channel tiles w * D/64 .. of the head.
+constexpr int kZtqSub = 128;
+template <int D>
+__global__ __launch_bounds__(kFThreads) void fac_ztq_kernel(const uint16_t* z, const float* q, float* part,
+                                                            uint32_t H, uint32_t T, uint32_t nchunks) {
+    constexpr int CTW = D / 64;          // channel tiles per wave: 2 (d = 128) or 1 (d = 64)
+    constexpr int KS = kZtqSub / 32;     // k-steps per sub-tile
+    constexpr int ZR = D + 8;            // LDS row of the Z tile, in bf16 (16-byte multiple, spreads banks)
+    __shared__ __attribute__((aligned(16))) uint16_t zs[kZtqSub * ZR];
+    __shared__ uint4 qb[2][KS][3][kWave];
+    const uint32_t chunk = blockIdx.x, h = blockIdx.y % H, m = blockIdx.y / H;
+    const uint32_t lane = lane_id(), w = wave_uniform(threadIdx.x / kWave);
+    const uint32_t tbeg = chunk * kFChunk;
+    const uint32_t tend = (T - tbeg < (uint32_t)kFChunk) ? T : tbeg + kFChunk;
+    const uint16_t* zh = z + ((uint64_t)m * H + h) * T * D;
+    const float* qm = q + (uint64_t)m * T * kFK;
+    ff32x4 acc[CTW][3];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+        for (int jt = 0; jt < 3; ++jt) acc[c][jt] = ff32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // A sub-tile's share of each thread: ZN 16-byte pieces of the Z tile
+    // (piece i = threadIdx.x + 256 n: row i / (D/8), 8 channels) and QN
+    // B fragments' 8 values of Q (fragment f = threadIdx.x + 256 n), loaded
+    // into registers one sub-tile ahead, then placed in LDS.
+    constexpr int ZN = kZtqSub * D / 8 / kFThreads;
+    constexpr int QN = KS * 3 * kWave / kFThreads;
+    uint4 zr[ZN];
+    float qv[QN][8];
+    auto load_tile = [&](uint32_t t0) {
+        const uint32_t nt = (tend - t0 < (uint32_t)kZtqSub) ? tend - t0 : (uint32_t)kZtqSub;
+#pragma unroll
+        for (int n = 0; n < ZN; ++n) {
+            const uint32_t i = threadIdx.x + n * kFThreads, r = i / (D / 8), c8 = i % (D / 8);
+            zr[n] = r < nt ? *reinterpret_cast<const uint4*>(zh + (uint64_t)(t0 + r) * D + c8 * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < QN; ++n) {
+            const uint32_t f = threadIdx.x + n * kFThreads;
+            const uint32_t ks = f / (3 * kWave), jt = (f / kWave) % 3, l = f % kWave;
+            const uint32_t tr = ks * 32 + 8 * (l / 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                qv[n][i] = tr + i < nt ? qm[(uint64_t)(t0 + tr + i) * kFK + jt * 16 + l % 16] : 0.0f;
+        }
+    };
+    load_tile(tbeg);
+    for (uint32_t t0 = tbeg; t0 < tend; t0 += kZtqSub) {
+        __syncthreads();  // the previous sub-tile's LDS reads are done
+#pragma unroll
+        for (int n = 0; n < ZN; ++n) {
+            const uint32_t i = threadIdx.x + n * kFThreads, r = i / (D / 8), c8 = i % (D / 8);
+            *reinterpret_cast<uint4*>(zs + r * ZR + c8 * 8) = zr[n];
+        }
+#pragma unroll
+        for (int n = 0; n < QN; ++n) {
+            const uint32_t f = threadIdx.x + n * kFThreads;
+            const uint32_t ks = f / (3 * kWave), jt = (f / kWave) % 3, l = f % kWave;
+            __bf16 hi[8], lo[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) split_bf16(qv[n][i], hi[i], lo[i]);
+            qb[0][ks][jt][l] = __builtin_bit_cast(uint4, hi);
+            qb[1][ks][jt][l] = __builtin_bit_cast(uint4, lo);
+        }
+        __syncthreads();
+        if (t0 + kZtqSub < tend) load_tile(t0 + kZtqSub);  // in flight during this sub-tile's products
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 bh[3], bl[3];
+#pragma unroll
+            for (int jt = 0; jt < 3; ++jt) {
+                bh[jt] = qb[0][ks][jt][lane];
+                bl[jt] = qb[1][ks][jt][lane];
+            }
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+                const uint32_t ch = (w * CTW + c) * 16 + lane % 16;
+                const uint16_t* col = zs + (ks * 32 + 8 * (lane / 16)) * ZR + ch;
+                uint16_t av[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) av[i] = col[i * ZR];
+                const uint4 a = __builtin_bit_cast(uint4, av);
+#pragma unroll
+                for (int jt = 0; jt < 3; ++jt) {
+                    acc[c][jt] = mfma_bf16(a, bh[jt], acc[c][jt]);
+                    acc[c][jt] = mfma_bf16(a, bl[jt], acc[c][jt]);
                 }
             }
         }
     }
-    if (t < T) {
-        float4* yr = reinterpret_cast<float4*>(y + ((uint64_t)m * T + t) * kFK + cg * 12);
+    float* pm = part + (((uint64_t)m * nchunks + chunk) * H + h) * (uint64_t)D * kFK;
 #pragma unroll
-        for (int v = 0; v < 3; ++v) yr[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
-    }
-}
-
-// Partial products P[m][chunk](h*d + c, :) = sum over the chunk's tokens t
-// of Z[m](t, h*d + c) Q[m](t, :). Block: one chunk of one head; thread c of
-// each group of d threads takes one channel and 48/G columns.
-template <int D>
-__global__ __launch_bounds__(kFThreads) void fac_ztq_kernel(const uint16_t* z, const float* q, float* part,
-                                                            uint32_t H, uint32_t T, uint32_t nchunks) {
-    constexpr int G = kFThreads / D;  // column groups: 2 (d = 128) or 4 (d = 64)
-    constexpr int CW = kFK / G;       // 24 or 12 columns per thread
-    __shared__ float4 qs[kFChunk * kFK / 4];
-    const uint32_t chunk = blockIdx.x, h = blockIdx.y % H, m = blockIdx.y / H;
-    const uint32_t c = threadIdx.x % D, g = wave_uniform(threadIdx.x / D);
-    const uint32_t t0 = chunk * kFChunk;
-    const uint32_t nt = (T - t0 < (uint32_t)kFChunk) ? T - t0 : (uint32_t)kFChunk;
-    const float4* qm = reinterpret_cast<const float4*>(q + ((uint64_t)m * T + t0) * kFK);
-    for (uint32_t i = threadIdx.x; i < nt * kFK / 4; i += kFThreads) qs[i] = qm[i];
-    __syncthreads();
-    const uint16_t* zm = z + (((uint64_t)m * H + h) * T + t0) * D + c;
-    float acc[CW];
+    for (int c = 0; c < CTW; ++c)
 #pragma unroll
-    for (int j = 0; j < CW; ++j) acc[j] = 0.0f;
-    uint32_t t = 0;
-    for (; t + 8 <= nt; t += 8) {
-        float zz[8];
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t ch = (w * CTW + c) * 16 + 4 * (lane / 16) + e;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) zz[u] = __uint_as_float((uint32_t)zm[(uint64_t)(t + u) * D] << 16);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float4* qr = qs + ((t + u) * kFK + g * CW) / 4;
-#pragma unroll
-            for (int v = 0; v < CW / 4; ++v) {
-                const float4 qv = qr[v];
-                acc[4 * v] = fmaf(zz[u], qv.x, acc[4 * v]);
-                acc[4 * v + 1] = fmaf(zz[u], qv.y, acc[4 * v + 1]);
-                acc[4 * v + 2] = fmaf(zz[u], qv.z, acc[4 * v + 2]);
-                acc[4 * v + 3] = fmaf(zz[u], qv.w, acc[4 * v + 3]);
-            }
+            for (int jt = 0; jt < 3; ++jt) pm[(uint64_t)ch * kFK + jt * 16 + lane % 16] = acc[c][jt][e];
         }
-    }
-    for (; t < nt; ++t) {
-        const float zz = __uint_as_float((uint32_t)zm[(uint64_t)t * D] << 16);
-        const float4* qr = qs + (t * kFK + g * CW) / 4;
-#pragma unroll
-        for (int v = 0; v < CW / 4; ++v) {
-            const float4 qv = qr[v];
-            acc[4 * v] = fmaf(zz, qv.x, acc[4 * v]);
-            acc[4 * v + 1] = fmaf(zz, qv.y, acc[4 * v + 1]);
-            acc[4 * v + 2] = fmaf(zz, qv.z, acc[4 * v + 2]);
-            acc[4 * v + 3] = fmaf(zz, qv.w, acc[4 * v + 3]);
-        }
-    }
-    float4* pr = reinterpret_cast<float4*>(part + (((uint64_t)m * nchunks + chunk) * ((uint64_t)H * D) +
-                                                   (uint64_t)h * D + c) * kFK + g * CW);
-#pragma unroll
-    for (int v = 0; v < CW / 4; ++v) pr[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
 }
 
 // W[m] = sum over chunks of P[m][chunk], chunks in order.
@@ -154,58 +264,72 @@ __global__ __launch_bounds__(kFThreads) void fac_reduce_kernel(const float* part
 }
 
 // Partial Gram matrices: Gp[m][chunk] = Y_chunk^T Y_chunk (48 x 48,
-// binary64) over chunks of 256 rows, one block per (chunk, matrix); the
-// chunk's rows pass through LDS and each thread owns a 3 x 3 tile of the
-// upper triangle of tiles.
-constexpr int kGRows = 256;
-constexpr int kGTile = 3;
-constexpr int kGTiles = kFK / kGTile;                    // 16 tiles per side
-constexpr int kGTilePairs = kGTiles * (kGTiles + 1) / 2;  // 136
+// binary64) over chunks of kGChunk rows, one block per (chunk, matrix), on
+// the matrix cores in binary64 (v_mfma_f64_16x16x4_f64: lane l supplies
+// A(l % 16, l / 16) and B(l / 16, l % 16), one double each, and its result
+// entry e is row l / 16 + 4 e of column l % 16 - measured on the GPU with a
+// probe whose entries encode their own row and column). With
+// A = Y^T and B = Y both operands of a k-step are 4 rows of Y, lane l
+// reading 16 consecutive columns of row l / 16; the six tiles (a, b), a <= b,
+// of the 3 x 3 tiling are accumulated. Wave w takes the k-steps of rows
+// 4 w + 16 s .. + 3; the four waves' sums are added in LDS, in wave order,
+// and the block writes the full symmetric matrix.
+constexpr int kGChunk = 256;
+
+typedef double fd4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kFThreads) void fac_gram_partial_kernel(const float* y, uint32_t N, uint32_t nchunks,
                                                                      double* gpart) {
-    __shared__ float4 ys[kGRows * kFK / 4];
+    __shared__ double red[kFThreads / kWave][6][kWave][4];
     const uint32_t chunk = blockIdx.x, m = blockIdx.y;
-    const uint32_t r0 = chunk * kGRows;
-    const uint32_t nr = (N - r0 < (uint32_t)kGRows) ? N - r0 : (uint32_t)kGRows;
-    const float4* src = reinterpret_cast<const float4*>(y + ((uint64_t)m * N + r0) * kFK);
-    for (uint32_t i = threadIdx.x; i < nr * kFK / 4; i += kFThreads) ys[i] = src[i];
+    const uint32_t lane = lane_id(), w = wave_uniform(threadIdx.x / kWave);
+    const uint32_t cbeg = chunk * kGChunk;
+    const uint32_t cend = (N - cbeg < (uint32_t)kGChunk) ? N : cbeg + kGChunk;
+    const float* ym = y + (uint64_t)m * N * kFK;
+    fd4 acc[6];
+#pragma unroll
+    for (int t = 0; t < 6; ++t) acc[t] = fd4{0.0, 0.0, 0.0, 0.0};
+    // k-steps of 4 rows, wave w every fourth (16 steps of a 256-row chunk);
+    // all of a wave's values loaded at once, then its matrix instructions
+    constexpr int kSteps = kGChunk / 16;
+    float v[kSteps][3];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const uint32_t row = cbeg + 4 * w + 16 * s + lane / 16;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) v[s][c] = row < cend ? ym[(uint64_t)row * kFK + 16 * c + lane % 16] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        int t = 0;
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = a; b < 3; ++b, ++t)
+                acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[s][a], (double)v[s][b], acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[w][t][lane][e] = acc[t][e];
     __syncthreads();
     double* out = gpart + ((uint64_t)m * nchunks + chunk) * kFK * kFK;
-    if (threadIdx.x >= (uint32_t)kGTilePairs) return;  // no barrier follows
-    uint32_t ti = 0, e = threadIdx.x, n = kGTiles;
-    while (e >= n) {
-        e -= n;
-        ++ti;
-        --n;
-    }
-    const uint32_t tj = ti + e;  // tile (ti, tj), ti <= tj
-    const float* yf = reinterpret_cast<const float*>(ys);
-    double acc[kGTile][kGTile];
+    // thread -> (tile t, lane l, entry e): 6 x 64 x 4 = 1536 sums of 4 waves
+    for (uint32_t k = threadIdx.x; k < 6u * kWave * 4u; k += kFThreads) {
+        const uint32_t t = k / (kWave * 4), l = (k / 4) % kWave, e = k % 4;
+        double sum = 0.0;
 #pragma unroll
-    for (int a = 0; a < kGTile; ++a)
-#pragma unroll
-        for (int b = 0; b < kGTile; ++b) acc[a][b] = 0.0;
-    for (uint32_t r = 0; r < nr; ++r) {
-        double u[kGTile], v[kGTile];
-#pragma unroll
-        for (int a = 0; a < kGTile; ++a) {
-            u[a] = yf[r * kFK + ti * kGTile + a];
-            v[a] = yf[r * kFK + tj * kGTile + a];
+        for (int ww = 0; ww < kFThreads / kWave; ++ww) sum += red[ww][t][l][e];
+        const uint32_t a = t < 3 ? 0u : (t < 5 ? 1u : 2u);
+        const uint32_t b = t < 3 ? t : (t < 5 ? t - 2 : 2u);
+        const uint32_t i = 16 * a + l / 16 + 4 * e, jj = 16 * b + l % 16;
+        // in a diagonal tile (i, j) and (j, i) are separate sums: the upper
+        // one is written to both places (one writer per address)
+        if (i <= jj) {
+            out[i * kFK + jj] = sum;
+            out[jj * kFK + i] = sum;
         }
-#pragma unroll
-        for (int a = 0; a < kGTile; ++a)
-#pragma unroll
-            for (int b = 0; b < kGTile; ++b) acc[a][b] = fma(u[a], v[b], acc[a][b]);
     }
-#pragma unroll
-    for (int a = 0; a < kGTile; ++a)
-#pragma unroll
-        for (int b = 0; b < kGTile; ++b) {
-            const uint32_t i = ti * kGTile + a, j = tj * kGTile + b;
-            out[i * kFK + j] = acc[a][b];
-            out[j * kFK + i] = acc[a][b];
-        }
 }
 
 // g = sum of the chunks' partial Gram matrices, chunks in order
@@ -236,59 +360,73 @@ __device__ __forceinline__ void sum_gram(const double* gpart, uint32_t m, uint32
     __syncthreads();
 }
 
+// Broadcast of lane `src`'s binary64 value to the wave (two readlanes).
+__device__ __forceinline__ double bcast_f64(double v, uint32_t src) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, (int)src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), (int)src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // One CholeskyQR step, factor part: G = Y^T Y = L L^T, then Rinv = (L^T)^-1
 // (upper triangular), binary64. A pivot at or below 1e-12 of the largest
 // diagonal entry drops its column: its row and column of Rinv are zero.
+// After the block sums the partial Gram matrices, one wave does both parts
+// in registers, lane i holding row i (48 binary64), fully unrolled so that
+// every register index is a constant: right-looking, column j of L is the
+// pivot column scaled by 1/sqrt(pivot) and the trailing rows lose its outer
+// product, the entries of column j reaching the other lanes by readlane;
+// then M = L^-1 (Rinv = M^T) row by row, row k final once divided by
+// L[k][k], the rows below updated with it. No barrier inside either part.
 __global__ __launch_bounds__(kFThreads) void fac_chol_kernel(const double* gpart, uint32_t nchunks, double* rinv) {
     __shared__ double g[kFK * kFK];
-    __shared__ double L[kFK * kFK];
     const uint32_t m = blockIdx.x;
     sum_gram<kFThreads>(gpart, m, nchunks, g);
-    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) L[i] = 0.0;
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        const uint32_t i = threadIdx.x;  // row handled by this lane
-        double maxdiag = 0.0;
-        for (int k = 0; k < kFK; ++k) maxdiag = fmax(maxdiag, g[k * kFK + k]);
-        const double tol = 1e-12 * maxdiag;
-        const uint32_t ri = i < (uint32_t)kFK ? i : 0u;
-        for (uint32_t j = 0; j < (uint32_t)kFK; ++j) {
-            // the pivot's sum and this row's sum in one loop: two independent
-            // chains of subtractions, each in its own order of k
-            double s = g[j * kFK + j];
-            double v = g[ri * kFK + j];
-            for (uint32_t k = 0; k < j; ++k) {
-                const double ljk = L[j * kFK + k];
-                s -= ljk * ljk;
-                v -= L[ri * kFK + k] * ljk;
-            }
-            const bool keep = s > tol;
-            const double ljj = keep ? sqrt(s) : 0.0;
-            if (keep && i > j && i < (uint32_t)kFK) v /= ljj;
-            else v = 0.0;
-            __builtin_amdgcn_wave_barrier();
-            if (i == j) L[j * kFK + j] = ljj;
-            if (i > j && i < (uint32_t)kFK) L[i * kFK + j] = v;
-            __builtin_amdgcn_wave_barrier();
-        }
-        // column i of Rinv (R = L^T, R(a, b) = L[b][a]): back substitution,
-        // in g (the Gram matrix is no longer needed)
-        __builtin_amdgcn_wave_barrier();
-        if (i < (uint32_t)kFK) {
-            for (int a = kFK - 1; a >= 0; --a) {
-                double xa = 0.0;
-                if ((uint32_t)a <= i && L[a * kFK + a] != 0.0) {
-                    double s = (a == (int)i) ? 1.0 : 0.0;
-                    for (uint32_t b = a + 1; b <= i; ++b) s -= L[b * kFK + a] * g[b * kFK + i];
-                    xa = s / L[a * kFK + a];
-                }
-                g[a * kFK + i] = xa;
-            }
-        }
+    if (threadIdx.x >= (uint32_t)kWave) return;  // no barrier follows
+    const uint32_t lane = threadIdx.x;
+    const uint32_t row = lane < (uint32_t)kFK ? lane : 0u;
+    double maxdiag = 0.0;
+    for (int k = 0; k < kFK; ++k) maxdiag = fmax(maxdiag, g[k * kFK + k]);
+    const double tol = 1e-12 * maxdiag;
+    double a[kFK];  // row `row` of G, then of L (lower part; the rest stays unused)
+#pragma unroll
+    for (int k = 0; k < kFK; ++k) a[k] = g[row * kFK + k];
+    double diag[kFK];  // L[j][j], uniform
+#pragma unroll
+    for (int j = 0; j < kFK; ++j) {
+        const double s = bcast_f64(a[j], j);  // the pivot, updated by columns 0 .. j-1
+        const bool keep = s > tol;
+        const double ljj = keep ? sqrt(s) : 0.0;
+        diag[j] = ljj;
+        // this lane's entry of column j (rows below j), then its trailing
+        // row; lanes at or above j carry lij = 0, and what they change above
+        // their diagonal is never read
+        const double rj = keep ? 1.0 / ljj : 0.0;
+        const double lij = lane > (uint32_t)j ? a[j] * rj : 0.0;
+        a[j] = lane == (uint32_t)j ? ljj : lij;
+#pragma unroll
+        for (int k = j + 1; k < kFK; ++k) a[k] = fma(-lij, bcast_f64(lij, k), a[k]);
     }
-    __syncthreads();
+    // M = L^-1: lane r holds row r of M (b) and of L (a)
+    double b[kFK];
+#pragma unroll
+    for (int c = 0; c < kFK; ++c) b[c] = (row == (uint32_t)c) ? 1.0 : 0.0;
+#pragma unroll
+    for (int k = 0; k < kFK; ++k) {
+        const double rk = diag[k] != 0.0 ? 1.0 / diag[k] : 0.0;
+        const double sk = lane == (uint32_t)k ? rk : 1.0;
+#pragma unroll
+        for (int c = 0; c <= k; ++c) b[c] *= sk;
+        const double lrk = lane > (uint32_t)k ? a[k] : 0.0;
+#pragma unroll
+        for (int c = 0; c <= k; ++c) b[c] = fma(-lrk, bcast_f64(b[c], k), b[c]);
+    }
+    // Rinv(r, c) = M(c, r): lane c holds row c of M, i.e. column c of Rinv
     double* out = rinv + (uint64_t)m * kFK * kFK;
-    for (uint32_t i = threadIdx.x; i < kFK * kFK; i += kFThreads) out[i] = g[i];
+    if (lane < (uint32_t)kFK) {
+#pragma unroll
+        for (int r = 0; r < kFK; ++r) out[r * kFK + lane] = (uint32_t)r <= lane ? b[r] : 0.0;
+    }
 }
 
 // Y <- Y Rinv (rows independent, in place), binary64 sums.
@@ -326,7 +464,7 @@ __global__ __launch_bounds__(kFThreads) void fac_apply_rinv_kernel(float* y, uin
 // Jacobi (round-robin pairing: 24 disjoint rotations per step, 47 steps per
 // sweep; each thread applies both sides of the rotations to whole 2 x 2
 // blocks, so a step is one pass), binary64, until the off-diagonal part is
-// below 1e-12 of the diagonal (in norm); writes ua = U_r diag(sigma),
+// below 1e-9 of the diagonal (in norm); writes ua = U_r diag(sigma),
 // ur = U_r diag(1/sigma) (0 where sigma = 0), both 48 x 32 binary32, and
 // sigma (descending).
 __global__ __launch_bounds__(kSvdThreads) void fac_small_svd_kernel(const double* gpart, uint32_t nchunks, float* ua,
@@ -363,7 +501,10 @@ __global__ __launch_bounds__(kSvdThreads) void fac_small_svd_kernel(const double
             sd += red[1][k];
         }
         __syncthreads();  // red is rewritten at the next sweep
-        if (so <= 1e-24 * sd) break;  // every thread takes the same branch
+        // off-diagonal norm below 1e-9 of the diagonal's: the eigenvalues
+        // are then exact to about 1e-14 relative of the largest, the vectors
+        // to far better than the bf16 factors keep
+        if (so <= 1e-18 * sd) break;  // every thread takes the same branch
         for (uint32_t step = 0; step < (uint32_t)kFK - 1; ++step) {
             // pairs: position 0 holds index 0, positions 1..47 rotate
             if (threadIdx.x < (uint32_t)kFK / 2) {
@@ -379,9 +520,18 @@ __global__ __launch_bounds__(kSvdThreads) void fac_small_svd_kernel(const double
                 const double apq = a[p * kFK + q];
                 double c = 1.0, sn = 0.0;
                 if (apq != 0.0) {
-                    const double tau = (a[q * kFK + q] - a[p * kFK + p]) / (2.0 * apq);
-                    const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-                    c = 1.0 / sqrt(1.0 + t * t);
+                    // t = tan(theta), the smaller root of t^2 + 2 tau t - 1 = 0
+                    // with tau = x / y: t = sgn(x y) |y| / (|x| + hypot(x, y));
+                    // c = (1 + t^2)^(-1/2) from the hardware estimate and two
+                    // Newton steps (each doubles the correct bits)
+                    const double x = a[q * kFK + q] - a[p * kFK + p], y = 2.0 * apq;
+                    const double r = sqrt(fma(x, x, y * y));
+                    const double t = copysign(fabs(y) / (fabs(x) + r), x * y);
+                    const double u = fma(t, t, 1.0);
+                    double c0 = __builtin_amdgcn_rsq(u);
+                    c0 = c0 * fma(-0.5 * u, c0 * c0, 1.5);
+                    c0 = c0 * fma(-0.5 * u, c0 * c0, 1.5);
+                    c = c0;
                     sn = t * c;
                 }
                 rp[i] = p;
@@ -501,7 +651,7 @@ LowrankFactorWs lowrank_factor_ws(uint32_t M, uint32_t H, uint32_t T, uint32_t d
     w.w = take((uint64_t)M * Dt * kFK * 4);
     w.part = take((uint64_t)M * nchunks * Dt * kFK * 4);
     w.rinv = take((uint64_t)M * kFK * kFK * 8);
-    const uint64_t gchunks = (((uint64_t)T > Dt ? (uint64_t)T : Dt) + kGRows - 1) / kGRows;
+    const uint64_t gchunks = (((uint64_t)T > Dt ? (uint64_t)T : Dt) + kGChunk - 1) / kGChunk;
     w.gpart = take((uint64_t)M * gchunks * kFK * kFK * 8);
     w.ua = take((uint64_t)M * kFK * kFR * 4);
     w.ur = take((uint64_t)M * kFK * kFR * 4);
@@ -530,7 +680,7 @@ hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d,
     hipError_t e = hipSuccess;
     auto zx = [&](const float* x, uint64_t x_stride) {
         if (e != hipSuccess) return;
-        const dim3 grid((T + 63) / 64, M);
+        const dim3 grid((T + 255) / 256, M);
         e = d == 64 ? launch_kernel(fac_zx_kernel<64>, grid, blk, stream, Z, x, x_stride, Y, H, T)
                     : launch_kernel(fac_zx_kernel<128>, grid, blk, stream, Z, x, x_stride, Y, H, T);
     };
@@ -546,7 +696,7 @@ hipError_t launch_lowrank_factor(uint32_t M, uint32_t H, uint32_t T, uint32_t d,
                           (const float*)P, W, M, per, nchunks);
     };
     auto gram = [&](const float* x, uint32_t N) -> uint32_t {
-        const uint32_t nc = (N + kGRows - 1) / kGRows;
+        const uint32_t nc = (N + kGChunk - 1) / kGChunk;
         if (e == hipSuccess) e = launch_kernel(fac_gram_partial_kernel, dim3(nc, M), blk, stream, x, N, nc, Gp);
         return nc;
     };
