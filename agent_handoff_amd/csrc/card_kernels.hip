@@ -238,75 +238,126 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
     }
 }
 
-// One 32-channel group at a per-lane width b (2, 4 or 8): the codes as
-// bytes, code j in byte j % 4 of by[j / 4]. Code j is
-// rne(min((x_j - mn) * inv, qmax)), which equals min(rne((x_j - mn) * inv),
-// qmax) as qmax is an integer; the rounding, the clamp at 255 and the
-// placement in a byte are one v_cvt_pk_u8_f32 (round to nearest even,
-// saturating; checked against rintf on the GPU for a million values). The
-// arithmetic is the same at every width but for qmax, so a wave whose tokens
-// mix widths runs it once; only the narrowing of the bytes to b-bit fields
-// (narrow_codes) depends on the width.
+// Codes of one group as bytes, in the order that makes narrowing them to
+// b-bit fields cheap at every width: code j = 16w + 4k + r (w < 2, k < 4,
+// r < 4) goes to byte k of by[4w + r]. Code j is rne(min((x_j - mn) * inv,
+// qmax)), which equals min(rne((x_j - mn) * inv), qmax) as qmax is an
+// integer; the rounding, the clamp at 255 and the placement in a byte are one
+// v_cvt_pk_u8_f32 (round to nearest even, saturating; checked against rintf
+// on the GPU for a million values). Without Clamp the min with qmax is left
+// out: the caller has shown that no code reaches it.
+template <bool Clamp>
+__device__ __forceinline__ void codes_to_bytes(const float (&x)[32], float mn, float inv, float qmax,
+                                               uint32_t (&by)[8]) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = 16 * (m / 4) + 4 * k + (m % 4);
+            float y = (x[j] - mn) * inv;
+            if (Clamp) y = __builtin_fminf(y, qmax);
+            acc = __builtin_amdgcn_cvt_pk_u8_f32(y, (uint32_t)k, acc);
+        }
+        by[m] = acc;
+    }
+}
+
+// One 32-channel group at a per-lane width b (2, 4 or 8): scale and minimum
+// bits and the codes as bytes (codes_to_bytes order). The arithmetic is the
+// same at every width but for qmax, so a wave whose tokens mix widths runs it
+// once; only the narrowing of the bytes to b-bit fields (narrow_codes)
+// depends on the width.
+//
+// The clamp at qmax. Rounding and multiplication by inv >= 0 are monotone,
+// so every (x_j - mn) * inv is at most (mx - mn) * inv, the same operations
+// on the maximum. While that is below qmax + 1/2 every code rounds to at most
+// qmax and min(y, qmax) changes no code; the usual case (the fp16 scale is
+// within 2^-11 of the exact step). A subnormal or saturated fp16 scale, or a
+// non-finite range, can break it, and a NaN group needs the clamp for its
+// codes: if any lane of the wave has either, the wave takes the clamped
+// form.
 __device__ __forceinline__ void quant_group(const float (&x)[32], uint32_t b, uint16_t& sbits, uint16_t& mbits,
                                             uint32_t (&by)[8]) {
+    // IEEE 754-2019 minimum and maximum (v_minimum3_f32, v_maximum3_f32):
+    // a NaN anywhere in the group, quiet or signalling, makes both NaN, and
+    // such a group takes the quiet NaN 0x7FC0 for its minimum and maximum
+    // (its scale then saturates at 65504, each code is qmax through the
+    // clamp, and the group decodes to NaN).
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int j = 1; j < 32; ++j) {
-        mn = __builtin_fminf(mn, x[j]);
-        mx = __builtin_fmaxf(mx, x[j]);
+        mn = __builtin_elementwise_minimum(mn, x[j]);
+        mx = __builtin_elementwise_maximum(mx, x[j]);
     }
+    const bool nan_in_wave = __builtin_amdgcn_ballot_w64(mx != mx) != 0;
+    if (nan_in_wave && mx != mx) mn = mx = __uint_as_float(0x7FC00000u);
     mn = mn + 0.0f;
     mx = mx + 0.0f;
     const float qmax = (float)((1u << b) - 1u);
-    const float s = (mx - mn) / qmax;
+    // s = (mx - mn) / qmax correctly rounded, from RN(1/qmax): z = RN(d y),
+    // the remainder d - z qmax exactly by an fma, and one fma to correct.
+    // Checked against the IEEE quotient for every finite d >= 0 (subnormals
+    // included) at qmax = 3, 15 and 255. A non-finite d gives NaN here and
+    // infinity or NaN in the quotient; the min with 65504 below makes both
+    // 65504.
+    const float d = mx - mn;
+    const float yq = b == 2 ? 1.0f / 3.0f : (b == 4 ? 1.0f / 15.0f : 1.0f / 255.0f);
+    const float z = d * yq;
+    const float s = __builtin_fmaf(__builtin_fmaf(-z, qmax, d), yq, z);
     const _Float16 s16 = (_Float16)__builtin_fminf(s, 65504.0f);
     const float sf = (float)s16;
-    const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float y = __builtin_fminf((x[4 * d + e] - mn) * inv, qmax);
-            acc = __builtin_amdgcn_cvt_pk_u8_f32(y, (uint32_t)e, acc);
-        }
-        by[d] = acc;
-    }
+    // inv = RN(1/sf) from v_rcp_f32 (r0 = (1 + e)/sf, |e| <= 2^-23) and one
+    // Newton step: 1 - sf r0 = -e exactly (an fma), and RN(r0 - e r0) =
+    // RN((1 - e^2)/sf). An 11-bit sf keeps 1/sf at least 2^-35 (relative)
+    // from every midpoint between binary32 neighbours, far beyond e^2 <=
+    // 2^-46, so the step lands on RN(1/sf).
+    const float r0 = __builtin_amdgcn_rcpf(sf);
+    const float inv = (sf == 0.0f) ? 0.0f : __builtin_fmaf(__builtin_fmaf(-sf, r0, 1.0f), r0, r0);
+    const bool clamp = !((mx - mn) * inv < qmax + 0.5f);
+    if (!nan_in_wave && __builtin_amdgcn_ballot_w64(clamp) == 0)
+        codes_to_bytes<false>(x, mn, inv, qmax, by);
+    else
+        codes_to_bytes<true>(x, mn, inv, qmax, by);
     sbits = __builtin_bit_cast(uint16_t, s16);
     mbits = (uint16_t)(__float_as_uint(mn) >> 16);
 }
 
-// Byte codes (each below 2^B) -> B-bit fields, 32 codes in B dwords, least
-// significant first (out[0 .. B-1]).
+// Byte codes (each below 2^B, codes_to_bytes order) -> B-bit fields, 32
+// codes in B dwords, code i of dword w at bits B*i (out[0 .. B-1]).
+// __builtin_amdgcn_perm(hi, lo, sel): byte n of the result is byte sel_n of
+// the 8 bytes lo (0-3), hi (4-7).
 template <int B>
 __device__ __forceinline__ void narrow_codes(const uint32_t (&by)[8], uint32_t (&out)[8]) {
     if (B == 8) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) out[w] = by[w];
-    } else if (B == 4) {
-        // bytes q0..q3 (each < 16) -> q0 | q1 << 4 | q2 << 8 | q3 << 12
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t f[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t t = by[2 * w + h] | (by[2 * w + h] >> 4);
-                f[h] = (t & 0xFFu) | ((t >> 8) & 0xFF00u);
-            }
-            out[w] = f[0] | (f[1] << 16);
-        }
-    } else {
-        // bytes q0..q3 (each < 4) -> q0 | q1 << 2 | q2 << 4 | q3 << 6
+        // out[4w + k] byte r = by[4w + r] byte k: a 4 x 4 byte transpose
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const uint32_t t = by[4 * w + h] | (by[4 * w + h] >> 6);
-                acc |= ((t & 0xFu) | ((t >> 12) & 0xF0u)) << (8 * h);
-            }
-            out[w] = acc;
+            const uint32_t* d = by + 4 * w;
+            const uint32_t p0 = __builtin_amdgcn_perm(d[1], d[0], 0x06020400u);  // d0.0 d1.0 d0.2 d1.2
+            const uint32_t p1 = __builtin_amdgcn_perm(d[1], d[0], 0x07030501u);  // d0.1 d1.1 d0.3 d1.3
+            const uint32_t p2 = __builtin_amdgcn_perm(d[3], d[2], 0x06020400u);
+            const uint32_t p3 = __builtin_amdgcn_perm(d[3], d[2], 0x07030501u);
+            out[4 * w + 0] = __builtin_amdgcn_perm(p2, p0, 0x05040100u);
+            out[4 * w + 1] = __builtin_amdgcn_perm(p3, p1, 0x05040100u);
+            out[4 * w + 2] = __builtin_amdgcn_perm(p2, p0, 0x07060302u);
+            out[4 * w + 3] = __builtin_amdgcn_perm(p3, p1, 0x07060302u);
         }
+    } else if (B == 4) {
+        // e_s byte k = code 16w+4k+s | code 16w+4k+s+1 << 4 (s = 0, 2); dword
+        // 2w + a takes bytes 2a, 2a+1 of e_0 and e_2 alternately
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const uint32_t e0 = by[4 * w] | (by[4 * w + 1] << 4);
+            const uint32_t e2 = by[4 * w + 2] | (by[4 * w + 3] << 4);
+            out[2 * w] = __builtin_amdgcn_perm(e2, e0, 0x05010400u);
+            out[2 * w + 1] = __builtin_amdgcn_perm(e2, e0, 0x07030602u);
+        }
+    } else {
+        // by[4w + r] byte k = code 16w + 4k + r, which belongs at bit 8k + 2r
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+            out[w] = by[4 * w] | (by[4 * w + 1] << 2) | (by[4 * w + 2] << 4) | (by[4 * w + 3] << 6);
     }
 }
 
@@ -334,7 +385,8 @@ __device__ __forceinline__ void quant_store_group(const float (&x)[32], uint32_t
         narrow_codes<4>(by, codes);
         store_group<4>(rec, G, g, sb, mb, codes);
     } else {
-        store_group<8>(rec, G, g, sb, mb, by);
+        narrow_codes<8>(by, codes);
+        store_group<8>(rec, G, g, sb, mb, codes);
     }
 }
 
@@ -415,61 +467,98 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
 }
 
 // The codes of one group at a per-lane width b (2, 4 or 8) from its record,
-// widened to bytes: code j in byte j % 4 of by[j / 4].
-__device__ __forceinline__ void widen_codes(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t b,
-                                            uint32_t (&by)[8]) {
+// two per dword in channel order (channel 2i in the low half of h[i], 2i + 1
+// in the high half), each left where masking its record bits puts it: at
+// bit e = 0, 2, 4 or 6 of its half's low byte, e depending on the channel's
+// place in its byte (e = 0 at b = 8; 0, 4 at b = 4; 0, 2, 4, 6 at b = 2). A
+// half read as an f16 is then the subnormal code * 2^(e - 24) (below 2^-14,
+// exact; the kernels keep f16 subnormals), and sc[j % 4] = sf * 2^(24 - e)
+// (a power-of-two scaling of an f16 value, exact in binary32) makes the
+// product of the two code * sf exactly.
+__device__ __forceinline__ void code_halves(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t b, float sf,
+                                            uint32_t (&h)[16], float (&sc)[4]) {
     // codes start 8-byte aligned (4*G is a multiple of 8, records 16-aligned)
     const uint2* src = reinterpret_cast<const uint2*>(rec + 4 * G + g * 4 * b);
+    const float s24 = sf * 16777216.0f;
     if (b == 8) {
+        // dword m: codes 4m .. 4m+3, one per byte
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint2 c = src[i];
-            by[2 * i] = c.x;
-            by[2 * i + 1] = c.y;
+            const uint2 v = src[i];
+            const uint32_t c[2] = {v.x, v.y};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int m = 2 * i + u;
+                h[2 * m] = __builtin_amdgcn_perm(0u, c[u], 0x0C010C00u);
+                h[2 * m + 1] = __builtin_amdgcn_perm(0u, c[u], 0x0C030C02u);
+            }
         }
+        sc[0] = sc[1] = sc[2] = sc[3] = s24;
     } else if (b == 4) {
-        // codes 4k .. 4k+3 are the nibbles of half k % 2 of dword k / 2
-        uint32_t c[4];
+        // dword m: codes 8m + 2k (low nibble) and 8m + 2k + 1 (high) in byte k
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint2 v = src[i];
-            c[2 * i] = v.x;
-            c[2 * i + 1] = v.y;
-        }
+            const uint32_t c[2] = {v.x, v.y};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t t = c[k / 2] >> (16 * (k % 2));
-            const uint32_t x = (t & 0xFFu) | ((t & 0xFF00u) << 8);
-            by[k] = (x | (x << 4)) & 0x0F0F0F0Fu;
+            for (int u = 0; u < 2; ++u) {
+                const int m = 2 * i + u;
+                const uint32_t lo = c[u] & 0x0F0F0F0Fu, hi = c[u] & 0xF0F0F0F0u;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    h[4 * m + k] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)k | ((uint32_t)(4 + k) << 16));
+            }
         }
+        sc[0] = sc[2] = s24;
+        sc[1] = sc[3] = s24 * 0.0625f;
     } else {
-        // codes 4k .. 4k+3 are the 2-bit fields of byte k % 4 of dword k / 4
+        // dword m: code 16m + 4k + r at bits 2r of byte k
         const uint2 v = src[0];
         const uint32_t c[2] = {v.x, v.y};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t t = (c[k / 4] >> (8 * (k % 4))) & 0xFFu;
-            const uint32_t x = (t | (t << 12)) & 0x000F000Fu;
-            by[k] = (x | (x << 6)) & 0x03030303u;
+        for (int m = 0; m < 2; ++m) {
+            const uint32_t q0 = c[m] & 0x03030303u, q1 = c[m] & 0x0C0C0C0Cu;
+            const uint32_t q2 = c[m] & 0x30303030u, q3 = c[m] & 0xC0C0C0C0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sel = 0x0C040C00u | (uint32_t)k | ((uint32_t)k << 16);
+                h[8 * m + 2 * k] = __builtin_amdgcn_perm(q1, q0, sel);
+                h[8 * m + 2 * k + 1] = __builtin_amdgcn_perm(q3, q2, sel);
+            }
         }
+        sc[0] = s24;
+        sc[1] = s24 * 0.25f;
+        sc[2] = s24 * 0.0625f;
+        sc[3] = s24 * 0.015625f;
     }
 }
 
-// One group at width b in {2, 4, 8} back to 32 bf16 values (o: pairs, channel
-// 2j in the low half of o[j]): q*s + mn in binary32 with one rounding (q*s
-// alone is exact), then bf16 round to nearest even. Only the widening of the
-// codes depends on the width: a wave whose tokens mix widths converts once.
+// One group at width b in {2, 4, 8} back to 32 binary32 values y_j = q_j*s +
+// mn with one rounding (q_j*s alone is exact), which the caller rounds to
+// bf16. Only the extraction of the codes depends on the width: a wave whose
+// tokens mix widths runs the rest once.
 __device__ __forceinline__ void dequant_group(const uint8_t* rec, uint32_t G, uint32_t g, uint32_t b,
-                                              uint32_t (&o)[16]) {
+                                              float (&y)[32]) {
     const float sf = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(rec)[g]);
     const float mn = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rec)[G + g] << 16);
-    uint32_t by[8];
-    widen_codes(rec, G, g, b, by);
-    float y[32];
+    uint32_t h[16];
+    float sc[4];
+    code_halves(rec, G, g, b, sf, h, sc);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf((float)((by[j / 4] >> (8 * (j % 4))) & 0xFFu), sf, mn);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[j] = pack_bf16x2(y[2 * j], y[2 * j + 1]);
+    for (int j = 0; j < 32; ++j) {
+        const uint16_t bits = (uint16_t)(j % 2 ? h[j / 2] >> 16 : h[j / 2]);
+        y[j] = __builtin_fmaf((float)__builtin_bit_cast(_Float16, bits), sc[j % 4], mn);
+    }
+}
+
+// y rounded to bf16 (round to nearest even), as a binary32 value: the
+// rounded bits land in the high half of v_cvt_pk_bf16_f32(0, y), the low
+// half is zero. (Written out: the compiler builds the same pair from a
+// conversion into the low half and a v_perm, two instructions.)
+__device__ __forceinline__ float round_bf16(float y) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(y));
+    return __uint_as_float(r);
 }
 
 template <int D>
@@ -522,7 +611,10 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rec + 64 * g)[i];
         } else {
-            dequant_group(rec, G, g, width, o);
+            float y[32];
+            dequant_group(rec, G, g, width, y);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] = pack_bf16x2(y[2 * j], y[2 * j + 1]);
         }
     }
     // Stage the wave's contiguous output image in LDS (over the records,
@@ -606,29 +698,38 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
         for (uint32_t j = 0; j < kSpanChunks / kWave; ++j) si[kWave * j + lane] = c[j];
     }
     if (valid) {
-        // rebuild the group (as unpack does) ...
-        uint32_t o[16];
+        // rebuild the group (as unpack does: binary32 values rounded to bf16) ...
+        float x[32];
         const uint8_t* rin = reinterpret_cast<const uint8_t*>(si) + (uint32_t)(my_a - a0);
         if (w_in == 16) {
+            uint32_t o[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(o)[i] = reinterpret_cast<const uint4*>(rin + 64 * g)[i];
-        } else {
-            dequant_group(rin, G, g, w_in, o);
-        }
-        // ... and quantise it at the new width (as pack does); the barrier
-        // keeps every lane's reads above ahead of the writes below
-        __builtin_amdgcn_wave_barrier();
-        uint8_t* rout = reinterpret_cast<uint8_t*>(so) + (uint32_t)(my_b - b0);
-        if (w_out == 16) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rout + 64 * g)[i] = reinterpret_cast<const uint4*>(o)[i];
-        } else {
-            float x[32];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 x[2 * j] = bf16_lo(o[j]);
                 x[2 * j + 1] = bf16_hi(o[j]);
             }
+        } else {
+            float y[32];
+            dequant_group(rin, G, g, w_in, y);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) x[j] = round_bf16(y[j]);
+        }
+
+        // ... and quantise it at the new width (as pack does); the barrier
+        // keeps every lane's reads above ahead of the writes below
+        __builtin_amdgcn_wave_barrier();
+        uint8_t* rout = reinterpret_cast<uint8_t*>(so) + (uint32_t)(my_b - b0);
+        if (w_out == 16) {
+            // the bf16 bits of the rebuilt values, pairs in channel order
+            uint32_t o[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                o[j] = __builtin_amdgcn_perm(__float_as_uint(x[2 * j + 1]), __float_as_uint(x[2 * j]), 0x07060302u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(rout + 64 * g)[i] = reinterpret_cast<const uint4*>(o)[i];
+        } else {
             quant_store_group(x, w_out, rout, G, g);
             // zero the record's tail padding (present for d = 64)
             const uint32_t used = 4 * G + D * w_out / 8;

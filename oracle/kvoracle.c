@@ -493,16 +493,27 @@ uint64_t or_card_bytes(uint32_t L, uint32_t H, uint32_t T, uint32_t d, const uin
 
 /* One group of 32 bf16 values at width b (QKVShare item 2, min-max):
  *   mn, mx = min, max of the group (both canonicalised: -0 becomes +0)
- *   s      = fp16((mx - mn) / (2^b - 1))        (binary32, then RNE)
- *   q_j    = min(rint((x_j - mn) * (1 / s)), 2^b - 1), q = 0 when s = 0 */
+ *   s      = fp16(min((mx - mn) / (2^b - 1), 65504))   (binary32, then RNE)
+ *   q_j    = min(rint((x_j - mn) * (1 / s)), 2^b - 1), q = 0 when s = 0
+ * NaN (the pages give no rule; this is the reading both sides implement):
+ * a group holding a NaN, quiet or signalling, has the quiet NaN 0x7FC0 for
+ * its minimum and maximum (IEEE 754-2019 minimum / maximum propagate it).
+ * Its scale is then 65504 (the min above) and each code min(NaN, 2^b - 1)
+ * = 2^b - 1 (fminf returns the number), so the group decodes to NaN. */
 static void card_quant_group(const uint16_t* x, uint32_t b, uint16_t* s_bits, uint16_t* mn_bits,
                              uint8_t* q) {
-    float mn = or_bf16_to_f32(x[0]), mx = mn;
-    for (uint32_t j = 1; j < CARD_GROUP; ++j) {
+    float mn = INFINITY, mx = -INFINITY;
+    int has_nan = 0;
+    for (uint32_t j = 0; j < CARD_GROUP; ++j) {
         float f = or_bf16_to_f32(x[j]);
+        if (isnan(f)) {
+            has_nan = 1;
+            continue;
+        }
         if (f < mn) mn = f;
         if (f > mx) mx = f;
     }
+    if (has_nan) mn = mx = or_bf16_to_f32(0x7FC0u);
     mn = mn + 0.0f;
     mx = mx + 0.0f;
     float qmax = (float)((1u << b) - 1u);
@@ -511,8 +522,7 @@ static void card_quant_group(const uint16_t* x, uint32_t b, uint16_t* s_bits, ui
     float sf = or_f16_to_f32(sb);
     float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
     for (uint32_t j = 0; j < CARD_GROUP; ++j) {
-        float u = rintf((or_bf16_to_f32(x[j]) - mn) * inv);
-        if (u > qmax) u = qmax;
+        float u = fminf(rintf((or_bf16_to_f32(x[j]) - mn) * inv), qmax);
         q[j] = (uint8_t)u;
     }
     *s_bits = sb;

@@ -81,6 +81,89 @@ def assert_bits_equal(got, want, what):
                              f"got {got.flat[idx[0]]:#06x} want {want.flat[idx[0]]:#06x}")
 
 
+# Group contents that reach the quantiser's and dequantiser's edge cases:
+# the rest of the tests draw student-t values, whose groups always have a
+# moderate, finite range.
+EDGE_KINDS = ("normal", "constant", "tiny_range", "huge_range", "pos_inf", "quiet_nan", "nan_payloads",
+              "signed_zeros", "both_infs", "subnormal_values")
+
+
+def _edge_kv(shape, seed):
+    """bf16 bit patterns [L, H, T, d] for K and V whose 32-channel groups
+    each take one of EDGE_KINDS, drawn independently per group: a constant
+    group (zero range, zero scale), a range of a few ulps at 1e-3 (a
+    subnormal fp16 scale, codes that reach the clamp), a range near the bf16
+    maximum (the fp16 scale saturates at 65504), +inf, quiet NaNs, NaNs with
+    payloads and both signs, +0 and -0 only, -inf with +inf, and bf16
+    subnormals. A wave mixes all of them with ordinary groups."""
+    L, H, T, d = shape
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(2):
+        x = synth.f32_to_bf16_bits(rng.standard_normal((L, H, T, d)).astype(np.float32))
+        g = x.reshape(L, H, T, d // 32, 32)
+        kinds = rng.integers(0, len(EDGE_KINDS), size=g.shape[:4])
+        for idx in np.ndindex(*kinds.shape):
+            kind = EDGE_KINDS[kinds[idx]]
+            grp = g[idx]
+            pos = rng.integers(0, 32, size=3)
+            if kind == "constant":
+                grp[:] = grp[0]
+            elif kind == "tiny_range":
+                grp[:] = 0x3A83 + rng.integers(0, 4, 32)
+            elif kind == "huge_range":
+                grp[:] = synth.f32_to_bf16_bits(rng.uniform(-3.3e38, 3.3e38, 32).astype(np.float32))
+                grp[pos[0]] = 0x7F7F
+            elif kind == "pos_inf":
+                grp[pos[0]] = 0x7F80
+            elif kind == "quiet_nan":
+                grp[pos[:2]] = 0x7FC0
+            elif kind == "nan_payloads":
+                grp[pos[0]], grp[pos[1]], grp[pos[2]] = 0xFFC1, 0x7F81, 0x7FFF
+            elif kind == "signed_zeros":
+                grp[:] = rng.choice(np.array([0x0000, 0x8000], np.uint16), 32)
+            elif kind == "both_infs":
+                grp[pos[0]], grp[pos[1]] = 0xFF80, 0x7F80
+            elif kind == "subnormal_values":
+                grp[:] = rng.integers(0, 0x80, 32).astype(np.uint16) | (rng.integers(0, 2, 32).astype(np.uint16) << 15)
+        out.append(x)
+    return out[0], out[1]
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 37, 128), (1, 4, 70, 64)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_edge_groups_pack_unpack_transcode_bit_exact(shape, seed):
+    """Groups at the quantiser's edges (zero, subnormal-scale and saturated
+    ranges, infinities, NaNs, signed zeros, subnormals) at every width: the
+    packed card, its unpacking and a hop to new widths bit-exact against the
+    oracle."""
+    say("edge groups", shape, seed)
+    k, v = _edge_kv(shape, seed)
+    T = shape[2]
+    widths = _widths("mixed", T, seed)
+    card, n, st = gpu_pack(shape, k, v, widths)
+    ref = oracle.card_pack(k, v, widths, b"llama-3.1-8b", 0)
+    assert st == 0 and n == ref.size
+    got = card[:n].cpu().numpy()
+    if not np.array_equal(got, ref):
+        idx = np.nonzero(got != ref)[0]
+        raise AssertionError(f"{idx.size} card bytes differ, first at {idx[0]}: got {got[idx[0]]} want {ref[idx[0]]}")
+    ko, vo, st = gpu_unpack(shape, torch.from_numpy(ref).to(DEV), n)
+    assert st == 0
+    rk, rv = oracle.card_unpack(ref, shape)
+    assert_bits_equal(to_host(ko), rk, "K")
+    assert_bits_equal(to_host(vo), rv, "V")
+    for new_seed in (seed + 5, seed + 6):
+        w1 = _widths("mixed", T, new_seed)
+        out, n1, st = gpu_transcode(shape, torch.from_numpy(ref).to(DEV), ref.size, w1)
+        ref1 = oracle.card_transcode(ref, shape, w1)
+        assert st == 0 and n1 == ref1.size
+        got1 = out[:n1].cpu().numpy()
+        if not np.array_equal(got1, ref1):
+            idx = np.nonzero(got1 != ref1)[0]
+            raise AssertionError(f"transcode: {idx.size} bytes differ, first at {idx[0]}")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_full_size_cachecard_workload(seed):
     """The Llama-3.1-8B 8K card (seeds 0-2: values and width runs): pack

@@ -12,7 +12,7 @@ import torch
 import oracle
 from agent_handoff_amd import kvcodec as kv
 from agent_handoff_amd import synth
-from gpu_util import (DEV, assert_decode_close, assert_pool_equal, dev_bytes, per_head_rel_mse, say, to_dev,
+from gpu_util import (DEV, assert_decode_close, assert_head_mse_close, assert_pool_equal, dev_bytes, say, to_dev,
                       to_host)
 
 pytestmark = pytest.mark.gpu
@@ -110,8 +110,7 @@ def test_decode_within_one_ulp(shape, cfg):
     assert int(status.item()) == 0
     # per-head reconstruction MSE against the input
     for src, g, r in ((k, to_host(ko[0]), rk), (v, to_host(vo[0]), rv)):
-        mg, mr = per_head_rel_mse(src, g), per_head_rel_mse(src, r)
-        assert np.all(np.abs(mg - mr) <= 1e-4 * mr + 1e-30)
+        say("  per-head MSE, largest relative difference:", assert_head_mse_close(src, g, r))
 
 
 def test_decode_fanout_and_layer_ranges():
@@ -189,8 +188,8 @@ def test_concurrent_decodes_on_streams():
 def test_full_size_workload_bit_exact(cfg, seed):
     """Full SmolLM2-1.7B 2K and Llama-3-8B 4K pools, seeds 0-2: encode
     bit-exact; decode (Llama: into 15 agents, the fan-out the bench times)
-    within 1 ulp; per-head reconstruction MSE within 1e-4 relative of the
-    oracle decode's."""
+    within 1 ulp; per-head reconstruction MSE within what those 1-ulp
+    differences can move it."""
     w = synth.WORKLOADS[cfg]
     say("full-size workload", w.name, "seed", seed, "generating inputs")
     k, v = synth.kv_bits(w, seed)
@@ -210,8 +209,7 @@ def test_full_size_workload_bit_exact(cfg, seed):
     n1 = assert_decode_close(gk, rk, "K") + assert_decode_close(gv, rv, "V")
     say("  values at 1 ulp:", n1, "of", 2 * k.size)
     for src, g, r in ((k, gk, rk), (v, gv, rv)):
-        mg, mr = per_head_rel_mse(src, g), per_head_rel_mse(src, r)
-        assert np.all(np.abs(mg - mr) <= 1e-4 * mr + 1e-30)
+        say("  per-head MSE, largest relative difference:", assert_head_mse_close(src, g, r))
 
 
 def test_long_context_32k_pool_layer_streamed():

@@ -146,6 +146,75 @@ def test_constant_group_and_zero_scale():
     assert rec[4:6].view("<u2")[0] == 0                        # -0 stored as +0
 
 
+def _group_record_fields(card, shape, widths, t, g):
+    """Scale bits, minimum bits and codes of group g of token t in stream 0."""
+    d = shape[3]
+    G = d // 32
+    b = int(widths[t])
+    h, _ = _parse(card, shape)
+    rec = _record(card, h, widths, 0, t, d)
+    scale = int(rec[2 * g:2 * g + 2].view("<u2")[0])
+    mn = int(rec[2 * G + 2 * g:2 * G + 2 * g + 2].view("<u2")[0])
+    bits = np.unpackbits(rec[4 * G:4 * G + d * b // 8], bitorder="little").reshape(d, b)
+    q = (bits * (1 << np.arange(b))).sum(axis=1)
+    return scale, mn, q[32 * g:32 * g + 32]
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_nan_group_rule(b):
+    """The card's NaN rule (the pages give none): a group holding a NaN,
+    quiet or signalling, wherever it sits, takes the quiet NaN 0x7FC0 as its
+    minimum and maximum; its scale saturates at 65504 (0x7BFF), every code
+    is 2^b - 1, and it decodes to 0x7FC0 throughout. The token's other group
+    is packed as if alone."""
+    d = 64
+    shape = (1, 1, 3, d)
+    ramp = np.linspace(-1.0, 2.0, 32).astype(np.float32)
+    x = np.tile(ramp, (1, 1, 3, 2))
+    k = f32_to_bf16_bits(x)
+    k[0, 0, 0, 0] = 0x7FC0        # quiet NaN first in group 0
+    k[0, 0, 1, 17] = 0x7F81       # signalling NaN inside group 0
+    k[0, 0, 2, 63] = 0xFFC1       # negative NaN with a payload, last of group 1
+    widths = np.full(3, b, np.uint8)
+    card = oracle.card_pack(k, k, widths)
+    clean = oracle.card_pack(f32_to_bf16_bits(x), f32_to_bf16_bits(x), widths)
+    ko, _ = oracle.card_unpack(card, shape)
+    for t, g in ((0, 0), (1, 0), (2, 1)):
+        scale, mn, q = _group_record_fields(card, shape, widths, t, g)
+        assert scale == 0x7BFF and mn == 0x7FC0 and np.all(q == 2 ** b - 1), (t, g)
+        assert np.all(ko[0, 0, t, 32 * g:32 * g + 32] == 0x7FC0)
+        other = 1 - g
+        assert _group_record_fields(card, shape, widths, t, other)[:2] == \
+            _group_record_fields(clean, shape, widths, t, other)[:2]
+        assert np.array_equal(_group_record_fields(card, shape, widths, t, other)[2],
+                              _group_record_fields(clean, shape, widths, t, other)[2])
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_infinite_groups(b):
+    """Infinities are values: with +inf the range is infinite, the scale
+    saturates at 65504 and only the infinite value reaches the top code (the
+    ramp's spread, 3, is far below one step); with -inf as the minimum every
+    difference is infinite (or NaN for -inf itself) and every code is the
+    top one, so the group decodes to -inf."""
+    d = 32
+    shape = (1, 1, 2, d)
+    ramp = np.linspace(-1.0, 2.0, 32).astype(np.float32)
+    k = f32_to_bf16_bits(np.tile(ramp, (1, 1, 2, 1)))
+    k[0, 0, 0, 5] = 0x7F80
+    k[0, 0, 1, 3], k[0, 0, 1, 9] = 0xFF80, 0x7F80
+    widths = np.full(2, b, np.uint8)
+    card = oracle.card_pack(k, k, widths)
+    ko, _ = oracle.card_unpack(card, shape)
+    scale, mn, q = _group_record_fields(card, shape, widths, 0, 0)
+    assert scale == 0x7BFF and mn == int(f32_to_bf16_bits(np.array([-1.0], np.float32))[0])
+    assert q[5] == 2 ** b - 1 and np.all(np.delete(q, 5) == 0)
+    assert np.all(np.delete(ko[0, 0, 0], 5) == mn)
+    scale, mn, q = _group_record_fields(card, shape, widths, 1, 0)
+    assert scale == 0x7BFF and mn == 0xFF80 and np.all(q == 2 ** b - 1)
+    assert np.all(ko[0, 0, 1] == 0xFF80)
+
+
 def test_unpack_rejects_corruption():
     shape = (1, 2, 20, 64)
     k, v = _kv(shape, 4)
