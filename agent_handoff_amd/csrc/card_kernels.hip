@@ -27,8 +27,6 @@ namespace kvc {
 namespace {
 
 constexpr uint32_t kFlagBadHeader = 1, kFlagBadWidth = 2, kFlagCapacity = 4;
-// internal: the input card of a transcode was refused (already reported)
-constexpr uint32_t kFlagInputRefused = 256;
 constexpr uint32_t kStatusBits = kFlagBadHeader | kFlagBadWidth | kFlagCapacity;
 
 // Workgroups are dealt to the 8 XCDs in turn, so consecutive token blocks
@@ -73,7 +71,12 @@ struct ScanParams {
     uint32_t L, H, T, d;
     CardMetaDev meta;
     const uint8_t* meta_src;   // transcode: card whose model ID and position offset are carried over
-    const uint64_t* prior_info;  // transcode, output scan: the input scan's info (its flags refuse the output)
+};
+
+// One scan per workgroup: a transcode scans its input and its output card
+// in one launch of two workgroups.
+struct ScanLaunch {
+    ScanParams s[2];
 };
 
 struct CardParams {
@@ -91,17 +94,29 @@ struct CardParams {
     uint64_t n_waves;
 };
 
-__global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
+// card_record_bytes as selects (the scan takes it for 8 tokens per thread;
+// the branches of the general form cost a divergent region per token)
+__device__ __forceinline__ uint32_t record_bytes_sel(uint32_t d, uint32_t b) {
+    const uint32_t q = (4u * (d / kCardGroup) + d * b / 8u + 15u) & ~15u;
+    const bool quant = (b == 2) | (b == 4) | (b == 8);
+    return b == 16 ? 2u * d : (quant ? q : 0u);
+}
+
+// The scan is one workgroup's chain of dependent steps (widths in, offsets
+// out) ahead of the pack / unpack grid, so it is kept short: every thread
+// works out the flags itself (no barrier to publish them), an invalid width
+// travels with the waves' totals (bit 31) instead of through a shared flag
+// that would need clearing first, and widths and offsets move 8 and 16 bytes
+// per access.
+__global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanLaunch sl) {
     constexpr int kScanWaves = kScanThreads / kWave;
+    constexpr uint32_t kBadBit = 0x80000000u;
+    const ScanParams& p = sl.s[blockIdx.x];
     __shared__ uint32_t wave_tot[kScanWaves];
-    __shared__ uint32_t bad;
-    __shared__ uint32_t flags_sh;
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid % kWave, w = tid / kWave;
-    if (tid == 0) bad = 0;
-    // The input card's header words (unpack and transcode), loaded before the
-    // scan so that their trip to memory overlaps the widths' rather than
-    // following it.
+    // The input card's header words (unpack and transcode), loaded first so
+    // that their trip to memory overlaps the widths'.
     uint32_t hw[7] = {};
     uint64_t hq[4] = {};
     if (!p.card_out && tid == 0) {
@@ -112,31 +127,38 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) hq[i] = h64[5 + i];
     }
-    __syncthreads();
     // With at most one chunk of tokens (the common case) each thread keeps
     // its widths, which the pack then copies into the card from registers.
     const bool one_chunk = p.T <= (uint64_t)kScanThreads * kScanItems;
+    const bool vec = ((uintptr_t)p.widths & 7) == 0;
     uint8_t wv[kScanItems] = {};
     // Chunks of kScanThreads * kScanItems tokens: each thread sums its
     // tokens' record sizes, the wave scans the sums with lane shifts, and the
-    // waves' totals go through LDS (two barriers per chunk). A chunk's bytes
-    // fit 32 bits (at most 8192 records of at most 256 bytes).
+    // waves' totals go through LDS. A chunk's bytes fit 31 bits (at most 8192
+    // records of at most 512 bytes).
     uint64_t carry = 0;
+    bool bad = false;
     for (uint64_t base = 0; base < p.T; base += (uint64_t)kScanThreads * kScanItems) {
         const uint64_t t0 = base + (uint64_t)tid * kScanItems;
+        const bool whole = t0 + kScanItems <= p.T;
+        if (vec && whole) {
+            const uint2 u = *reinterpret_cast<const uint2*>(p.widths + t0);
+#pragma unroll
+            for (int i = 0; i < kScanItems; ++i) wv[i] = (uint8_t)((i < 4 ? u.x : u.y) >> (8 * (i % 4)));
+        } else {
+#pragma unroll
+            for (int i = 0; i < kScanItems; ++i) wv[i] = t0 + i < p.T ? p.widths[t0 + i] : 0;
+        }
         uint32_t rs[kScanItems];
         uint32_t local = 0;
+        bool my_bad = false;
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) {
-            uint32_t r = 0;
-            wv[i] = 0;
-            if (t0 + i < p.T) {
-                wv[i] = p.widths[t0 + i];
-                r = card_record_bytes(p.d, wv[i]);
-                if (r == 0) bad = 1;
-            }
-            rs[i] = r;
-            local += r;
+            const bool in = t0 + i < p.T;
+            const uint32_t r = record_bytes_sel(p.d, wv[i]);
+            my_bad |= in & (r == 0);
+            rs[i] = in ? r : 0u;
+            local += rs[i];
         }
         uint32_t inc = local;  // inclusive scan within the wave
 #pragma unroll
@@ -144,33 +166,46 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
             const uint32_t t = (uint32_t)__shfl_up((int)inc, o);
             if (lane >= (uint32_t)o) inc += t;
         }
-        if (lane == kWave - 1) wave_tot[w] = inc;
+        const bool wave_bad = __builtin_amdgcn_ballot_w64(my_bad) != 0;
+        if (lane == kWave - 1) wave_tot[w] = inc | (wave_bad ? kBadBit : 0u);
         __syncthreads();
-        uint32_t before = 0, chunk = 0;
+        uint32_t before = 0, chunk = 0, bad_bits = 0;
 #pragma unroll
         for (int k = 0; k < kScanWaves; ++k) {
             const uint32_t v = wave_tot[k];
-            before += (uint32_t)k < w ? v : 0u;
-            chunk += v;
+            bad_bits |= v;
+            before += (uint32_t)k < w ? (v & ~kBadBit) : 0u;
+            chunk += v & ~kBadBit;
         }
+        bad |= (bad_bits & kBadBit) != 0;
         uint64_t run = carry + before + inc - local;  // exclusive prefix of this thread
+        uint64_t o[kScanItems];
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) {
-            if (t0 + i < p.T) p.off[t0 + i] = run;
+            o[i] = run;
             run += rs[i];
         }
+        if (whole) {
+            // 16-byte stores: off is 16-byte aligned and t0 a multiple of 8
+#pragma unroll
+            for (int i = 0; i < kScanItems; i += 2)
+                *reinterpret_cast<ulonglong2*>(p.off + t0 + i) = make_ulonglong2(o[i], o[i + 1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kScanItems; ++i)
+                if (t0 + i < p.T) p.off[t0 + i] = o[i];
+        }
         carry += chunk;
-        __syncthreads();
+        if (base + (uint64_t)kScanThreads * kScanItems < p.T) __syncthreads();  // wave_tot is reused
     }
     const uint64_t S = align_up(carry, 256);
     const uint64_t payload = card_payload_offset(p.T);
     const uint64_t total = payload + 2ull * p.L * p.H * S;
+    uint32_t flags = bad ? kFlagBadWidth : 0u;
+    if (p.card_out && total > p.limit) flags |= kFlagCapacity;
     if (tid == 0) {
-        uint32_t flags = bad ? kFlagBadWidth : 0u;
         p.off[p.T] = carry;
         if (p.card_out) {
-            if (total > p.limit) flags |= kFlagCapacity;
-            if (p.prior_info && p.prior_info[2] != 0) flags |= kFlagInputRefused;
             if (p.dev_card_bytes) *p.dev_card_bytes = total;
             // a card that will not be written gets a zero magic word (the
             // buffer holds at least a header), so that nothing it held before
@@ -186,10 +221,8 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
         p.info[1] = total;
         p.info[2] = flags;
         if ((flags & kStatusBits) && p.status) atomicOr(p.status, (int)(flags & kStatusBits));
-        flags_sh = flags;
     }
-    __syncthreads();
-    if (!p.card_out || flags_sh) return;
+    if (!p.card_out || flags) return;
     // header (256 B) + widths + zero padding up to the payload
     uint32_t* hdr = reinterpret_cast<uint32_t*>(p.card_out);
     if (tid < 64) {
@@ -227,9 +260,20 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanParams p) {
     }
     if (one_chunk) {
         const uint64_t t0 = (uint64_t)tid * kScanItems;
+        if (t0 + kScanItems <= p.T) {
+            // card + 256 + t0 is 8-byte aligned
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i)
-            if (t0 + i < p.T) p.card_out[kCardHeaderBytes + t0 + i] = wv[i];
+            for (int i = 0; i < 4; ++i) {
+                lo |= (uint32_t)wv[i] << (8 * i);
+                hi |= (uint32_t)wv[4 + i] << (8 * i);
+            }
+            *reinterpret_cast<uint2*>(p.card_out + kCardHeaderBytes + t0) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kScanItems; ++i)
+                if (t0 + i < p.T) p.card_out[kCardHeaderBytes + t0 + i] = wv[i];
+        }
         for (uint64_t i = p.T + tid; i < payload - kCardHeaderBytes; i += kScanThreads)
             p.card_out[kCardHeaderBytes + i] = 0;
     } else {
@@ -670,12 +714,19 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
     const bool valid = tok < p.T;
     const uint32_t tc = valid ? tok : t0;
     const uint32_t nv = (p.T - t0 < TPW) ? p.T - t0 : TPW;
-    const uint64_t flags = p.info_in[2] | p.info_out[2];
+    const uint64_t f_in = p.info_in[2], f_out = p.info_out[2];
     const uint64_t S_in = p.info_in[0], S_out = p.info_out[0];
     const uint64_t a0 = p.off_in[t0], a1 = p.off_in[t0 + nv], my_a = p.off_in[tc];
     const uint64_t b0 = p.off_out[t0], b1 = p.off_out[t0 + nv], my_b = p.off_out[tc];
     const uint32_t w_in = p.w_in[tc], w_out = p.w_out[tc];
-    if (flags != 0) return;
+    if ((f_in | f_out) != 0) {
+        // A refused output card already has a zero magic word. A refused
+        // input (reported by its scan, which ran beside the output's) leaves
+        // an output whose header was written: its magic is zeroed here, so
+        // that it cannot pass for a transcode of the input.
+        if (f_in != 0 && f_out == 0 && wave == 0 && lane == 0) reinterpret_cast<uint32_t*>(p.card_out)[0] = 0;
+        return;
+    }
 
     // One LDS image per wave holds the input span, then the output span: every
     // lane's group reads (in the rebuild below, whatever its width) are issued
@@ -774,7 +825,8 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
                             const CardMetaDev& meta, void* card, uint64_t capacity,
                             uint64_t* dev_card_bytes, int32_t* dev_status, void* ws,
                             hipStream_t stream) {
-    ScanParams sp{};
+    ScanLaunch sl{};
+    ScanParams& sp = sl.s[0];
     sp.widths = widths;
     sp.card_out = static_cast<uint8_t*>(card);
     sp.card_in = nullptr;
@@ -788,7 +840,7 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
     sp.T = s.T;
     sp.d = s.d;
     sp.meta = meta;
-    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sp);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
     if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k = static_cast<const uint16_t*>(k);
@@ -802,7 +854,8 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
 
 hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_bytes, void* k_out,
                               void* v_out, int32_t* dev_status, void* ws, hipStream_t stream) {
-    ScanParams sp{};
+    ScanLaunch sl{};
+    ScanParams& sp = sl.s[0];
     sp.widths = static_cast<const uint8_t*>(card) + kCardHeaderBytes;
     sp.card_out = nullptr;
     sp.card_in = static_cast<const uint8_t*>(card);
@@ -815,7 +868,7 @@ hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_by
     sp.H = s.H;
     sp.T = s.T;
     sp.d = s.d;
-    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sp);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
     if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k_out = static_cast<uint16_t*>(k_out);
@@ -832,8 +885,11 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
                                  uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, hipStream_t stream) {
     uint8_t* ws_in = static_cast<uint8_t*>(ws);
     uint8_t* ws_out = ws_in + card_workspace_half(s.T);
-    // offsets of the input records (and a check of its header) ...
-    ScanParams a{};
+    // offsets of the input records (and a check of its header), and of the
+    // output's, whose header and widths are written with the input's model ID
+    // and position offset: two workgroups of one launch
+    ScanLaunch sl{};
+    ScanParams& a = sl.s[0];
     a.widths = static_cast<const uint8_t*>(card_in) + kCardHeaderBytes;
     a.card_in = static_cast<const uint8_t*>(card_in);
     a.info = reinterpret_cast<uint64_t*>(ws_in);
@@ -844,11 +900,7 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
     a.H = s.H;
     a.T = s.T;
     a.d = s.d;
-    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, a);
-    if (e != hipSuccess) return e;
-    // ... and of the output's, whose header and widths are written with the
-    // input's model ID and position offset
-    ScanParams b{};
+    ScanParams& b = sl.s[1];
     b.widths = new_widths;
     b.card_out = static_cast<uint8_t*>(card_out);
     b.info = reinterpret_cast<uint64_t*>(ws_out);
@@ -861,8 +913,7 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
     b.T = s.T;
     b.d = s.d;
     b.meta_src = static_cast<const uint8_t*>(card_in);
-    b.prior_info = a.info;
-    e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, b);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(2), dim3(kScanThreads), stream, sl);
     if (e != hipSuccess) return e;
     const CardParams cp = card_params(s, ws);
     TranscodeParams p{};
