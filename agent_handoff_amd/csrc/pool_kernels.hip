@@ -35,8 +35,10 @@
 #include "layout.h"
 
 #include <atomic>
+#include <chrono>
 #include <cstdlib>
 #include <mutex>
+#include <random>
 #include <utility>
 
 // Encode workspace held by the library for kvpool_encode_noalloc (callers
@@ -74,10 +76,10 @@ struct EncodeParams {
 //  - Single pass: one 64-bit exchange word per (layer, workgroup) that its
 //    workgroup publishes and every workgroup reads, some before it is
 //    written. Each call tags the words it writes with a call number of its
-//    own (48 bits, from a per-process counter on the host, never reused): a
-//    word counts only if it carries this call's number, so words left by
-//    earlier calls (or zeros) are never taken for this call's, and nothing
-//    needs clearing between calls. Head words [2..3]: the number of a call
+//    own (48 bits, from a host counter of the library instance that starts
+//    at a random point and skips 0): a word counts only if it carries this
+//    call's number, so words left by earlier calls (or zeros) are not taken
+//    for this call's, and nothing needs clearing between calls. Head words [2..3]: the number of a call
 //    whose wait gave up (64 bits).
 //  - Two passes: the key-maximum pass stores each workgroup's partial
 //    maximum of a layer in a word of its own, at the end of the region
@@ -86,7 +88,7 @@ struct EncodeParams {
 // A single-pass word is (call << 16) | 0x8000 | maximum bits (15 bits): a
 // pair of two-pass words (each below 0x8000) never has bit 15 set, so it
 // cannot pass for one. The workspace must hold zeros before its first
-// single-pass encode (zero never matches a call number, which starts at 1).
+// single-pass encode (zero never matches a call number).
 constexpr uint32_t kMaxAbsmaxGroups = 64;
 constexpr uint32_t kWsHead = 64;              // words
 constexpr uint32_t kWsWordsPerLayer = 1024;  // = encode_workspace_words(L) / L, less the head
@@ -1091,11 +1093,26 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
 // wait for their coordinator.
 constexpr uint64_t kMaxPollUs = 5000;
 
-// Call numbers of the single-pass encode: unique within the process, from
-// 1 (a zeroed workspace word never matches), 48 bits (never wrap).
+// Call numbers of the single-pass encode (the tags of its exchange words):
+// consecutive within one instance of the library, 48 bits, never 0 (a
+// zeroed workspace word never matches). Each instance starts at a random
+// point, so a workspace used by one instance and then by another holds no
+// word carrying the other's current tag, bar a 2^-48 coincidence.
+static uint64_t first_call_number() {
+    uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    try {
+        std::random_device rd;
+        x ^= ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+    } catch (...) {
+    }
+    return x;
+}
 uint64_t next_call_number() {
-    static std::atomic<uint64_t> counter{1};
-    return counter.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+    static std::atomic<uint64_t> counter{first_call_number()};
+    for (;;) {
+        const uint64_t c = counter.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+        if (c != 0) return c;
+    }
 }
 uint64_t encode_poll_ticks() {
     uint64_t us = 200;

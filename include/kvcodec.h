@@ -28,8 +28,10 @@
  *    row = one head vector; d is 64 or 128.
  *  - Pointers are device memory unless marked "host". Device pointers must
  *    be 16-byte aligned (pools and cards 256-byte aligned).
- *  - The caller owns every buffer. The library allocates and frees nothing
- *    and keeps no state between calls; size queries give every buffer size.
+ *  - The caller owns every buffer; size queries give every buffer size. The
+ *    library allocates and frees nothing (kvpool_encode_noalloc's per-GPU
+ *    array is part of the library's device image). Between calls it keeps
+ *    only the encode's call counter and the addresses of those arrays.
  *  - Device work is enqueued on `stream` and is asynchronous: synchronise
  *    before reading outputs, byte counts or status words on the host.
  *  - Host-detectable errors return a negative KVC_E_* code before anything is
@@ -109,7 +111,9 @@ size_t kvpool_bytes(const kvc_shape* shape);
  * after allocation) and must not be written by anything else afterwards;
  * it then serves any number of encodes in sequence, of any shapes, with no
  * clearing in between (each call tags the words it writes with a number of
- * its own, and ignores words that carry another). */
+ * its own, and ignores words that carry another; the numbers run on from a
+ * random start in each loaded instance of the library, so a workspace may
+ * also pass from one instance to another). */
 size_t kvpool_workspace_bytes(const kvc_shape* shape);
 
 /* Compress bf16 K and V ([L][H][T][d]) into `pool` (PolyKV 2.B items 1-2).
