@@ -39,11 +39,15 @@ constexpr uint32_t kStatusBits = kFlagBadHeader | kFlagBadWidth | kFlagCapacity;
 // work exit). Measured on the Llama 4K card with the configs' width mix:
 // unpack 151 -> 132 us with C = 64 (one stream of 4096 tokens per run; 16:
 // 134, 128: 136), pack 144 -> 135 us with C = 16, transcode 130 -> 126 us
-// with C = 64.
+// with C = 64. The transcode runs one wave per workgroup: a workgroup's LDS
+// is released only when its slowest wave ends, and the transcode's waves
+// differ in length with their widths (99.1 -> 92.3 us; pack and unpack,
+// shorter and alike, run slower that way: 134 -> 139, 128 -> 134 us).
 constexpr uint32_t kXcdCount = 8;
 constexpr uint32_t kUnpackXcdRun = 64;
 constexpr uint32_t kPackXcdRun = 16;
-constexpr uint32_t kTranscodeXcdRun = 64;
+constexpr uint32_t kTranscodeXcdRun = 256;  // one-wave workgroups: one stream per run
+constexpr int kTranscodeThreads = kWave;
 
 template <uint32_t C>
 __device__ __forceinline__ uint64_t xcd_run_block(uint32_t b) {
@@ -701,11 +705,11 @@ struct TranscodeParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(TranscodeParams p) {
+__global__ __launch_bounds__(kTranscodeThreads) void card_transcode_kernel(TranscodeParams p) {
     constexpr uint32_t G = D / kCardGroup;  // lanes per token
     constexpr uint32_t TPW = kWave / G;     // tokens per wave
     const uint32_t lane = lane_id();
-    const uint64_t wave = xcd_run_block<kTranscodeXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    const uint64_t wave = xcd_run_block<kTranscodeXcdRun>(blockIdx.x) * (kTranscodeThreads / kWave) + wave_uniform(threadIdx.x / kWave);
     if (wave >= p.n_waves) return;
     const uint64_t s = wave / p.nbk;
     const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
@@ -733,7 +737,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_transcode_kernel(Transcode
     // before any lane's group writes, and a wave's LDS operations complete in
     // order. (A second image doubled the LDS of a workgroup and halved the
     // waves a CU can hold.)
-    __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
+    __shared__ uint4 stage[kTranscodeThreads / kWave][kSpanChunks];
     uint4* si = stage[threadIdx.x / kWave];
     uint4* so = si;
     {
@@ -931,9 +935,9 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
     p.nbk = cp.nbk;
     p.payload = cp.payload;
     p.n_waves = cp.n_waves;
-    const uint32_t nblocks = xcd_run_grid<kTranscodeXcdRun>((p.n_waves + 3) / 4);
+    const uint32_t nblocks = xcd_run_grid<kTranscodeXcdRun>(p.n_waves);
     return launch_kernel(s.d == 64 ? card_transcode_kernel<64> : card_transcode_kernel<128>, dim3(nblocks),
-                         dim3(kBlockThreads), stream, p);
+                         dim3(kTranscodeThreads), stream, p);
 }
 
 }  // namespace kvc
