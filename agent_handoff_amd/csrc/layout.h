@@ -47,10 +47,10 @@ KVC_HD PoolLayout pool_layout(uint32_t L, uint32_t H, uint32_t T, uint32_t d) {
     return p;
 }
 
-// kvpool_encode workspace: 64 head words, then a region used by one path
-// per call: per layer 64 partial-max words (two-pass encode) or one flag
-// word per workgroup of the single-pass encode (fewer than 1024 workgroups)
-// plus one count.
+// kvpool_encode workspace: 64 head words, then 1024 words per layer for the
+// 64-bit exchange words of one path per call: one per workgroup of the
+// single-pass encode (at most 512), or one per key-maximum workgroup of the
+// layered encode (at most 256).
 KVC_HD uint64_t encode_workspace_words(uint32_t L) { return 64u + (uint64_t)L * 1024u; }
 
 KVC_HD bool card_shape_ok(uint32_t L, uint32_t H, uint32_t T, uint32_t d) {

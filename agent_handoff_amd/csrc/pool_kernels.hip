@@ -66,38 +66,29 @@ struct EncodeParams {
     uint32_t layers_per_round;  // single-pass encode: whole layers per round
     uint64_t n_waves;           // L * H * nb
     uint64_t poll_ticks;        // single-pass encode: bound on the wait for other workgroups' maxima
-    uint32_t absmax_groups;     // two-pass encode: key-maximum workgroups per layer
-    uint64_t call;              // single-pass encode: this call's number (tags its exchange words)
+    uint32_t absmax_groups;     // layered encode: key-maximum workgroups per layer
+    uint32_t encode_groups;     // layered encode: encode workgroups per layer
+    uint64_t call;              // this call's number (tags its exchange words)
     PoolLayout lay;
 };
 
 // Encode workspace (u32 words): 64 head words, then kWsWordsPerLayer words
-// per layer, used by one of two paths per call.
-//  - Single pass: one 64-bit exchange word per (layer, workgroup) that its
-//    workgroup publishes and every workgroup reads, some before it is
-//    written. Each call tags the words it writes with a call number of its
-//    own (48 bits, from a host counter of the library instance that starts
-//    at a random point and skips 0): a word counts only if it carries this
-//    call's number, so words left by earlier calls (or zeros) are not taken
-//    for this call's, and nothing needs clearing between calls. Head words [2..3]: the number of a call
-//    whose wait gave up (64 bits).
-//  - Two passes: the key-maximum pass stores each workgroup's partial
-//    maximum of a layer in a word of its own, at the end of the region
-//    (kMaxAbsmaxGroups words per layer), and the encode pass reads them:
-//    every word read is written earlier in the same call.
-// A single-pass word is (call << 16) | 0x8000 | maximum bits (15 bits): a
-// pair of two-pass words (each below 0x8000) never has bit 15 set, so it
-// cannot pass for one. The workspace must hold zeros before its first
-// single-pass encode (zero never matches a call number).
-constexpr uint32_t kMaxAbsmaxGroups = 64;
+// per layer. Both encode paths exchange 64-bit words that one workgroup
+// publishes and others read, some before it is written: the single pass one
+// per (layer, workgroup), the layered encode one per (layer, key-maximum
+// workgroup). Each call tags the words it writes with a call number of its
+// own (48 bits, from a host counter of the library instance that starts at
+// a random point and skips 0): a word is (call << 16) | 0x8000 | maximum
+// bits (15 bits), and it counts only if it carries this call's number, so
+// words left by earlier calls of either path (or zeros) are not taken for
+// this call's, and nothing needs clearing between calls. The workspace must
+// hold zeros before its first encode (zero never matches a call number).
+// Head words [2..3]: the number of a call whose wait gave up (64 bits).
 constexpr uint32_t kWsHead = 64;              // words
 constexpr uint32_t kWsWordsPerLayer = 1024;  // = encode_workspace_words(L) / L, less the head
 constexpr uint32_t kWsGaveUp = 2;             // u64 at words 2..3
 constexpr int32_t kDevTimeout = 8;            // KVC_DEV_ENCODE_TIMEOUT
 
-__device__ __forceinline__ uint32_t* absmax_slot(uint32_t* ws, uint32_t L, uint32_t l, uint32_t s) {
-    return ws + kWsHead + (uint64_t)L * (kWsWordsPerLayer - kMaxAbsmaxGroups) + (uint64_t)l * kMaxAbsmaxGroups + s;
-}
 
 
 struct DecodeParams {
@@ -199,55 +190,6 @@ __device__ void pool_header_and_padding(const EncodeParams& p, uint32_t d, uint3
 __global__ void fill_zero_kernel(uint4* p, uint32_t n4) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n4) p[i] = make_uint4(0, 0, 0, 0);
-}
-
-// Per-layer max |K| (PolyKV 2.B item 1: one linear scale per tensor). For
-// bf16, |x| ordering equals integer ordering of the bits with the sign
-// cleared, so the maximum is taken on 16-bit integers (packed max, two
-// values per instruction). Workgroup x of layer l (gridDim.x <=
-// kMaxAbsmaxGroups) stores its partial maximum in word x of the layer.
-__global__ __launch_bounds__(kBlockThreads) void key_absmax_kernel(const uint4* __restrict__ k,
-                                                                  uint64_t per_layer_u4, uint32_t L,
-                                                                  uint32_t* __restrict__ ws) {
-    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-    const uint32_t l = blockIdx.y;
-    const uint4* src = k + (uint64_t)l * per_layer_u4;
-    us2 mx = {0, 0};
-    // kUnroll independent 16-byte loads in flight per thread
-    constexpr uint32_t kUnroll = 8;
-    const uint64_t stride = (uint64_t)gridDim.x * kBlockThreads;
-    for (uint64_t i0 = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x; i0 < per_layer_u4;
-         i0 += kUnroll * stride) {
-        // past the end, re-load the last element: max is idempotent, and the
-        // loads stay unconditional (no branch between them)
-        uint4 w[kUnroll];
-#pragma unroll
-        for (uint32_t j = 0; j < kUnroll; ++j) {
-            const uint64_t i = i0 + j * stride;
-            w[j] = src[i < per_layer_u4 ? i : per_layer_u4 - 1];
-        }
-#pragma unroll
-        for (uint32_t j = 0; j < kUnroll; ++j) {
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].x & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].y & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].z & 0x7FFF7FFFu));
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[j].w & 0x7FFF7FFFu));
-        }
-    }
-    uint32_t r = mx.x > mx.y ? mx.x : mx.y;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
-        r = t > r ? t : r;
-    }
-    __shared__ uint32_t red[kBlockThreads / kWave];
-    if (lane_id() == 0) red[threadIdx.x / kWave] = r;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int w = 1; w < kBlockThreads / kWave; ++w) r = red[w] > r ? red[w] : r;
-        *absmax_slot(ws, L, l, blockIdx.x) = r;
-    }
 }
 
 // Coordinate I of the lane: code = number of thresholds <= z, found bit by
@@ -423,34 +365,10 @@ __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const Block
             finite ? __float_as_uint((mk == 0.0f) ? 0.0f : mk / 127.0f) : 0x7FC00000u;
 }
 
-// Two passes: the per-layer key maxima were reduced by key_absmax_kernel;
-// one wave per 16-token block.
-template <int D>
-__global__ __launch_bounds__(kBlockThreads) void pool_encode_kernel(EncodeParams p) {
-    constexpr int WPB = kBlockThreads / kWave;
-    __shared__ EncodeStage<D> stage_all[WPB];
-    const uint32_t lane = lane_id();
-    const uint32_t wib = wave_uniform(threadIdx.x / kWave);
-    if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
-    const uint64_t wave = (uint64_t)blockIdx.x * WPB + wib;
-    if (wave >= p.n_waves) return;
-    const BlockPos b = block_pos<D>(p, (uint32_t)(wave / p.blocks_per_layer), (uint32_t)(wave % p.blocks_per_layer),
-                                    lane);
-    uint4 kraw[D / 32], vraw[D / 32];
-    load_lane<D>(p.k, b.elem, kraw);
-    load_lane<D>(p.v, b.elem, vraw);
-    encode_values<D>(p, b, vraw, stage_all[wib], lane);
-    // the layer's partial maxima, one per key-maximum workgroup (lane i reads
-    // word i), reduced across the wave
-    const uint32_t part = lane < p.absmax_groups ? *absmax_slot(p.ws, p.L, b.l, lane) : 0u;
-    const uint32_t mbits = wave_max_u32(part);
-    quantize_keys<D>(p, b, kraw, mbits, stage_all[wib], lane);
-}
-
 // ---------------------------------------------------------------- single-pass encode
 //
-// The key scale of a layer needs every key of the layer, so the two-pass
-// encode reads K twice. Here K is read once and parked in LDS: a
+// The key scale of a layer needs every key of the layer before any key is
+// quantised. Here K is read once and parked in LDS: a
 // persistent grid (one workgroup per CU at this LDS size) walks the layers
 // in rounds of whole layers. A workgroup owns 8 block slots per round (one
 // 16-token block each at d = 128, two at d = 64) and splits the work by
@@ -491,6 +409,7 @@ constexpr int kHoldRounds = kQuantLag + 1;  // LDS key buffers and handshake ent
 constexpr uint32_t kMaxRoundLayers = 32;
 constexpr uint32_t kMaxFusedGrid = 1024;  // bound on the grid (the launch keeps it below 960); sizes the poll registers
 constexpr uint64_t kWordFlag = 0x8000u;
+constexpr uint32_t kLayeredMaxGroups = 256;  // layered encode: bound on the key-maximum workgroups per layer
 // Spin limit of the waits inside a workgroup (key waves for their
 // coordinator, coordinator for its key waves), in ticks of the 100 MHz
 // constant clock: 0.5 s. These waits depend only on the workgroup's own
@@ -1082,6 +1001,127 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
     st_stream(p.dst[s] + e, x);
 }
 
+// ---------------------------------------------------------------- layered encode
+//
+// Shapes whose layer does not fit a round of the single pass (long contexts:
+// a Llama 32K layer holds 67 MB of keys) still read each key once from HBM.
+// One ordinary launch lays its workgroups out in layer order,
+//     [max 0] [max 1][encode 0] [max 2][encode 1] ... [max L-1][encode L-2] [encode L-1],
+// A workgroups of each "max" segment, E of each "encode" segment. A "max l"
+// workgroup reads its share of layer l's keys and publishes the share's
+// largest magnitude as a tagged word, (call << 16) | 0x8000 | bits, one per
+// (layer, workgroup). An "encode l" workgroup (one 16-token block per wave)
+// issues its key and value loads, then reads layer l's A words until all
+// carry this call's number, takes their maximum, quantises the keys and
+// encodes the values. Measured on the Llama 32K pool: 1226 us against 1377
+// us for a key-maximum pass over all layers followed by the encode (the
+// keys read twice from HBM), bit-identical. Workgroups are dispatched in order on each XCD, so a wave waits
+// only on workgroups dispatched before it, about one segment earlier; and the
+// keys it re-reads were read by the max workgroups one period before, with
+// the period's other traffic (one layer's values, pool and the next layer's
+// keys) in between, within the 256 MB Infinity Cache. A wait that runs past
+// the poll bound reads the layer's keys itself: the maximum is exact either
+// way, residency decides only the speed.
+__device__ __forceinline__ uint64_t* layered_words(uint32_t* ws, uint32_t A, uint32_t l) {
+    return reinterpret_cast<uint64_t*>(ws + kWsHead) + (uint64_t)l * A;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void pool_encode_layered_kernel(EncodeParams p) {
+    constexpr int WPB = kBlockThreads / kWave;
+    __shared__ EncodeStage<D> stage_all[WPB];
+    __shared__ uint32_t red[WPB];
+    const uint32_t lane = lane_id();
+    const uint32_t wib = wave_uniform(threadIdx.x / kWave);
+    if (blockIdx.x == 0) pool_header_and_padding(p, D, threadIdx.x);
+    const uint32_t A = p.absmax_groups, E = p.encode_groups;
+    // this workgroup's role, layer and index within its segment
+    bool is_max;
+    uint32_t layer, idx;
+    {
+        const uint64_t b = blockIdx.x, per = (uint64_t)A + E;
+        if (b < A) {
+            is_max = true;
+            layer = 0;
+            idx = (uint32_t)b;
+        } else if (b - A < (uint64_t)(p.L - 1) * per) {
+            const uint64_t q = (b - A) / per, m = (b - A) % per;
+            is_max = m < A;
+            layer = is_max ? (uint32_t)q + 1 : (uint32_t)q;
+            idx = is_max ? (uint32_t)m : (uint32_t)(m - A);
+        } else {
+            is_max = false;
+            layer = p.L - 1;
+            idx = (uint32_t)(b - A - (uint64_t)(p.L - 1) * per);
+        }
+    }
+    const uint64_t tag = (p.call << 16) | kWordFlag;
+    if (is_max) {
+        // share idx of the layer's keys (16-byte units), 8 loads in flight per thread
+        const uint64_t n = (uint64_t)p.H * p.T * (D / 8);
+        const uint64_t per_g = (n + A - 1) / A;
+        const uint64_t lo = (uint64_t)idx * per_g, hi = lo + per_g < n ? lo + per_g : n;
+        const uint4* src = reinterpret_cast<const uint4*>(p.k) + (uint64_t)layer * n;
+        uint32_t m = 0;
+        for (uint64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 8 * kBlockThreads) {
+            uint4 w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t i = i0 + (uint64_t)j * kBlockThreads;
+                w[j] = src[i < hi ? i : hi - 1];  // past the share: its last unit again (max is idempotent)
+            }
+            const uint32_t x = lane_absmax_bits<8>(w);
+            m = x > m ? x : m;
+        }
+        m = wave_max_u32(m);
+        if (lane == 0) red[wib] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int w = 1; w < WPB; ++w) m = red[w] > m ? red[w] : m;
+            __hip_atomic_store(layered_words(p.ws, A, layer) + idx, tag | m, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    const uint32_t blk = idx * WPB + wib;
+    if (blk >= p.blocks_per_layer) return;
+    const BlockPos b = block_pos<D>(p, layer, blk, lane);
+    uint4 kraw[D / 32], vraw[D / 32];
+    load_lane<D>(p.k, b.elem, kraw);
+    load_lane<D>(p.v, b.elem, vraw);
+    // the layer's A words (lane i reads words i, i + 64, ...), again until all
+    // carry this call's number or the poll bound runs out
+    constexpr int kPer = kLayeredMaxGroups / kWave;
+    const uint64_t* f = layered_words(p.ws, A, layer);
+    const uint64_t start = wall_clock64();
+    uint32_t mx = 0;
+    bool all_flagged = false;
+    for (;;) {
+        bool all = true;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t g = lane + (uint32_t)i * kWave;
+            const uint64_t w = g < A ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+            all = all && ((w & ~0x7FFFull) == tag);
+            const uint32_t x = (uint32_t)(w & 0x7FFFu);
+            m = x > m ? x : m;
+        }
+        if (p.poll_ticks != 0 && __builtin_amdgcn_ballot_w64(!all) == 0) {
+            mx = wave_max_u32(m);
+            all_flagged = true;
+            break;
+        }
+        if (wall_clock64() - start >= p.poll_ticks) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (!all_flagged) mx = layer_absmax_direct<D>(p, layer, lane);
+    // keys first: their registers are free before the value transform's
+    quantize_keys<D>(p, b, kraw, mx, stage_all[wib], lane);
+    encode_values<D>(p, b, vraw, stage_all[wib], lane);
+}
+
 // Bound on a coordinator's wait for the other workgroups' key maxima, in
 // ticks of the 100 MHz constant clock. Default 200 us: a resident grid
 // publishes a round within a few microseconds, so the bound trips only for
@@ -1170,22 +1210,22 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
     p.n_waves = (uint64_t)s.L * p.blocks_per_layer;
     p.poll_ticks = encode_poll_ticks();
     p.absmax_groups = 0;
+    p.encode_groups = 0;
     p.call = next_call_number();
     p.lay = pool_layout(s.L, s.H, s.T, s.d);
 
     // Single pass when a round of whole layers fits the LDS of a grid of one
-    // workgroup per CU; otherwise two passes (the per-layer key maxima, then
-    // the encode proper). The single pass is an ordinary launch: its waits
-    // never depend on every workgroup being resident (see the kernel). Its
-    // exchange words (two u32 words per layer and workgroup) must leave the
-    // two-pass words at the end of each layer's share free.
+    // workgroup per CU; otherwise the layered encode. Both are ordinary
+    // launches whose waits never depend on a workgroup dispatched after the
+    // waiting one (see the kernels). The single pass's exchange words (two
+    // u32 words per layer and workgroup) must fit each layer's share.
     const void* fused = s.d == 64 ? reinterpret_cast<const void*>(pool_encode_fused_kernel<64>)
                                   : reinterpret_cast<const void*>(pool_encode_fused_kernel<128>);
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused, kFusedThreads, 0) == hipSuccess && per_cu > 0 &&
-        2 * (uint64_t)cus * (uint64_t)per_cu <= kWsWordsPerLayer - kMaxAbsmaxGroups &&
+        2 * (uint64_t)cus * (uint64_t)per_cu <= kWsWordsPerLayer &&
         (uint64_t)cus * (uint64_t)per_cu <= kMaxFusedGrid) {
         const uint64_t grid = (uint64_t)cus * (uint64_t)per_cu;
         const uint64_t per_round = grid * kFusedSlots * (128u / s.d);  // blocks a round can hold
@@ -1199,16 +1239,20 @@ hipError_t launch_pool_encode(const Shape& s, const void* k, const void* v, void
                                  "pool_encode_fused_kernel");
         }
     }
+    // Layered: per layer, A key-maximum workgroups (each 16 16-byte units
+    // per thread or more, at most kLayeredMaxGroups) and the encode
+    // workgroups, in layer order in one launch.
     const uint64_t per_layer_u4 = (uint64_t)s.H * s.T * s.d / 8;
-    uint64_t gx = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
-    if (gx > kMaxAbsmaxGroups) gx = kMaxAbsmaxGroups;
-    p.absmax_groups = (uint32_t)gx;
-    hipError_t e = launch_kernel(key_absmax_kernel, dim3((uint32_t)gx, s.L), dim3(kBlockThreads), stream,
-                                 static_cast<const uint4*>(k), per_layer_u4, s.L, ws);
-    if (e != hipSuccess) return e;
-    const uint64_t nblocks = (p.n_waves + 3) / 4;
-    return launch_kernel(s.d == 64 ? pool_encode_kernel<64> : pool_encode_kernel<128>, dim3((uint32_t)nblocks),
-                         dim3(kBlockThreads), stream, p);
+    uint64_t A = (per_layer_u4 + 16 * kBlockThreads - 1) / (16 * kBlockThreads);
+    if (A > kLayeredMaxGroups) A = kLayeredMaxGroups;
+    if (A == 0) A = 1;
+    const uint64_t E = (p.blocks_per_layer + kBlockThreads / kWave - 1) / (kBlockThreads / kWave);
+    p.absmax_groups = (uint32_t)A;
+    p.encode_groups = (uint32_t)E;
+    const uint64_t nblocks = (uint64_t)s.L * (A + E);
+    if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    return launch_kernel(s.d == 64 ? pool_encode_layered_kernel<64> : pool_encode_layered_kernel<128>,
+                         dim3((uint32_t)nblocks), dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_pool_decode(const Shape& s, const void* pool, uint32_t l0, uint32_t l1,

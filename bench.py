@@ -536,8 +536,7 @@ def hop_drift(kv, synth, k, v, shape, widths_np, seed, stream, dev, hops=5):
 
 
 CALIBRATION_BYTES = 1 << 30
-CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_kernel",
-                 "key_absmax_kernel",
+CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_layered_kernel",
                  "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
                  "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel",
                  "fac_zx_kernel", "fac_ztq_kernel"]
@@ -606,7 +605,7 @@ def other_configs(args):
         reps = 20 if cfg != 5 else 8
         te = timed(lambda: kv.kvpool_encode(shape, k, v, pool, ws, stream=stream), reps)
         emit(w, "encode", te, 2 * kv_bytes + pool_b,
-             path="single pass" if cfg != 5 else "two passes (a layer exceeds one round)")
+             path="single pass" if cfg != 5 else "layered (a layer exceeds one round)")
         if cfg == 5:
             ko = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
             vo = torch.empty_like(ko)

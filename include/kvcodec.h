@@ -133,10 +133,12 @@ size_t kvpool_workspace_bytes(const kvc_shape* shape);
  * comparisons of its (non-finite) rotated coordinates (NaN: code 0).
  * Values: per vector, s = fp16(sqrt(sum x^2 / d)), y = H x (Sylvester
  * order), z = y / (sqrt(d) s), code = number of Lloyd-Max thresholds <= z.
- * Execution: where a round of whole layers fits the LDS of one workgroup per
- * CU, one kernel reads K once (keys wait in LDS for their layer's maximum);
- * otherwise a key-maximum pass runs first. The single pass is an ordinary
- * launch: a workgroup that has not received every other workgroup's key
+ * Execution: one kernel, which reads each key once from memory. Where a
+ * round of whole layers fits the LDS of one workgroup per CU, keys wait in
+ * LDS for their layer's maximum; otherwise (long contexts) workgroups that
+ * take a layer's maximum run one layer ahead of those that encode it, which
+ * re-read the keys shortly after (from the GPU's cache, not HBM). Both are
+ * ordinary launches: a wave that has not received every workgroup's key
  * maximum for a layer within a bound (200 us by default; environment
  * variable KVC_ENCODE_POLL_US, read at each call, 0 = always) reads the
  * layer's keys itself (values above 5000 are ignored). The pool is the

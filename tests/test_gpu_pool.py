@@ -248,7 +248,7 @@ def test_encode_many_blocks_per_layer(shape, cfg):
     """Layers of hundreds of 16-token blocks: the key max is reduced over
     many workgroups before any key is coded. On a 256-CU GPU a single-pass
     round holds 2048 blocks at d = 128 and 4096 at d = 64, so the 4112- and
-    2064-token shapes (2056 and 4128 blocks per layer) take the two-pass
+    2064-token shapes (2056 and 4128 blocks per layer) take the layered
     encode; 40 one-block layers take more than one round of 32 layers."""
     say("encode", shape)
     k, v = _inputs(shape, cfg, 4)
@@ -257,7 +257,7 @@ def test_encode_many_blocks_per_layer(shape, cfg):
 
 def test_one_workspace_serves_encodes_in_sequence():
     """A workspace zeroed once serves encodes of different shapes, data and
-    paths in a row (single pass, two passes, single pass again with other
+    paths in a row (single pass, layered, single pass again with other
     layer counts, and the first shape again): each pool bit-exact, so no
     word an earlier call left behind is taken for a later call's."""
     calls = [((3, 8, 512, 128), 3), ((2, 8, 4112, 128), 3), ((5, 2, 77, 64), 1), ((40, 1, 16, 64), 1),

@@ -4,7 +4,7 @@ a caller workspace, called through the C ABI on the same seeded inputs.
 
 Bar: the two pools are byte-identical (codes, scales, header, padding), on
 two calls in a row, the second with a smaller input; the first call takes
-the two-pass path (a layer larger than one round of the single-pass grid),
+the layered path (a layer larger than one round of the single-pass grid),
 the second the single pass, so the second also shows that what the first
 left in the scratch does not leak into it."""
 
@@ -35,7 +35,7 @@ def _pool_both_ways(shape, cfg, seed):
 
 def test_noalloc_encode_equals_workspace_encode():
     # d = 128, 8 heads x 4200 tokens: 2104 blocks per layer, more than a
-    # round of 256 workgroups x 8 slots holds -> two-pass path
+    # round of 256 workgroups x 8 slots holds -> layered path
     calls = [((2, 8, 4200, 128), 3, 11), ((3, 4, 300, 64), 2, 12)]
     for shape, cfg, seed in calls:
         say("noalloc encode", shape, "recipe", cfg, "seed", seed)
