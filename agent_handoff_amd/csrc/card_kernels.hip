@@ -96,7 +96,60 @@ struct CardParams {
     uint32_t L, H, T, nbk;  // nbk = token blocks per stream
     uint64_t payload;
     uint64_t n_waves;
+    // offsets computed in the grid (see ingrid_scan): what the scan kernel
+    // would otherwise check and write
+    uint64_t limit;            // pack: capacity; unpack: card bytes
+    uint64_t* dev_card_bytes;  // pack, nullable
+    int32_t* status;           // nullable
+    CardMetaDev meta;          // pack
 };
+
+// Word i (< 64) of a card's 256-byte header.
+__device__ __forceinline__ uint32_t card_header_word(uint32_t i, uint32_t L, uint32_t H, uint32_t T, uint32_t d,
+                                                     uint64_t payload, uint64_t S, uint64_t total,
+                                                     const CardMetaDev& meta, const uint8_t* meta_src) {
+    uint32_t val = 0;
+    switch (i) {
+        case 0: val = kCardMagic; break;
+        case 1: val = 1u | (2u << 16); break;  // version 1, kind 2
+        case 2: val = L; break;
+        case 3: val = H; break;
+        case 4: val = T; break;
+        case 5: val = d; break;
+        case 6: val = kCardGroup; break;
+        case 8: val = (uint32_t)(uint64_t)meta.position_offset; break;
+        case 9: val = (uint32_t)((uint64_t)meta.position_offset >> 32); break;
+        case 10: val = kCardHeaderBytes; break;
+        case 12: val = (uint32_t)payload; break;
+        case 13: val = (uint32_t)(payload >> 32); break;
+        case 14: val = (uint32_t)S; break;
+        case 15: val = (uint32_t)(S >> 32); break;
+        case 16: val = (uint32_t)total; break;
+        case 17: val = (uint32_t)(total >> 32); break;
+        default:
+            if (i >= 18 && i < 34) {
+                const int c = (int)(i - 18) * 4;
+                val = (uint32_t)(uint8_t)meta.model_id[c] | ((uint32_t)(uint8_t)meta.model_id[c + 1] << 8) |
+                      ((uint32_t)(uint8_t)meta.model_id[c + 2] << 16) |
+                      ((uint32_t)(uint8_t)meta.model_id[c + 3] << 24);
+            }
+    }
+    if (meta_src && (i == 8 || i == 9 || (i >= 18 && i < 34))) {
+        val = reinterpret_cast<const uint32_t*>(meta_src)[i];
+        if (i == 33) val &= 0x00FFFFFFu;  // at most 63 characters, NUL-terminated
+    }
+    return val;
+}
+
+// Whether a card's header matches the shape and the sizes its widths give.
+__device__ __forceinline__ bool card_header_ok(const uint8_t* card, uint32_t L, uint32_t H, uint32_t T, uint32_t d,
+                                               uint64_t payload, uint64_t S, uint64_t total, uint64_t limit) {
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(card);
+    const uint64_t* h64 = reinterpret_cast<const uint64_t*>(card);
+    return h[0] == kCardMagic && h[1] == (1u | (2u << 16)) && h[2] == L && h[3] == H && h[4] == T && h[5] == d &&
+           h[6] == kCardGroup && h64[5] == kCardHeaderBytes && h64[6] == payload && h64[7] == S && h64[8] == total &&
+           total <= limit;
+}
 
 // card_record_bytes as selects (the scan takes it for 8 tokens per thread;
 // the branches of the general form cost a divergent region per token)
@@ -104,6 +157,20 @@ __device__ __forceinline__ uint32_t record_bytes_sel(uint32_t d, uint32_t b) {
     const uint32_t q = (4u * (d / kCardGroup) + d * b / 8u + 15u) & ~15u;
     const bool quant = (b == 2) | (b == 4) | (b == 8);
     return b == 16 ? 2u * d : (quant ? q : 0u);
+}
+
+// Inclusive sum over the wave's lanes in lane order, by DPP: partial sums
+// within each row of 16 lanes (row_shr 1, 2, 4, 8; lanes whose source lies
+// before the row take 0), then row 0's total into rows 1-3 and row 1's into
+// rows 2-3 (row_bcast 15 and 31, rows selected by the row mask).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
 }
 
 // The scan is one workgroup's chain of dependent steps (widths in, offsets
@@ -164,12 +231,7 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanLaunch sl) 
             rs[i] = in ? r : 0u;
             local += rs[i];
         }
-        uint32_t inc = local;  // inclusive scan within the wave
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t t = (uint32_t)__shfl_up((int)inc, o);
-            if (lane >= (uint32_t)o) inc += t;
-        }
+        const uint32_t inc = wave_inclusive_sum(local);
         const bool wave_bad = __builtin_amdgcn_ballot_w64(my_bad) != 0;
         if (lane == kWave - 1) wave_tot[w] = inc | (wave_bad ? kBadBit : 0u);
         __syncthreads();
@@ -229,39 +291,7 @@ __global__ __launch_bounds__(kScanThreads) void card_scan_kernel(ScanLaunch sl) 
     if (!p.card_out || flags) return;
     // header (256 B) + widths + zero padding up to the payload
     uint32_t* hdr = reinterpret_cast<uint32_t*>(p.card_out);
-    if (tid < 64) {
-        uint32_t val = 0;
-        switch (tid) {
-            case 0: val = kCardMagic; break;
-            case 1: val = 1u | (2u << 16); break;  // version 1, kind 2
-            case 2: val = p.L; break;
-            case 3: val = p.H; break;
-            case 4: val = p.T; break;
-            case 5: val = p.d; break;
-            case 6: val = kCardGroup; break;
-            case 8: val = (uint32_t)(uint64_t)p.meta.position_offset; break;
-            case 9: val = (uint32_t)((uint64_t)p.meta.position_offset >> 32); break;
-            case 10: val = kCardHeaderBytes; break;
-            case 12: val = (uint32_t)payload; break;
-            case 13: val = (uint32_t)(payload >> 32); break;
-            case 14: val = (uint32_t)S; break;
-            case 15: val = (uint32_t)(S >> 32); break;
-            case 16: val = (uint32_t)total; break;
-            case 17: val = (uint32_t)(total >> 32); break;
-            default:
-                if (tid >= 18 && tid < 34) {
-                    const int c = (int)(tid - 18) * 4;
-                    val = (uint32_t)(uint8_t)p.meta.model_id[c] | ((uint32_t)(uint8_t)p.meta.model_id[c + 1] << 8) |
-                          ((uint32_t)(uint8_t)p.meta.model_id[c + 2] << 16) |
-                          ((uint32_t)(uint8_t)p.meta.model_id[c + 3] << 24);
-                }
-        }
-        if (p.meta_src && (tid == 8 || tid == 9 || (tid >= 18 && tid < 34))) {
-            val = reinterpret_cast<const uint32_t*>(p.meta_src)[tid];
-            if (tid == 33) val &= 0x00FFFFFFu;  // at most 63 characters, NUL-terminated
-        }
-        hdr[tid] = val;
-    }
+    if (tid < 64) hdr[tid] = card_header_word(tid, p.L, p.H, p.T, p.d, payload, S, total, p.meta, p.meta_src);
     if (one_chunk) {
         const uint64_t t0 = (uint64_t)tid * kScanItems;
         if (t0 + kScanItems <= p.T) {
@@ -443,16 +473,129 @@ __device__ __forceinline__ void quant_store_group(const float (&x)[32], uint32_t
 // of at most 2d bytes: 4 KiB), 16-byte aligned at both ends.
 constexpr uint32_t kSpanChunks = 256;  // 16-byte chunks
 
+// ---------------------------------------------------------------- record offsets in the grid
+//
+// Cards of up to kInGridTokens tokens skip the scan kernel and the launch
+// gap behind it: every pack or unpack workgroup computes the record offsets
+// itself from the widths (at most 8 KiB, read from L2 after the first
+// workgroups), 32 per thread. Per dword x of four widths: v_sad_u8 sums
+// them, v_sad_u8 of (x >> 4) & 0x01010101 counts the 16s (a valid width has
+// bit 4 only when it is 16), and x & 0xE1E1E1E1, the borrow bits of
+// x - 0x01010101 and x & (x - 0x01010101) are all zero exactly when each
+// byte is 2, 4, 8 or 16 (one set bit among bits 1-4, no zero byte). A record
+// is 16 + (d/8) w bytes, and 2d = 16 + (d/8) 16 - 16 at w = 16, so a block
+// of n tokens takes 16 n + (d/8) sum(w) - 16 n16 bytes. A workgroup scan of
+// the block sums gives every block's offset; a wave scan gives each token's
+// within its block. Tails and unaligned widths take the bytes one by one.
+constexpr uint32_t kInGridTokens = 8192;
+constexpr uint32_t kInGridBlocks = 512;  // 16-token blocks at d = 128 (256 of 32 at d = 64)
+constexpr uint32_t kInGridBytes = 32;    // widths per thread
+
+struct InGridLds {
+    uint32_t pref[kInGridBlocks + 1];  // record bytes before each block; [nbk] = the stream's
+    uint32_t wtot[kBlockThreads / kWave];
+};
+
+// Fills sh.pref[0 .. nbk]; all threads return the stream's record bytes and
+// whether any width is invalid. wreg: the thread's 32 widths when it loaded
+// them whole (w_whole), for the card copy.
 template <int D>
+__device__ __forceinline__ void ingrid_scan(const uint8_t* widths, uint32_t T, uint32_t nbk, InGridLds& sh,
+                                            uint32_t& total, bool& bad, uint4 (&wreg)[2], bool& w_whole) {
+    constexpr uint32_t TPW = kWave / (D / kCardGroup);             // tokens per block
+    constexpr uint32_t BPT = kInGridBytes / TPW;                    // blocks per thread: 2 or 1
+    constexpr uint32_t DPB = TPW / 4;                               // dwords per block
+    static_assert(kInGridTokens / TPW <= kInGridBlocks && BPT * kBlockThreads * TPW == kInGridTokens, "layout");
+    const uint32_t tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const uint32_t t0 = tid * kInGridBytes;
+    w_whole = ((uintptr_t)widths & 15) == 0 && t0 + kInGridBytes <= T;
+    uint32_t bs[BPT];
+    uint32_t badbits = 0;
+    wreg[0] = make_uint4(0, 0, 0, 0);
+    wreg[1] = make_uint4(0, 0, 0, 0);
+    if (w_whole) {
+        wreg[0] = *reinterpret_cast<const uint4*>(widths + t0);
+        wreg[1] = *reinterpret_cast<const uint4*>(widths + t0 + 16);
+        const uint32_t x[8] = {wreg[0].x, wreg[0].y, wreg[0].z, wreg[0].w, wreg[1].x, wreg[1].y, wreg[1].z, wreg[1].w};
+#pragma unroll
+        for (uint32_t j = 0; j < BPT; ++j) {
+            uint32_t sw = 0, n16 = 0;
+#pragma unroll
+            for (uint32_t q = 0; q < DPB; ++q) {
+                const uint32_t v = x[j * DPB + q];
+                sw = __builtin_amdgcn_sad_u8(v, 0u, sw);
+                n16 = __builtin_amdgcn_sad_u8((v >> 4) & 0x01010101u, 0u, n16);
+                const uint32_t t = v - 0x01010101u;
+                badbits |= (v & 0xE1E1E1E1u) | (t & 0x80808080u) | (v & t);
+            }
+            bs[j] = 16u * TPW + (uint32_t)(D / 8) * sw - 16u * n16;
+        }
+    } else {
+#pragma unroll
+        for (uint32_t j = 0; j < BPT; ++j) {
+            uint32_t r = 0;
+            for (uint32_t i = 0; i < TPW && t0 + j * TPW < T; ++i) {
+                const uint32_t t = t0 + j * TPW + i;
+                if (t < T) {
+                    const uint32_t rb = record_bytes_sel(D, widths[t]);
+                    badbits |= rb == 0 ? 1u : 0u;
+                    r += rb;
+                }
+            }
+            bs[j] = r;
+        }
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < BPT; ++j) local += bs[j];
+    const uint32_t inc = wave_inclusive_sum(local);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(badbits != 0) != 0;
+    // at most 8192 records of at most 256 bytes: bit 31 is free for the flag
+    if (lane == kWave - 1) sh.wtot[w] = inc | (wave_bad ? 0x80000000u : 0u);
+    __syncthreads();
+    uint32_t before = 0, tot = 0, flag = 0;
+#pragma unroll
+    for (int k = 0; k < kBlockThreads / kWave; ++k) {
+        const uint32_t v = sh.wtot[k];
+        flag |= v;
+        before += (uint32_t)k < w ? (v & 0x7FFFFFFFu) : 0u;
+        tot += v & 0x7FFFFFFFu;
+    }
+    uint32_t run = before + inc - local;
+#pragma unroll
+    for (uint32_t j = 0; j < BPT; ++j) {
+        const uint32_t b = tid * BPT + j;
+        if (b < nbk) sh.pref[b] = run;
+        run += bs[j];
+    }
+    if (tid == 0) sh.pref[nbk] = tot;
+    total = tot;
+    bad = (flag & 0x80000000u) != 0;
+    __syncthreads();
+}
+
+// Offset of this lane's token within its wave's block (tokens in lane order,
+// G lanes per token): exclusive sum of the record bytes of the tokens before
+// it, from one wave scan over the first lane of each token.
+__device__ __forceinline__ uint32_t token_offset_in_block(uint32_t rec, uint32_t g) {
+    return wave_inclusive_sum(g == 0 ? rec : 0u) - rec;
+}
+
+template <int D, bool InGrid>
 __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) {
     constexpr uint32_t G = D / kCardGroup;  // lanes per token
     constexpr uint32_t TPW = kWave / G;     // tokens per wave
     static_assert(TPW * 2 * D <= 16 * kSpanChunks, "span exceeds the stage");
     const uint32_t lane = lane_id();
-    const uint64_t wave = xcd_run_block<kPackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
-    if (wave >= p.n_waves) return;
+    const uint64_t wave_id = xcd_run_block<kPackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    // with offsets computed in the grid every wave takes part in its
+    // workgroup's scan; a wave past the end does nothing else
+    const bool active = wave_id < p.n_waves;
+    if (!InGrid && !active) return;
+    const uint64_t wave = active ? wave_id : 0;
     const uint64_t s = wave / p.nbk;
-    const uint32_t t0 = (uint32_t)(wave % p.nbk) * TPW;
+    const uint32_t blk = (uint32_t)(wave % p.nbk);
+    const uint32_t t0 = blk * TPW;
     const uint32_t tok = t0 + lane / G;
     const uint32_t g = lane % G;
     const bool valid = tok < p.T;
@@ -462,19 +605,61 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
     // The input loads go out first: they depend on nothing the scan wrote
     // (lanes past the last token load the wave's first token), so their
-    // latency overlaps that of the scan's results below.
-    uint4 raw[4];
-    {
+    // latency overlaps that of the offsets below.
+    uint4 raw[4] = {};
+    if (active) {
         const uint16_t* src =
             (kv ? p.v : p.k) + (((uint64_t)l * p.H + h) * p.T + (valid ? tok : t0)) * D + g * kCardGroup;
 #pragma unroll
         for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
     }
-    const uint64_t flags = p.info[2], S = p.info[0];
-    const uint64_t span0 = p.off[t0], span1 = p.off[t0 + nv];
-    const uint64_t my_off = p.off[valid ? tok : t0];
     const uint32_t width = p.widths[valid ? tok : t0];
-    if (flags != 0) return;
+    uint64_t S, span0, span1, my_off;
+    if (InGrid) {
+        __shared__ InGridLds sh;
+        uint32_t tot;
+        bool bad, w_whole;
+        uint4 wreg[2];
+        ingrid_scan<D>(p.widths, p.T, p.nbk, sh, tot, bad, wreg, w_whole);
+        S = align_up(tot, 256);
+        const uint64_t total = p.payload + 2ull * p.L * p.H * S;
+        const uint32_t flags = (bad ? kFlagBadWidth : 0u) | (total > p.limit ? kFlagCapacity : 0u);
+        if (blockIdx.x == 0) {
+            // the card's header, widths and padding (what the scan kernel writes)
+            const uint32_t tid = threadIdx.x;
+            if (tid == 0) {
+                if (p.dev_card_bytes) *p.dev_card_bytes = total;
+                if (flags && p.status) atomicOr(p.status, (int)flags);
+                // a card that will not be written gets a zero magic word
+                if (flags) reinterpret_cast<uint32_t*>(p.card)[0] = 0;
+            }
+            if (!flags) {
+                if (tid < 64)
+                    reinterpret_cast<uint32_t*>(p.card)[tid] =
+                        card_header_word(tid, p.L, p.H, p.T, D, p.payload, S, total, p.meta, nullptr);
+                const uint64_t w0 = (uint64_t)tid * kInGridBytes;
+                uint8_t* cw = p.card + kCardHeaderBytes;
+                if (w_whole) {
+                    reinterpret_cast<uint4*>(cw + w0)[0] = wreg[0];
+                    reinterpret_cast<uint4*>(cw + w0)[1] = wreg[1];
+                } else {
+                    for (uint64_t i = w0; i < w0 + kInGridBytes && i < p.T; ++i) cw[i] = p.widths[i];
+                }
+                for (uint64_t i = p.T + tid; i < p.payload - kCardHeaderBytes; i += kBlockThreads) cw[i] = 0;
+            }
+        }
+        if (flags || !active) return;
+        span0 = sh.pref[blk];
+        span1 = sh.pref[blk + 1];
+        my_off = span0 + token_offset_in_block(valid ? record_bytes_sel(D, width) : 0u, g);
+    } else {
+        const uint64_t flags = p.info[2];
+        S = p.info[0];
+        span0 = p.off[t0];
+        span1 = p.off[t0 + nv];
+        my_off = p.off[valid ? tok : t0];
+        if (flags != 0) return;
+    }
     uint8_t* stream = p.card + p.payload + s * S;
 
     __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
@@ -511,7 +696,7 @@ __global__ __launch_bounds__(kBlockThreads) void card_pack_kernel(CardParams p) 
     }
     // zero the stream's tail padding after the last record
     if (t0 + nv == p.T && lane == 0)
-        for (uint64_t i = p.off[p.T]; i < S; i += 16) *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
+        for (uint64_t i = span1; i < S; i += 16) *reinterpret_cast<uint4*>(stream + i) = make_uint4(0, 0, 0, 0);
 }
 
 // The codes of one group at a per-lane width b (2, 4 or 8) from its record,
@@ -609,13 +794,17 @@ __device__ __forceinline__ float round_bf16(float y) {
     return __uint_as_float(r);
 }
 
-template <int D>
+template <int D, bool InGrid>
 __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p) {
     constexpr uint32_t G = D / kCardGroup;
     constexpr uint32_t TPW = kWave / G;  // the wave's tokens: 4 KiB of bf16 output
     const uint32_t lane = lane_id();
-    const uint64_t wave = xcd_run_block<kUnpackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
-    if (wave >= p.n_waves) return;
+    const uint64_t wave_id = xcd_run_block<kUnpackXcdRun>(blockIdx.x) * (kBlockThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+    // with offsets computed in the grid every wave takes part in its
+    // workgroup's scan; a wave past the end does nothing else
+    const bool active = wave_id < p.n_waves;
+    if (!InGrid && !active) return;
+    const uint64_t wave = active ? wave_id : 0;
     const uint64_t s = wave / p.nbk;
     const uint32_t b = (uint32_t)(wave % p.nbk);
     const uint32_t t0 = b * TPW;
@@ -627,13 +816,37 @@ __global__ __launch_bounds__(kBlockThreads) void card_unpack_kernel(CardParams p
     const uint32_t h = (uint32_t)(s % p.H);
     const uint32_t kv = (uint32_t)((s / p.H) & 1);
     const uint32_t l = (uint32_t)(s / (2ull * p.H));
-    // Everything the scan wrote that this wave needs, in one round of loads
-    // (none depends on another), before the status check: a short-lived
-    // wave pays each dependent round trip in full.
-    const uint64_t flags = p.info[2], S = p.info[0];
-    const uint64_t span0 = p.off[t0], span1 = p.off[t0 + nv], my_off = p.off[tc];
+    uint64_t S, span0, span1, my_off;
     const uint32_t width = p.widths[tc];
-    if (flags != 0) return;
+    if (InGrid) {
+        __shared__ InGridLds sh;
+        uint32_t tot;
+        bool bad, w_whole;
+        uint4 wreg[2];
+        ingrid_scan<D>(p.widths, p.T, p.nbk, sh, tot, bad, wreg, w_whole);
+        S = align_up(tot, 256);
+        const uint64_t total = p.payload + 2ull * p.L * p.H * S;
+        // every wave checks the header itself (uniform addresses: scalar
+        // loads); the widths say how large the card must be, and a card
+        // shorter than that is refused before any record is read
+        uint32_t flags = bad ? kFlagBadWidth : 0u;
+        if (!card_header_ok(p.card_in, p.L, p.H, p.T, D, p.payload, S, total, p.limit)) flags |= kFlagBadHeader;
+        if (blockIdx.x == 0 && threadIdx.x == 0 && flags && p.status) atomicOr(p.status, (int)flags);
+        if (flags || !active) return;
+        span0 = sh.pref[b];
+        span1 = sh.pref[b + 1];
+        my_off = span0 + token_offset_in_block(valid ? record_bytes_sel(D, width) : 0u, g);
+    } else {
+        // Everything the scan wrote that this wave needs, in one round of loads
+        // (none depends on another), before the status check: a short-lived
+        // wave pays each dependent round trip in full.
+        const uint64_t flags = p.info[2];
+        S = p.info[0];
+        span0 = p.off[t0];
+        span1 = p.off[t0 + nv];
+        my_off = p.off[tc];
+        if (flags != 0) return;
+    }
     // The wave's records are one contiguous span of the stream: load it with
     // 16-byte coalesced loads into LDS, then decode each group from there.
     __shared__ uint4 stage[kBlockThreads / kWave][kSpanChunks];
@@ -844,15 +1057,23 @@ hipError_t launch_card_pack(const Shape& s, const void* k, const void* v, const 
     sp.T = s.T;
     sp.d = s.d;
     sp.meta = meta;
-    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
-    if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
     p.widths = widths;
     p.card = static_cast<uint8_t*>(card);
+    p.limit = capacity;
+    p.dev_card_bytes = dev_card_bytes;
+    p.status = dev_status;
+    p.meta = meta;
     const uint32_t nblocks = xcd_run_grid<kPackXcdRun>((p.n_waves + 3) / 4);
-    return launch_kernel(s.d == 64 ? card_pack_kernel<64> : card_pack_kernel<128>, dim3(nblocks),
+    // cards of up to kInGridTokens tokens: offsets computed in the grid
+    if (s.T <= kInGridTokens)
+        return launch_kernel(s.d == 64 ? card_pack_kernel<64, true> : card_pack_kernel<128, true>, dim3(nblocks),
+                             dim3(kBlockThreads), stream, p);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
+    if (e != hipSuccess) return e;
+    return launch_kernel(s.d == 64 ? card_pack_kernel<64, false> : card_pack_kernel<128, false>, dim3(nblocks),
                          dim3(kBlockThreads), stream, p);
 }
 
@@ -872,16 +1093,22 @@ hipError_t launch_card_unpack(const Shape& s, const void* card, uint64_t card_by
     sp.H = s.H;
     sp.T = s.T;
     sp.d = s.d;
-    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
-    if (e != hipSuccess) return e;
     CardParams p = card_params(s, ws);
     p.k_out = static_cast<uint16_t*>(k_out);
     p.v_out = static_cast<uint16_t*>(v_out);
     p.widths = sp.widths;
     p.card_in = static_cast<const uint8_t*>(card);
+    p.limit = card_bytes;
+    p.status = dev_status;
     const uint32_t nblocks = xcd_run_grid<kUnpackXcdRun>((p.n_waves + 3) / 4);
-    return launch_kernel(s.d == 64 ? card_unpack_kernel<64> : card_unpack_kernel<128>, dim3(nblocks),
-                         dim3(kBlockThreads), stream, p);
+    // cards of up to kInGridTokens tokens: offsets computed in the grid
+    if (s.T <= kInGridTokens)
+        return launch_kernel(s.d == 64 ? card_unpack_kernel<64, true> : card_unpack_kernel<128, true>,
+                             dim3(nblocks), dim3(kBlockThreads), stream, p);
+    hipError_t e = launch_kernel(card_scan_kernel, dim3(1), dim3(kScanThreads), stream, sl);
+    if (e != hipSuccess) return e;
+    return launch_kernel(s.d == 64 ? card_unpack_kernel<64, false> : card_unpack_kernel<128, false>,
+                         dim3(nblocks), dim3(kBlockThreads), stream, p);
 }
 
 hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t card_in_bytes,
