@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     constexpr int NCB = D / 16;   // channel blocks of 16
     constexpr int CPL = D / 4;    // channels per lane in the output layout
     constexpr int SQ = CPL / 8;   // 16-byte source chunks per lane and token
-    extern __shared__ u32x4 frag[];  // [V][r/32][NCB][64 lanes]
+    extern __shared__ u32x4 frag[];  // [V][r/32][NCB][64 lanes], then the waves' output staging
 
     // workgroup -> (matrix, token chunk, head), matrices grouped by XCD
     const uint32_t b = blockIdx.x;
@@ -164,11 +164,20 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
             for (int e = 0; e < 4; ++e) acc[j][cb][e] = 0.0f;
 
     // lane holds token t, channels (d/4) g + 4cb + e: add the source, round
-    // once, store 16 bytes (two channel blocks) at a time
+    // once. The 16 tokens of a block are one contiguous 16 x d image of the
+    // output; it goes through the wave's LDS staging (row-major, 16-byte chunk
+    // c of token i at c ^ swz(i), so that the writers - 16 tokens, one chunk
+    // each - and the readers - whole rows - meet no bank twice) and out with
+    // each store covering a contiguous 1 KiB. Stores where every lane writes
+    // its own d/2-byte piece ran at about half the write bandwidth.
+    constexpr uint32_t CR = D / 8;  // 16-byte chunks per token row
+    u32x4* stg = frag + p.V * KC * NCB * kWave + wave * 16 * CR;
+    auto swz = [](uint32_t i) { return D == 128 ? (i & 15u) : ((i >> 1) & 7u); };
     auto store_tile = [&](uint32_t tile) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t t = tile * kLrTileTokens + row_in_tile + 16 * j;
+            const uint32_t tb = tile * kLrTileTokens + wave * 32 + 16 * j;  // the block's first token
+            const uint32_t i = lane % 16;
 #pragma unroll
             for (int q = 0; q < SQ; ++q) {
                 const uint32_t sw[4] = {sv[j][q].x, sv[j][q].y, sv[j][q].z, sv[j][q].w};
@@ -178,11 +187,17 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
                     const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
                     o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
                 }
-                // plain stores: a wave's later waits for its A fragments also
-                // wait for these, and non-temporal stores took longer to
-                // retire (the call ran 1.9x slower with them)
-                if (t < p.T) *reinterpret_cast<u32x4*>(out + (uint64_t)t * D + g * CPL + 8 * q) = u32x4{o[0], o[1], o[2], o[3]};
+                const uint32_t c = g * SQ + q;
+                stg[i * CR + (c ^ swz(i))] = u32x4{o[0], o[1], o[2], o[3]};
             }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int u = 0; u < SQ; ++u) {
+                const uint32_t pos = kWave * u + lane, ti = pos / CR, c = pos % CR;
+                const u32x4 x = stg[ti * CR + (c ^ swz(ti))];
+                if (tb + ti < p.T) *reinterpret_cast<u32x4*>(out + (uint64_t)tb * D + 8 * pos) = x;
+            }
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -263,6 +278,9 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 
 uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r) { return (uint64_t)V * d * r * 2; }
 
+// the waves' output staging beside the R fragments: 16 tokens x d bf16 each
+static uint64_t lowrank_stage_bytes(uint32_t d) { return (uint64_t)kLrWaves * 16 * d * 2; }
+
 hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
                                       const void* src, const void* a, const void* rf, const float* w, void* out,
                                       hipStream_t stream) {
@@ -287,7 +305,7 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     const uint64_t groups = (M + kXcds - 1) / kXcds;
     const uint64_t nblocks = groups * kXcds * p.chunks * H;
     if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    const uint32_t lds = (uint32_t)lowrank_lds_bytes(d, V, r);
+    const uint32_t lds = (uint32_t)(lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(d));
     void (*kernel)(LowrankParams) =
         d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2> : lowrank_materialize_kernel<64, 1>)
                 : (r == 64 ? lowrank_materialize_kernel<128, 2> : lowrank_materialize_kernel<128, 1>);
