@@ -57,6 +57,7 @@ struct LowrankParams {
     uint32_t tiles;       // ceil(T / 256)
     uint32_t chunks;      // token chunks per (matrix, head)
     uint32_t chunk_tiles; // tiles per chunk
+    uint32_t stage_row;   // 16-byte chunks between token rows of the output staging
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -141,18 +142,21 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) rc[kc][cb] = frag[((v * KC + kc) * NCB + cb) * kWave + lane];
     };
-    // source chunks of a tile, requested at its first step and used at its
-    // last (at r = 64 the registers hold operands, and the source is read
-    // at the last step)
+    // source chunks of a tile, requested at the last step of the tile before
+    // it (as soon as that tile's own are consumed, and ahead of its output
+    // stores, which later waits would otherwise also wait for) and used at
+    // its last; at r = 64 the registers hold operands, and the source is
+    // read at the last step
     constexpr bool kEarlySrc = KC == 1;
     u32x4 sv[2][SQ];
+    auto load_src_block = [&](uint32_t tile, int j) {
+        const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) sv[j][q] = ld16(src + (uint64_t)t * D + g * CPL + 8 * q);
+    };
     auto load_src = [&](uint32_t tile) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
-#pragma unroll
-            for (int q = 0; q < SQ; ++q) sv[j][q] = ld16(src + (uint64_t)t * D + g * CPL + 8 * q);
-        }
+        for (int j = 0; j < 2; ++j) load_src_block(tile, j);
     };
 
     float acc[2][NCB][4];
@@ -165,19 +169,22 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 
     // lane holds token t, channels (d/4) g + 4cb + e: add the source, round
     // once. The 16 tokens of a block are one contiguous 16 x d image of the
-    // output; it goes through the wave's LDS staging (row-major, 16-byte chunk
-    // c of token i at c ^ swz(i), so that the writers - 16 tokens, one chunk
-    // each - and the readers - whole rows - meet no bank twice) and out with
-    // each store covering a contiguous 1 KiB. Stores where every lane writes
-    // its own d/2-byte piece ran at about half the write bandwidth.
+    // output; it goes through the wave's LDS staging (token rows p.stage_row
+    // chunks apart: one chunk more than a row where the LDS has room, so that
+    // the writers - 16 tokens, one chunk each - fall in different banks) and
+    // out with each store covering a contiguous 1 KiB. Stores where every
+    // lane writes its own d/2-byte piece ran at about half the write
+    // bandwidth.
     constexpr uint32_t CR = D / 8;  // 16-byte chunks per token row
-    u32x4* stg = frag + p.V * KC * NCB * kWave + wave * 16 * CR;
-    auto swz = [](uint32_t i) { return D == 128 ? (i & 15u) : ((i >> 1) & 7u); };
+    constexpr uint32_t TPS = kWave / CR;  // token rows per store instruction
+    const uint32_t SR = p.stage_row;
+    u32x4* stg = frag + p.V * KC * NCB * kWave + wave * 16 * SR;
+    u32x4* stg_w = stg + (lane % 16) * SR + g * SQ;       // this lane's chunks
+    u32x4* stg_r = stg + (lane / CR) * SR + lane % CR;    // chunk lane of rows 0, TPS, ...
     auto store_tile = [&](uint32_t tile) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t tb = tile * kLrTileTokens + wave * 32 + 16 * j;  // the block's first token
-            const uint32_t i = lane % 16;
 #pragma unroll
             for (int q = 0; q < SQ; ++q) {
                 const uint32_t sw[4] = {sv[j][q].x, sv[j][q].y, sv[j][q].z, sv[j][q].w};
@@ -187,16 +194,17 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
                     const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
                     o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[j][cb][e], bf16_hi(sw[e2]) + acc[j][cb][e + 1]);
                 }
-                const uint32_t c = g * SQ + q;
-                stg[i * CR + (c ^ swz(i))] = u32x4{o[0], o[1], o[2], o[3]};
+                stg_w[q] = u32x4{o[0], o[1], o[2], o[3]};
             }
+            if (kEarlySrc) load_src_block(tile + 1, j);
             __builtin_amdgcn_wave_barrier();
+            u32x4 x[SQ];
 #pragma unroll
-            for (int u = 0; u < SQ; ++u) {
-                const uint32_t pos = kWave * u + lane, ti = pos / CR, c = pos % CR;
-                const u32x4 x = stg[ti * CR + (c ^ swz(ti))];
-                if (tb + ti < p.T) *reinterpret_cast<u32x4*>(out + (uint64_t)tb * D + 8 * pos) = x;
-            }
+            for (int u = 0; u < SQ; ++u) x[u] = stg_r[u * TPS * SR];
+            u32x4* dst = reinterpret_cast<u32x4*>(out + (uint64_t)tb * D) + lane;
+#pragma unroll
+            for (int u = 0; u < SQ; ++u)
+                if (tb + (kWave * u + lane) / CR < p.T) dst[kWave * u] = x[u];
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
@@ -234,7 +242,6 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     auto step = [&](uint32_t s, const u32x4 (&ca)[2][KC], u32x4 (&na)[2][KC]) {
         const uint32_t tile = tile0 + s / p.V, v = s % p.V;
         load_a(s + NSET - 1, na);
-        if (kEarlySrc && v == 0 && s != 0) load_src(tile);
         f32x4 t[2][NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -278,8 +285,10 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 
 uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r) { return (uint64_t)V * d * r * 2; }
 
-// the waves' output staging beside the R fragments: 16 tokens x d bf16 each
-static uint64_t lowrank_stage_bytes(uint32_t d) { return (uint64_t)kLrWaves * 16 * d * 2; }
+// the waves' output staging beside the R fragments: 16 token rows of
+// row_chunks 16-byte chunks each (d / 8, or one more where it fits)
+static uint64_t lowrank_stage_bytes(uint32_t row_chunks) { return (uint64_t)kLrWaves * 16 * row_chunks * 16; }
+constexpr uint64_t kLdsBytes = 160 * 1024;
 
 hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
                                       const void* src, const void* a, const void* rf, const float* w, void* out,
@@ -305,7 +314,9 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     const uint64_t groups = (M + kXcds - 1) / kXcds;
     const uint64_t nblocks = groups * kXcds * p.chunks * H;
     if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    const uint32_t lds = (uint32_t)(lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(d));
+    p.stage_row = d / 8 + 1;
+    if (lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(p.stage_row) > kLdsBytes) p.stage_row = d / 8;
+    const uint32_t lds = (uint32_t)(lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(p.stage_row));
     void (*kernel)(LowrankParams) =
         d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2> : lowrank_materialize_kernel<64, 1>)
                 : (r == 64 ? lowrank_materialize_kernel<128, 2> : lowrank_materialize_kernel<128, 1>);
