@@ -15,22 +15,25 @@
 // binary32 (fmaf), anchors in index order; src is added last and the sum is
 // rounded once to bf16, ties to even.
 //
-// Work mapping. A workgroup (8 waves) owns one head of one matrix over a
-// chunk of token tiles (256 tokens each; at Llama-3-8B sizes a chunk is the
-// whole sequence, one workgroup per CU): its source and output are one
-// contiguous block of [H][T][d]. The anchors' R rows for that head
-// (V x d x r bf16) are staged once into LDS in MFMA-fragment order, so every
-// operand read is a lane-contiguous ds_read_b128. In each tile, wave w owns
-// token blocks 2w and 2w + 1 (16 tokens each) and all d channels, computed
-// transposed: out^T block = R_block (16 channels x r) * A_block^T
-// (r x 16 tokens). MFMA row i of channel block cb is channel
-// (d/4)(i/4) + 4cb + i%4, which leaves lane l holding token l%16 and the d/4
-// consecutive channels from (d/4)(l/16) on, so source loads and output
-// stores are 16-byte accesses. The (tile, anchor) steps of a chunk form one
-// pipeline: A fragments are requested five steps ahead (at r = 32), a
-// tile's source at its first step, its output stored at its last. Matrices are
-// dealt to XCDs (workgroup b runs on XCD b % 8) so that the 8 heads sharing
-// one matrix's A factors run on one XCD and re-read them from its L2.
+// Work mapping. A workgroup owns one head of one matrix over a chunk of
+// token tiles (at Llama-3-8B sizes a chunk is the whole sequence, one
+// workgroup per CU): its source and output are one contiguous block of
+// [H][T][d]. The anchors' R rows for that head (V x d x r bf16) are staged
+// once into LDS in MFMA-fragment order, so every operand read is a
+// lane-contiguous ds_read_b128. A wave owns NJ token blocks of 16 tokens
+// per tile and all d channels, computed transposed: out^T block = R_block
+// (16 channels x r) * A_block^T (r x 16 tokens). At r = 32, where the LDS
+// has room, 12 waves own one block each (192-token tiles, 168 VGPRs, three
+// waves per SIMD); otherwise 8 waves own two (256-token tiles, two waves per
+// SIMD, each R fragment read from LDS serving two blocks). MFMA row i of
+// channel block cb is channel (d/4)(i/4) + 4cb + i%4, which leaves lane l
+// holding token l%16 and the d/4 consecutive channels from (d/4)(l/16) on,
+// so source loads are 16-byte accesses. The (tile, anchor) steps of a chunk
+// form one pipeline: A fragments are requested five steps ahead (at r = 32),
+// a tile's source at the last step of the tile before, its output staged
+// and stored at its last. Matrices are dealt to XCDs (workgroup b runs on
+// XCD b % 8) so that the 8 heads sharing one matrix's A factors run on one
+// XCD and re-read them from its L2.
 #include "kernels_common.h"
 #include "launch.h"
 
@@ -41,10 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLrWaves = 8;
-constexpr int kLrThreads = kLrWaves * kWave;
-constexpr int kLrTileTokens = kLrWaves * 2 * 16;  // 256
 constexpr int kXcds = 8;
+constexpr uint64_t kLdsBytes = 160 * 1024;
 constexpr uint64_t kLowrankTargetGroups = 256;  // one workgroup per CU
 
 struct LowrankParams {
@@ -54,7 +55,7 @@ struct LowrankParams {
     const float* w;       // [M][V]
     uint16_t* out;        // [M][H][T][d]
     uint32_t M, H, T, V, r;
-    uint32_t tiles;       // ceil(T / 256)
+    uint32_t tiles;       // ceil(T / tile tokens)
     uint32_t chunks;      // token chunks per (matrix, head)
     uint32_t chunk_tiles; // tiles per chunk
     uint32_t stage_row;   // 16-byte chunks between token rows of the output staging
@@ -62,8 +63,14 @@ struct LowrankParams {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-template <int D, int KC>
-__global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(LowrankParams p) {
+// waves per workgroup with NJ token blocks per wave
+constexpr int lr_waves(int nj) { return nj == 2 ? 8 : 12; }
+
+template <int D, int KC, int NJ>
+__global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kernel(LowrankParams p) {
+    constexpr int W = lr_waves(NJ);
+    constexpr int THR = W * kWave;
+    constexpr int TT = W * NJ * 16;  // tile tokens
     constexpr int NCB = D / 16;   // channel blocks of 16
     constexpr int CPL = D / 4;    // channels per lane in the output layout
     constexpr int SQ = CPL / 8;   // 16-byte source chunks per lane and token
@@ -88,18 +95,18 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
         const uint32_t per_anchor = D * p.r / 8;  // 16-byte chunks
         const uint32_t total = p.V * per_anchor;
         const uint32_t qpr = p.r / 8;             // chunks per row
-        for (uint32_t c0 = 0; c0 < total; c0 += 8 * kLrThreads) {
+        for (uint32_t c0 = 0; c0 < total; c0 += 8 * THR) {
             u32x4 x[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const uint32_t c = min(c0 + u * kLrThreads + threadIdx.x, total - 1);
+                const uint32_t c = min(c0 + u * THR + threadIdx.x, total - 1);
                 const uint32_t v = c / per_anchor, rest = c % per_anchor;
                 const uint32_t row = rest / qpr, q = rest % qpr;
                 x[u] = ld16(p.rf + (((uint64_t)m * p.V + v) * HD + (uint64_t)h * D + row) * p.r + q * 8);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const uint32_t c = c0 + u * kLrThreads + threadIdx.x;
+                const uint32_t c = c0 + u * THR + threadIdx.x;
                 if (c < total) {
                     const uint32_t v = c / per_anchor, rest = c % per_anchor;
                     const uint32_t row = rest / qpr, q = rest % qpr;
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     const uint32_t lane = lane_id();
     const uint32_t wave = wave_uniform(threadIdx.x / kWave);
     const uint32_t g = lane / 16;
-    const uint32_t row_in_tile = wave * 32 + lane % 16;  // + 16 j
+    const uint32_t row_in_tile = wave * 16 * NJ + lane % 16;  // + 16 j
     const uint16_t* src = p.src + ((uint64_t)m * p.H + h) * p.T * D;
     uint16_t* out = p.out + ((uint64_t)m * p.H + h) * p.T * D;
     const uint16_t* a = p.a + (uint64_t)m * p.V * p.T * p.r;
@@ -124,13 +131,13 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     // A fragments of step s (tile s / V, anchor s % V): token row of the
     // block, k = 32 kc + 8 g .. + 7; rows past T (and steps past the end)
     // are clamped to valid ones and their results discarded
-    auto load_a = [&](uint32_t s, u32x4 (&x)[2][KC]) {
+    auto load_a = [&](uint32_t s, u32x4 (&x)[NJ][KC]) {
         s = min(s, S - 1);
         const uint32_t tile = tile0 + s / p.V, v = s % p.V;
         const uint16_t* av = a + (uint64_t)v * p.T * p.r;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
+        for (int j = 0; j < NJ; ++j) {
+            const uint32_t t = min(tile * TT + row_in_tile + 16 * j, p.T - 1);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) x[j][kc] = ld16(av + (uint64_t)t * p.r + 32 * kc + 8 * g);
         }
@@ -148,20 +155,20 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     // its last; at r = 64 the registers hold operands, and the source is
     // read at the last step
     constexpr bool kEarlySrc = KC == 1;
-    u32x4 sv[2][SQ];
+    u32x4 sv[NJ][SQ];
     auto load_src_block = [&](uint32_t tile, int j) {
-        const uint32_t t = min(tile * kLrTileTokens + row_in_tile + 16 * j, p.T - 1);
+        const uint32_t t = min(tile * TT + row_in_tile + 16 * j, p.T - 1);
 #pragma unroll
         for (int q = 0; q < SQ; ++q) sv[j][q] = ld16(src + (uint64_t)t * D + g * CPL + 8 * q);
     };
     auto load_src = [&](uint32_t tile) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load_src_block(tile, j);
+        for (int j = 0; j < NJ; ++j) load_src_block(tile, j);
     };
 
-    float acc[2][NCB][4];
+    float acc[NJ][NCB][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -183,8 +190,8 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     u32x4* stg_r = stg + (lane / CR) * SR + lane % CR;    // chunk lane of rows 0, TPS, ...
     auto store_tile = [&](uint32_t tile) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t tb = tile * kLrTileTokens + wave * 32 + 16 * j;  // the block's first token
+        for (int j = 0; j < NJ; ++j) {
+            const uint32_t tb = tile * TT + wave * 16 * NJ + 16 * j;  // the block's first token
 #pragma unroll
             for (int q = 0; q < SQ; ++q) {
                 const uint32_t sw[4] = {sv[j][q].x, sv[j][q].y, sv[j][q].z, sv[j][q].w};
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
     // loop-carried sets in registers (it would otherwise merge the loads
     // feeding one into a single load at the loop head, just before its use).
     constexpr int NSET = KC == 1 ? 6 : 2;
-    u32x4 set[NSET][2][KC];
+    u32x4 set[NSET][NJ][KC];
 #pragma unroll
     for (int u = 0; u + 1 < NSET; ++u) load_a(u, set[u]);
     load_r(0);
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 #pragma unroll
     for (int u = 0; u + 1 < NSET; ++u)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+v"(set[u][j][kc]));
 #pragma unroll
@@ -239,14 +246,14 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(rc[kc][cb]));
 
-    auto step = [&](uint32_t s, const u32x4 (&ca)[2][KC], u32x4 (&na)[2][KC]) {
+    auto step = [&](uint32_t s, const u32x4 (&ca)[NJ][KC], u32x4 (&na)[NJ][KC]) {
         const uint32_t tile = tile0 + s / p.V, v = s % p.V;
         load_a(s + NSET - 1, na);
-        f32x4 t[2][NCB];
+        f32x4 t[NJ][NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 t[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rc[0][cb]),
                                                                    __builtin_bit_cast(bf16x8, ca[j][0]),
                                                                    f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(kLrThreads) void lowrank_materialize_kernel(Lowrank
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[j][cb][e] = fmaf(wv, t[j][cb][e], acc[j][cb][e]);
         if (v + 1 == p.V) {
@@ -287,8 +294,7 @@ uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r) { return (uint64_
 
 // the waves' output staging beside the R fragments: 16 token rows of
 // row_chunks 16-byte chunks each (d / 8, or one more where it fits)
-static uint64_t lowrank_stage_bytes(uint32_t row_chunks) { return (uint64_t)kLrWaves * 16 * row_chunks * 16; }
-constexpr uint64_t kLdsBytes = 160 * 1024;
+static uint64_t lowrank_stage_bytes(uint32_t row_chunks, uint32_t waves) { return (uint64_t)waves * 16 * row_chunks * 16; }
 
 hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
                                       const void* src, const void* a, const void* rf, const float* w, void* out,
@@ -304,7 +310,12 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     p.T = T;
     p.V = V;
     p.r = r;
-    p.tiles = (T + kLrTileTokens - 1) / kLrTileTokens;
+    // one token block per wave (12 waves) at r = 32 where its staging fits
+    // beside the R fragments, else two (8 waves)
+    const uint64_t rb = lowrank_lds_bytes(d, V, r);
+    const bool nj1 = r == 32 && rb + lowrank_stage_bytes(d / 8, lr_waves(1)) <= kLdsBytes;
+    const uint32_t waves = lr_waves(nj1 ? 1 : 2), tt = waves * (nj1 ? 1 : 2) * 16;
+    p.tiles = (T + tt - 1) / tt;
     // enough (matrix, head, chunk) items to give every CU one workgroup
     const uint64_t mh = (uint64_t)M * H;
     const uint64_t per_mh = (kLowrankTargetGroups + mh - 1) / mh;
@@ -314,18 +325,17 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     const uint64_t groups = (M + kXcds - 1) / kXcds;
     const uint64_t nblocks = groups * kXcds * p.chunks * H;
     if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    p.stage_row = d / 8 + 1;
-    if (lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(p.stage_row) > kLdsBytes) p.stage_row = d / 8;
-    const uint32_t lds = (uint32_t)(lowrank_lds_bytes(d, V, r) + lowrank_stage_bytes(p.stage_row));
+    p.stage_row = rb + lowrank_stage_bytes(d / 8 + 1, waves) <= kLdsBytes ? d / 8 + 1 : d / 8;
+    const uint32_t lds = (uint32_t)(rb + lowrank_stage_bytes(p.stage_row, waves));
     void (*kernel)(LowrankParams) =
-        d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2> : lowrank_materialize_kernel<64, 1>)
-                : (r == 64 ? lowrank_materialize_kernel<128, 2> : lowrank_materialize_kernel<128, 1>);
+        d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2, 2> : (nj1 ? lowrank_materialize_kernel<64, 1, 1> : lowrank_materialize_kernel<64, 1, 2>))
+                : (r == 64 ? lowrank_materialize_kernel<128, 2, 2> : (nj1 ? lowrank_materialize_kernel<128, 1, 1> : lowrank_materialize_kernel<128, 1, 2>));
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return report_launch(e, "lowrank_materialize (LDS attribute)");
     void* argv[] = {&p};
     return report_launch(hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((uint32_t)nblocks),
-                                         dim3(kLrThreads), argv, lds, stream),
+                                         dim3(waves * kWave), argv, lds, stream),
                          "lowrank_materialize");
 }
 
