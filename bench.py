@@ -39,11 +39,12 @@ PROBE_BYTES = 2 << 30  # buffers of the streaming ceilings
 OPS = ["encode", "decode", "pack", "unpack"]
 CARD_MODEL_ID = b"llama-3-8b"  # the step's card metadata (position offset 0)
 # kernels of each op, in launch order (the single-pass encode applies to
-# this workload: a round of whole layers fits the GPU's LDS)
+# this workload: a round of whole layers fits the GPU's LDS; pack and unpack
+# scan the record offsets inside their own grid at 4096 tokens)
 OP_KERNELS = {"encode": ["pool_encode_fused_kernel"],
               "decode": ["pool_decode_kernel<128, true>", "fanout_copy_kernel"],
-              "pack": ["card_scan_kernel", "card_pack_kernel"],
-              "unpack": ["card_scan_kernel", "card_unpack_kernel"]}
+              "pack": ["card_pack_kernel"],
+              "unpack": ["card_unpack_kernel"]}
 
 
 def log(*a):
@@ -468,13 +469,7 @@ def trace_summary(trace_dir, bench_json, warmup, steps):
     for o in OPS:
         total = 0.0
         for kname in OP_KERNELS[o]:
-            scan = kname == "card_scan_kernel"
-            if scan:
-                # two scans per step: pack's, then unpack's
-                t, allv = durs(kname, 2)
-                t = t[0::2] if o == "pack" else t[1::2]
-            else:
-                t, allv = durs(kname)
+            t, allv = durs(kname)
             total += float(np.mean(t))
             table.append(f"| {kname} | {o} | {len(allv)} | {np.mean(t):.1f} | {np.median(t):.1f} | "
                          f"{np.mean(allv):.1f} |")
