@@ -8,10 +8,12 @@
 //
 // Offsets. Records are variable-sized, so token t's record starts at the sum
 // of the record sizes of tokens 0..t-1 (the same in every stream, since the
-// width is per token). A single-workgroup scan kernel computes these offsets
-// once into the workspace (and, for pack, writes the header and widths);
-// the pack / unpack kernels then place one record per (layer, K/V, head,
-// token).
+// width is per token). For cards of up to kInGridTokens tokens every pack /
+// unpack workgroup sums the record sizes before its own tokens from the
+// widths itself (workgroup 0 writes the header and widths); longer cards,
+// and the transcode, take them from a single-workgroup scan kernel that
+// writes them once into the workspace. The pack / unpack kernels place one
+// record per (layer, K/V, head, token).
 //
 // Work mapping: one lane per 32-channel group (d/32 lanes per token, so 16
 // tokens per wave at d = 128); a lane loads its 64 input bytes, finds the

@@ -205,7 +205,10 @@ size_t cachecard_max_bytes(const kvc_shape* shape);
  *     of the record sizes of tokens 0..t-1; S rounds that sum up to 256. */
 size_t cachecard_bytes_host(const kvc_shape* shape, const uint8_t* widths_host);
 
-/* Workspace bytes needed by cachecard_pack / cachecard_unpack. */
+/* Workspace bytes needed by cachecard_pack / cachecard_unpack (record
+ * offsets; cards of up to 8192 tokens compute them inside the pack / unpack
+ * grid and leave the workspace untouched, but the argument is checked the
+ * same way for every T). */
 size_t cachecard_workspace_bytes(const kvc_shape* shape);
 
 /* Package K and V into a CacheCard (QKVShare item 2).
