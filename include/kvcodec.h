@@ -236,6 +236,10 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
  *   card        device, card_bytes valid bytes, read only
  *   k_out, v_out device bf16 [L][H][T][d]
  *   dev_status  device int32 or NULL; KVC_DEV_BAD_HEADER, KVC_DEV_BAD_WIDTH
+ * The header is checked against the shape and against the sizes the widths
+ * give (payload offset, stream bytes S, total, card_bytes); a card whose
+ * widths were altered without changing any of those sizes is decoded as it
+ * stands (the format carries no checksum).
  * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
  * KVC_E_HIP. */
 int cachecard_unpack(const kvc_shape* shape, const void* card, size_t card_bytes, void* k_out,

@@ -38,8 +38,13 @@ def gpu_unpack(shape, card, n):
     return ko, vo, int(status.item())
 
 
+# Cards of up to 8192 tokens have their record offsets computed inside the
+# pack / unpack grid; longer ones go through the separate offset scan, so
+# both sides of that boundary are cases.
 CASES = [((1, 2, 37, 128), "mixed"), ((2, 3, 70, 64), "mixed"), ((1, 1, 1, 128), "mixed"),
-         ((2, 2, 64, 128), "all2"), ((1, 2, 33, 64), "all16"), ((3, 1, 50, 128), "runs")]
+         ((2, 2, 64, 128), "all2"), ((1, 2, 33, 64), "all16"), ((3, 1, 50, 128), "runs"),
+         ((1, 1, 8192, 64), "runs"), ((1, 1, 8193, 64), "mixed"), ((1, 2, 9000, 128), "all16")]
+LONG_T = [20, 8300]  # in-grid offsets, then the separate scan
 
 
 def _widths(kind, T, seed):
@@ -183,34 +188,43 @@ def test_full_size_cachecard_workload(seed):
     assert_bits_equal(to_host(vo), rv, "V")
 
 
-def test_bad_width_is_reported():
-    shape = (1, 2, 20, 128)
+@pytest.mark.parametrize("T", LONG_T)
+@pytest.mark.parametrize("bad_at", ["early", "last"])
+def test_bad_width_is_reported(T, bad_at):
+    shape = (1, 2, T, 128)
     k, v = synth.kv_bits(synth.WORKLOADS[4], 0, shape=shape)
-    widths = np.full(20, 4, np.uint8)
-    widths[7] = 5
+    widths = np.full(T, 4, np.uint8)
+    widths[7 if bad_at == "early" else T - 1] = 5
     card, n, st = gpu_pack(shape, k, v, widths)
     assert st & kv.KVC_DEV_BAD_WIDTH
     # nothing written but a zero magic word (a stale card cannot pass)
     assert int(card[:4].view(torch.int32).item()) == 0 and torch.all(card[4:] == 0xA5)
 
 
-def test_small_capacity_is_reported_with_needed_size():
-    shape = (1, 2, 20, 128)
+@pytest.mark.parametrize("T", LONG_T)
+def test_small_capacity_is_reported_with_needed_size(T):
+    shape = (1, 2, T, 128)
     k, v = synth.kv_bits(synth.WORKLOADS[4], 0, shape=shape)
-    widths = np.full(20, 8, np.uint8)
+    widths = np.full(T, 8, np.uint8)
     need = kv.cachecard_bytes_host(shape, widths)
     card, n, st = gpu_pack(shape, k, v, widths, capacity=need - 256)
     assert st == kv.KVC_DEV_CAPACITY and n == need
     assert int(card[:4].view(torch.int32).item()) == 0 and torch.all(card[4:] == 0xA5)
 
 
-def test_unpack_rejects_bad_header_and_widths():
-    shape = (1, 2, 20, 64)
+@pytest.mark.parametrize("T", LONG_T)
+def test_unpack_rejects_bad_header_and_widths(T):
+    shape = (1, 2, T, 64)
     k, v = synth.kv_bits(synth.WORKLOADS[4], 0, shape=shape)
-    widths = np.full(20, 4, np.uint8)
+    widths = np.full(T, 4, np.uint8)
     ref = oracle.card_pack(k, v, widths)
+    # The last case widens eight tokens from 4 to 16 bits, which grows every
+    # stream by 640 bytes, more than the 256-byte rounding of S can absorb,
+    # so the sizes the widths give no longer match the header's. (A widths
+    # change that leaves every size as it was cannot be seen: the card
+    # carries no checksum.)
     for pos, val, flag in [(0, 0, kv.KVC_DEV_BAD_HEADER), (16, 21, kv.KVC_DEV_BAD_HEADER),
-                           (256 + 3, 3, kv.KVC_DEV_BAD_WIDTH), (256 + 4, 16, kv.KVC_DEV_BAD_HEADER)]:
+                           (256 + 3, 3, kv.KVC_DEV_BAD_WIDTH), (slice(256 + 4, 256 + 12), 16, kv.KVC_DEV_BAD_HEADER)]:
         bad = ref.copy()
         bad[pos] = val
         ko, vo, st = gpu_unpack(shape, torch.from_numpy(bad).to(DEV), ref.size)
