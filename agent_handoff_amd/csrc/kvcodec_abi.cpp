@@ -228,6 +228,7 @@ int kvc_lowrank_materialize(const kvc_shape* shape, uint32_t rank, uint32_t n_an
         return KVC_E_RANGE;
     const uint64_t tiles = ((uint64_t)T + 191) / 192, groups = ((uint64_t)L + 7) / 8;  // the smaller tile
     if (groups * 8 * tiles * H > 0x7FFFFFFFull) return KVC_E_SHAPE;
+    if ((uint64_t)T * rank * 2 > 0x7FFFFFFFull) return KVC_E_SHAPE;  // one anchor's A rows as a buffer
     if (!aligned(src, 16) || !aligned(a, 16) || !aligned(r, 16) || !aligned(out, 16) || !aligned(weights, 4))
         return KVC_E_ALIGN;
     const uint64_t kb = kv_bytes(shape);

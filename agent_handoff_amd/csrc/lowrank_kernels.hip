@@ -46,6 +46,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
 constexpr uint64_t kLdsBytes = 160 * 1024;
+// third word of a raw buffer resource on the gfx9 family: 32-bit data
+// format, no swizzle, bounds checked against the record count in bytes
+constexpr int kBufferWord3 = 0x00020000;
 constexpr uint64_t kLowrankTargetGroups = 256;  // one workgroup per CU
 
 struct LowrankParams {
@@ -131,16 +134,30 @@ __global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kern
     // A fragments of step s (tile s / V, anchor s % V): token row of the
     // block, k = 32 kc + 8 g .. + 7; rows past T (and steps past the end)
     // are clamped to valid ones and their results discarded
+    // A of one step as a buffer (scalar registers): it starts at the step's
+    // tile of the step's anchor and holds the rows from there to T (at most
+    // T x r bf16, under 2^31 bytes, checked at the call); this lane's row and
+    // k are a constant vector offset, so an address costs no vector
+    // instructions. Rows past T fall past the buffer's end, which the range
+    // check on the vector offset turns into zeros; their results are never
+    // stored.
+    uint32_t a_off[NJ][KC];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) a_off[j][kc] = ((row_in_tile + 16 * j) * p.r + 32 * kc + 8 * g) * 2;
     auto load_a = [&](uint32_t s, u32x4 (&x)[NJ][KC]) {
         s = min(s, S - 1);
         const uint32_t tile = tile0 + s / p.V, v = s % p.V;
-        const uint16_t* av = a + (uint64_t)v * p.T * p.r;
+        const uint32_t row0 = tile * TT;  // below T: s is clamped to the last step
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a + ((uint64_t)v * p.T + row0) * p.r), (short)0,
+                                              (int)((p.T - row0) * p.r * 2), kBufferWord3);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const uint32_t t = min(tile * TT + row_in_tile + 16 * j, p.T - 1);
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) x[j][kc] = ld16(av + (uint64_t)t * p.r + 32 * kc + 8 * g);
-        }
+            for (int kc = 0; kc < KC; ++kc)
+                x[j][kc] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)a_off[j][kc], 0, 0);
     };
     u32x4 rc[KC][NCB];
     auto load_r = [&](uint32_t v) {

@@ -319,7 +319,7 @@ int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int6
  * error, at most (2r + V + 1) * 2^-24 * (|src| + sum_v |w_v| sum_k |A R|)
  * to first order (the products of bf16 operands are exact in binary32; 2r
  * covers r - 1 additions inside the matrix core even if they truncate).
- *   shape      L (matrices), H, T, d (64 or 128)
+ *   shape      L (matrices), H, T, d (64 or 128); T * r * 2 < 2^31
  *   rank       r: 32 or 64
  *   n_anchors  V: 1 .. 32, and V * d * r * 2 <= 131072 (at d = 128, r = 32:
  *              V <= 16)
