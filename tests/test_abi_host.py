@@ -276,6 +276,9 @@ def test_lowrank_argument_errors():
     assert lr(V=0) == kv.KVC_E_RANGE
     assert lr(V=17) == kv.KVC_E_RANGE                        # 17 * 128 * 32 * 2 bytes exceed the LDS budget
     assert lr(rank=64, V=9) == kv.KVC_E_RANGE
+    # one anchor's A rows must stay under 2^31 bytes (T * r * 2)
+    assert lr(shape=kv.kvc_shape(1, 1, 1 << 25, 64), rank=32) == kv.KVC_E_SHAPE
+    assert lr(shape=kv.kvc_shape(1, 1, 1 << 24, 64), rank=64) == kv.KVC_E_SHAPE
     assert lr(shape=kv.kvc_shape(2, 2, 32, 64), V=33) == kv.KVC_E_RANGE   # one weight per lane, at most 32
     assert lr(a=2 * A + 8) == kv.KVC_E_ALIGN
     assert lr(out=4 * A + 8) == kv.KVC_E_ALIGN
