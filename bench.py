@@ -561,7 +561,8 @@ def other_configs(args):
     on one stream, inputs resident): the tiny pool, the SmolLM2-1.7B 2K pool
     (decode into one agent), the Llama-3-8B 32K pool (encode of the whole
     pool in one call, then the decode streamed one layer per call, the 32
-    calls timed as one sequence) and the Llama-3.1-8B 8K card."""
+    calls timed as one sequence, and the whole pool decoded in one call)
+    and the Llama-3.1-8B 8K card."""
     import torch
 
     from agent_handoff_amd import kvcodec as kv
@@ -610,6 +611,11 @@ def other_configs(args):
                     kv.kvpool_decode(shape, pool, l, l + 1, [ko], [vo], status, stream=stream)
             td = timed(dec, reps)
             emit(w, "decode, one layer per call (32 calls)", td, pool_b + 2 * kv_bytes)
+            del ko, vo
+            # and the whole pool in one call (4.3 GB of bf16 out)
+            ko, vo = torch.empty_like(k), torch.empty_like(v)
+            td = timed(lambda: kv.kvpool_decode(shape, pool, 0, L, [ko], [vo], status, stream=stream), reps)
+            emit(w, "decode, one agent, all layers in one call", td, pool_b + 2 * kv_bytes)
             del ko, vo
         else:
             ko, vo = torch.empty_like(k), torch.empty_like(v)
