@@ -186,12 +186,6 @@ __device__ void pool_header_and_padding(const EncodeParams& p, uint32_t d, uint3
 
 // ---------------------------------------------------------------- kernels
 
-// Zeroes n4 16-byte chunks (the encode workspace is 16-byte aligned).
-__global__ void fill_zero_kernel(uint4* p, uint32_t n4) {
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n4) p[i] = make_uint4(0, 0, 0, 0);
-}
-
 // Coordinate I of the lane: code = number of thresholds <= z, found bit by
 // bit (binary search over the 7 sorted thresholds); each bit is appended to
 // its plane word. Slots run from the last coordinate down so that

@@ -532,7 +532,7 @@ def hop_drift(kv, synth, k, v, shape, widths_np, seed, stream, dev, hops=5):
 
 CALIBRATION_BYTES = 1 << 30
 CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_layered_kernel",
-                 "fill_zero_kernel", "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
+                 "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
                  "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel",
                  "fac_zx_kernel", "fac_ztq_kernel"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
