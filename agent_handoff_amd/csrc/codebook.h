@@ -28,5 +28,12 @@ constexpr float kLv3 = 70515.0f / 32768.0f;
 constexpr float kTh5 = 32804.0f / 65536.0f;
 constexpr float kTh6 = 68810.0f / 65536.0f;
 constexpr float kTh7 = 114552.0f / 65536.0f;
+static_assert(kLv0 == kLevelUnits[0] / 32768.0f && kLv1 == kLevelUnits[1] / 32768.0f &&
+                  kLv2 == kLevelUnits[2] / 32768.0f && kLv3 == kLevelUnits[3] / 32768.0f,
+              "levels are the table's units of 2^-15");
+static_assert(kTh5 == (kLevelUnits[0] + kLevelUnits[1]) / 65536.0f &&
+                  kTh6 == (kLevelUnits[1] + kLevelUnits[2]) / 65536.0f &&
+                  kTh7 == (kLevelUnits[2] + kLevelUnits[3]) / 65536.0f,
+              "thresholds are the midpoints of neighbouring levels");
 
 }  // namespace kvc
