@@ -76,7 +76,7 @@ struct EncodeParams {
 // per layer. Both encode paths exchange 64-bit words that one workgroup
 // publishes and others read, some before it is written: the single pass one
 // per (layer, workgroup), the layered encode one per (layer, key-maximum
-// workgroup). Each call tags the words it writes with a call number of its
+// workgroup) and then one per layer. Each call tags the words it writes with a call number of its
 // own (48 bits, from a host counter of the library instance that starts at
 // a random point and skips 0): a word is (call << 16) | 0x8000 | maximum
 // bits (15 bits), and it counts only if it carries this call's number, so
@@ -143,14 +143,24 @@ __device__ __forceinline__ float fwht_quad_sign(uint32_t m) {
     return (__builtin_popcount(m & 3u) & 1) ? -1.0f : 1.0f;
 }
 
-// Maximum of r over the wave.
+// Maximum of r over the wave, as a wave-uniform (scalar) value; every lane
+// must be active. DPP folds each quad (lane xor 1, xor 2), then each 16-lane
+// row (rotations by 4 and 8), so every lane holds its row's maximum; the
+// four rows' are read into scalar registers and folded there.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t r) {
+    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, CTRL, 0xF, 0xF, false);
+    return t > r ? t : r;
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t r) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)r, o);
-        r = t > r ? t : r;
-    }
-    return r;
+    r = dpp_max_step<0xB1>(r);   // quad_perm [1,0,3,2]
+    r = dpp_max_step<0x4E>(r);   // quad_perm [2,3,0,1]
+    r = dpp_max_step<0x124>(r);  // row_ror:4
+    r = dpp_max_step<0x128>(r);  // row_ror:8
+    const uint32_t a = __builtin_amdgcn_readlane(r, 0), b = __builtin_amdgcn_readlane(r, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(r, 32), d = __builtin_amdgcn_readlane(r, 48);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
 }
 
 // Header (64 B) and every padding byte of the pool; run by workgroup 0.
@@ -324,25 +334,27 @@ template <int D>
 __device__ __forceinline__ void quantize_keys(const EncodeParams& p, const BlockPos& b, const uint4 (&kraw)[D / 32],
                                               uint32_t mbits, EncodeStage<D>& stg, uint32_t lane) {
     constexpr int C = D / 4;
+    mbits = wave_uniform(mbits);  // the same for every lane: one scalar branch below
     const float mk = __uint_as_float(mbits << 16);
     const bool finite = mbits < 0x7F80u;
     const float inv = (mk == 0.0f) ? 0.0f : 127.0f / mk;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(kraw);
     uint32_t out[C / 4];
+    if (finite) {
 #pragma unroll
-    for (int j = 0; j < C / 4; ++j) {
-        if (!finite) {
-            out[j] = 0;
-            continue;
+        for (int j = 0; j < C / 4; ++j) {
+            const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+            const float q0 = bf16_lo(w0) * inv + 12582912.0f;
+            const float q1 = bf16_hi(w0) * inv + 12582912.0f;
+            const float q2 = bf16_lo(w1) * inv + 12582912.0f;
+            const float q3 = bf16_hi(w1) * inv + 12582912.0f;
+            const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
+            const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
+            out[j] = ab | cd;
         }
-        const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
-        const float q0 = bf16_lo(w0) * inv + 12582912.0f;
-        const float q1 = bf16_hi(w0) * inv + 12582912.0f;
-        const float q2 = bf16_lo(w1) * inv + 12582912.0f;
-        const float q3 = bf16_hi(w1) * inv + 12582912.0f;
-        const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x0c0c0400u);
-        const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(q3), __float_as_uint(q2), 0x04000c0cu);
-        out[j] = ab | cd;
+    } else {
+#pragma unroll
+        for (int j = 0; j < C / 4; ++j) out[j] = 0;
     }
     constexpr int KC = C / 16;  // 16-byte chunks of codes per lane
 #pragma unroll
@@ -404,6 +416,7 @@ constexpr uint32_t kMaxRoundLayers = 32;
 constexpr uint32_t kMaxFusedGrid = 1024;  // bound on the grid (the launch keeps it below 960); sizes the poll registers
 constexpr uint64_t kWordFlag = 0x8000u;
 constexpr uint32_t kLayeredMaxGroups = 256;  // layered encode: bound on the key-maximum workgroups per layer
+static_assert(2 * (kLayeredMaxGroups + 1) <= kWsWordsPerLayer, "layered encode words exceed the workspace");
 // Spin limit of the waits inside a workgroup (key waves for their
 // coordinator, coordinator for its key waves), in ticks of the 100 MHz
 // constant clock: 0.5 s. These waits depend only on the workgroup's own
@@ -1004,20 +1017,29 @@ __global__ __launch_bounds__(kBlockThreads) void fanout_copy_kernel(FanoutParams
 // A workgroups of each "max" segment, E of each "encode" segment. A "max l"
 // workgroup reads its share of layer l's keys and publishes the share's
 // largest magnitude as a tagged word, (call << 16) | 0x8000 | bits, one per
-// (layer, workgroup). An "encode l" workgroup (one 16-token block per wave)
-// issues its key and value loads, then reads layer l's A words until all
-// carry this call's number, takes their maximum, quantises the keys and
-// encodes the values. Measured on the Llama 32K pool: 1226 us against 1377
-// us for a key-maximum pass over all layers followed by the encode (the
-// keys read twice from HBM), bit-identical. Workgroups are dispatched in order on each XCD, so a wave waits
-// only on workgroups dispatched before it, about one segment earlier; and the
-// keys it re-reads were read by the max workgroups one period before, with
-// the period's other traffic (one layer's values, pool and the next layer's
-// keys) in between, within the 256 MB Infinity Cache. A wait that runs past
-// the poll bound reads the layer's keys itself: the maximum is exact either
-// way, residency decides only the speed.
+// (layer, workgroup). The segment's last workgroup then reads the layer's A
+// words until all carry this call's number and publishes their maximum as
+// one more tagged word, the layer's. An "encode l" workgroup (one 16-token
+// block per wave) issues its key and value loads, reads the layer's word
+// until it carries this call's number, quantises the keys and encodes the
+// values. Measured on the Llama 32K pool: 1226 us against 1377 us for a
+// key-maximum pass over all layers followed by the encode (the keys read
+// twice from HBM), bit-identical; one word per layer rather than the A
+// share words read by every encode wave: fewer instructions per block.
+// Workgroups are dispatched in order on each XCD, so a wave waits only on
+// workgroups dispatched before it (the layer's word: about one segment
+// earlier); and the keys it re-reads were read by the max workgroups one
+// period before, with the period's other traffic (one layer's values, pool
+// and the next layer's keys) in between, within the 256 MB Infinity Cache.
+// A wait that runs past the poll bound reads the layer's keys itself (an
+// encode wave) or publishes nothing (the last max workgroup): the maximum
+// is exact either way, residency decides only the speed.
 __device__ __forceinline__ uint64_t* layered_words(uint32_t* ws, uint32_t A, uint32_t l) {
     return reinterpret_cast<uint64_t*>(ws + kWsHead) + (uint64_t)l * A;
+}
+// The layer's word, after all layers' share words.
+__device__ __forceinline__ uint64_t* layered_layer_word(uint32_t* ws, uint32_t A, uint32_t L, uint32_t l) {
+    return reinterpret_cast<uint64_t*>(ws + kWsHead) + (uint64_t)L * A + l;
 }
 
 template <int D>
@@ -1076,7 +1098,33 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_layered_kernel(Enco
             __hip_atomic_store(layered_words(p.ws, A, layer) + idx, tag | m, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        return;
+        if (idx != A - 1 || wib != 0 || p.poll_ticks == 0) return;
+        // the segment's last workgroup, one wave: the layer's word from the
+        // A share words (lane i reads words i, i + 64, ...)
+        constexpr int kPer = kLayeredMaxGroups / kWave;
+        const uint64_t* f = layered_words(p.ws, A, layer);
+        const uint64_t start = wall_clock64();
+        for (;;) {
+            bool all = true;
+            uint32_t mx = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t g = lane + (uint32_t)i * kWave;
+                const uint64_t w = g < A ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
+                all = all && ((w & ~0x7FFFull) == tag);
+                const uint32_t x = (uint32_t)(w & 0x7FFFu);
+                mx = x > mx ? x : mx;
+            }
+            if (__builtin_amdgcn_ballot_w64(!all) == 0) {
+                mx = wave_max_u32(mx);
+                if (lane == 0)
+                    __hip_atomic_store(layered_layer_word(p.ws, A, p.L, layer), tag | mx, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                return;
+            }
+            if (wall_clock64() - start >= p.poll_ticks) return;
+            __builtin_amdgcn_s_sleep(1);
+        }
     }
     const uint32_t blk = idx * WPB + wib;
     if (blk >= p.blocks_per_layer) return;
@@ -1084,33 +1132,26 @@ __global__ __launch_bounds__(kBlockThreads) void pool_encode_layered_kernel(Enco
     uint4 kraw[D / 32], vraw[D / 32];
     load_lane<D>(p.k, b.elem, kraw);
     load_lane<D>(p.v, b.elem, vraw);
-    // the layer's A words (lane i reads words i, i + 64, ...), again until all
-    // carry this call's number or the poll bound runs out
-    constexpr int kPer = kLayeredMaxGroups / kWave;
-    const uint64_t* f = layered_words(p.ws, A, layer);
+    // the layer's word (one address for the wave), again until it carries
+    // this call's number or the poll bound runs out
+    const uint64_t* f = layered_layer_word(p.ws, A, p.L, layer);
     const uint64_t start = wall_clock64();
     uint32_t mx = 0;
-    bool all_flagged = false;
-    for (;;) {
-        bool all = true;
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const uint32_t g = lane + (uint32_t)i * kWave;
-            const uint64_t w = g < A ? __hip_atomic_load(f + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
-            all = all && ((w & ~0x7FFFull) == tag);
-            const uint32_t x = (uint32_t)(w & 0x7FFFu);
-            m = x > m ? x : m;
+    bool flagged = false;
+    if (p.poll_ticks != 0) {
+        for (;;) {
+            const uint64_t w = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t lo = wave_uniform((uint32_t)w), hi = wave_uniform((uint32_t)(w >> 32));
+            if ((((uint64_t)hi << 32 | lo) & ~0x7FFFull) == tag) {
+                mx = lo & 0x7FFFu;
+                flagged = true;
+                break;
+            }
+            if (wall_clock64() - start >= p.poll_ticks) break;
+            __builtin_amdgcn_s_sleep(1);
         }
-        if (p.poll_ticks != 0 && __builtin_amdgcn_ballot_w64(!all) == 0) {
-            mx = wave_max_u32(m);
-            all_flagged = true;
-            break;
-        }
-        if (wall_clock64() - start >= p.poll_ticks) break;
-        __builtin_amdgcn_s_sleep(1);
     }
-    if (!all_flagged) mx = layer_absmax_direct<D>(p, layer, lane);
+    if (!flagged) mx = layer_absmax_direct<D>(p, layer, lane);
     // keys first: their registers are free before the value transform's
     quantize_keys<D>(p, b, kraw, mx, stage_all[wib], lane);
     encode_values<D>(p, b, vraw, stage_all[wib], lane);
