@@ -243,13 +243,16 @@ def test_long_context_32k_pool_layer_streamed():
 
 
 @pytest.mark.parametrize("shape,cfg", [((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2), ((5, 2, 77, 128), 5),
-                                       ((2, 8, 4112, 128), 3), ((1, 32, 2064, 64), 2), ((40, 1, 16, 64), 1)])
+                                       ((2, 8, 4112, 128), 3), ((1, 2, 17000, 128), 5), ((3, 8, 32768, 128), 5),
+                                       ((1, 1, 262400, 128), 5), ((1, 32, 2064, 64), 2), ((40, 1, 16, 64), 1)])
 def test_encode_many_blocks_per_layer(shape, cfg):
-    """Layers of hundreds of 16-token blocks: the key max is reduced over
-    many workgroups before any key is coded. On a 256-CU GPU a single-pass
-    round holds 2048 blocks at d = 128 and 4096 at d = 64, so the 4112- and
-    2064-token shapes (2056 and 4128 blocks per layer) take the layered
-    encode; 40 one-block layers take more than one round of 32 layers."""
+    """Layers of hundreds to thousands of 16-token blocks: the key max is
+    reduced over many workgroups before any key is coded. On a 256-CU GPU a
+    single-pass round holds 2048 blocks at d = 128 and 4096 at d = 64, so
+    the 4112-, 17000- (last block of 8 tokens), 32K- and 262400-token d = 128
+    shapes (2056 to 16400 blocks per layer) and the 2064-token d = 64 shape
+    (4128) take the layered encode; 40 one-block layers take more than one
+    round of 32 layers."""
     say("encode", shape)
     k, v = _inputs(shape, cfg, 4)
     assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
@@ -288,13 +291,16 @@ def test_two_concurrent_encodes():
 
 @pytest.mark.parametrize("poll_us", ["0", "1"])
 @pytest.mark.parametrize("shape,cfg", [((1, 4, 256, 64), 1), ((3, 8, 512, 128), 3), ((2, 32, 256, 64), 2),
-                                       ((40, 1, 16, 64), 1), ((32, 8, 4096, 128), 3)])
+                                       ((40, 1, 16, 64), 1), ((32, 8, 4096, 128), 3), ((2, 8, 4112, 128), 3),
+                                       ((1, 32, 2064, 64), 2)])
 def test_encode_layer_max_computed_directly(monkeypatch, poll_us, shape, cfg):
-    """The single-pass encode gathers each layer's key maximum from every
-    workgroup's published word; a coordinator that has not seen them all
-    within the poll bound reads the layer's keys itself. With a bound of 0
-    every coordinator takes that route for every layer, with 1 us whenever
-    a word is late: the pool must be the same bytes either way."""
+    """Both encode paths gather a layer's key maximum from words other
+    workgroups publish; a wave that has not seen them within the poll bound
+    reads the layer's keys itself (a single-pass coordinator, or a layered
+    encode wave; the layered encode's last key-maximum workgroup then
+    publishes nothing). With a bound of 0 every such wait takes that route
+    for every layer, with 1 us whenever a word is late: the pool must be the
+    same bytes either way (single-pass and layered shapes)."""
     monkeypatch.setenv("KVC_ENCODE_POLL_US", poll_us)
     say("encode, poll bound", poll_us, "us, shape", shape)
     k, v = _inputs(shape, cfg, 6)
