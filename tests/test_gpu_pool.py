@@ -74,6 +74,57 @@ def test_encode_special_vectors():
     assert_pool_equal(got, oracle.pool_encode(bits, v), shape)
 
 
+def _near_midpoint_values(n, seed):
+    """Channels 0..3 (bf16 bits) of n value vectors whose binary32 root of
+    the mean square, rounded to binary32, lies within 3 ulps of a binary16
+    rounding midpoint, or on one: the encoder rounds that root to binary32
+    and then to binary16, so these are the vectors where a root off by an
+    ulp would round to the other binary16. Found among random vectors whose
+    four nonzero channels' squares fall off by 2^-8 each, summed in the
+    encoder's pairwise binary32 order."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    found, have = [], 0
+    while have < n:
+        m = 1 << 20
+        mag = np.sqrt(128.0) * 2.0 ** rng.uniform(-13.5, 15.5, m)
+        ch = [synth.f32_to_bf16_bits((mag * 2.0 ** (-4 * i) * rng.uniform(0.5, 1.0, m)).astype(f32))
+              for i in range(4)]
+        sq = [synth.bf16_bits_to_f32(c) * synth.bf16_bits_to_f32(c) for c in ch]  # exact in binary32
+        ss = (sq[0] + sq[1]) + (sq[2] + sq[3])
+        r = np.sqrt(ss * f32(1.0 / 128))
+        bits = r.view(np.uint32)
+        sel = ((((bits - np.uint32(0xFFD)) & np.uint32(0x1FFF)) <= 6) & (r >= f32(2.0 ** -14)) &
+               (r < f32(65504.0)))
+        found.append(np.stack([c[sel] for c in ch], axis=1))
+        have += int(sel.sum())
+    return np.concatenate(found)[:n]
+
+
+def test_encode_value_scale_near_binary16_midpoints():
+    """Value vectors whose scale sits at the edges of its binary16 rounding:
+    the root of the mean square within 3 binary32 ulps of a binary16
+    rounding midpoint (ties included), below binary16's normal range, and
+    zero vectors; the scale's reciprocal then meets every binary16 these
+    round to. The pool must match the oracle's binary32 square root and
+    division byte for byte."""
+    shape = (1, 2, 2048, 128)
+    k, _ = _inputs(shape, 3, 9)
+    rng = np.random.default_rng(11)
+    v = synth.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    flat = v.reshape(-1, 128)
+    n_mid = 3584
+    flat[:n_mid] = 0
+    flat[:n_mid, :4] = _near_midpoint_values(n_mid, 10)
+    # means below binary16's normal range (scales 2^-24 .. 2^-14) and zeros
+    flat[n_mid:n_mid + 256] = 0
+    flat[n_mid:n_mid + 256, 0] = synth.f32_to_bf16_bits(
+        (np.sqrt(128.0) * 2.0 ** rng.uniform(-25.0, -13.5, 256)).astype(np.float32))
+    flat[n_mid + 256:n_mid + 288] = 0
+    say("encode,", n_mid, "vectors at binary16 rounding midpoints")
+    assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
+
+
 def test_encode_non_finite_inputs_bit_exact():
     """The stated rule for Inf and NaN inputs, on the GPU as in the oracle:
     a layer with an Inf or NaN key gets a NaN scale and zero codes; value
