@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="only parse two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a "
                          "--calibrate-copy run, write --traffic and print a summary table")
+    ap.add_argument("--traffic-runs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="only print FETCH_SIZE / WRITE_SIZE per dispatch for each run of consecutive dispatches of "
+                         "one codec kernel with one grid size (e.g. of an --other-configs --calibrate-copy run)")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="only parse the kernel trace of a profiled bench run (rocprofv3 --kernel-trace, csv): "
                          "per-kernel durations over the step's timed dispatches, the op sums and the roofline "
@@ -139,6 +142,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.warmup, args.steps)
+        return
+    if args.traffic_runs:
+        traffic_runs(*args.traffic_runs)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this codec is measured on "
@@ -409,13 +415,7 @@ def main():
                 "frac_of_mix_ceiling": round(mix_ceiling_us(dom) / (t_dom * 1e6), 4)}
 
     if args.calibrate_copy:
-        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        with torch.cuda.stream(stream):
-            for _ in range(3):
-                dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -531,6 +531,19 @@ def hop_drift(kv, synth, k, v, shape, widths_np, seed, stream, dev, hops=5):
 
 
 CALIBRATION_BYTES = 1 << 30
+
+
+def calibration_copies(dev, stream):
+    """Three device copies of CALIBRATION_BYTES, whose FETCH_SIZE and
+    WRITE_SIZE readings scale those counters to bytes."""
+    import torch
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 CODEC_KERNELS = ["pool_decode_kernel", "fanout_copy_kernel", "pool_encode_fused_kernel", "pool_encode_layered_kernel",
                  "card_pack_kernel", "card_unpack_kernel", "card_scan_kernel",
                  "card_transcode_kernel", "realign_keys_kernel", "lowrank_materialize_kernel",
@@ -644,6 +657,10 @@ def other_configs(args):
     emit(w, "card unpack", tu, card_n + 2 * kv_bytes, card_bytes=card_n)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set"
+    del k, v, card, ko, vo
+    torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        calibration_copies(dev, stream)
 
 
 def traffic_from_counters(fetch_dir, write_dir, out_path, agents):
@@ -686,6 +703,52 @@ def traffic_from_counters(fetch_dir, write_dir, out_path, agents):
         json.dump(out, f, indent=1)
     print("\n".join(lines))
     print(f"copy factors: {factors}; library sha {sha}")
+
+
+def traffic_runs(fetch_dir, write_dir):
+    """FETCH_SIZE and WRITE_SIZE per dispatch (medians, scaled to bytes as in
+    traffic_from_counters) for each run of consecutive dispatches of one
+    codec kernel with one grid size: the workloads of an --other-configs run
+    call the same kernels in turn."""
+    import csv
+    import glob
+    import re
+
+    import numpy as np
+    runs = {}
+    factors = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {folder}, found {files}")
+        with open(files[0]) as f:
+            rows = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
+                          for r in csv.DictReader(f) if r["Counter_Name"] == counter)
+        copies = [v for _, n, _, v in rows if n.startswith(COPY_KERNEL)][-3:]
+        if len(copies) != 3:
+            raise SystemExit(f"{counter}: calibration copies not found")
+        factors[counter] = CALIBRATION_BYTES / (float(np.median(copies)) * 1024.0)
+        seq = []
+        for _, n, g, v in rows:
+            k = next((k for k in CODEC_KERNELS if k + "<" in n or k + "(" in n), None)
+            if k is None:
+                continue
+            m = re.search(re.escape(k) + r"(<[^>]*>)?", n)
+            name = m.group(0)
+            if seq and seq[-1][0] == (name, g):
+                seq[-1][1].append(v)
+            else:
+                seq.append(((name, g), [v]))
+        runs[counter] = seq
+    print("| kernel | grid (threads) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes read | bytes written |")
+    print("|---|---|---|---|---|---|---|")
+    for (key, fv), (key2, wv) in zip(runs["FETCH_SIZE"], runs["WRITE_SIZE"]):
+        if key != key2:
+            raise SystemExit("the two runs dispatched different kernels")
+        fk, wk = float(np.median(fv)), float(np.median(wv))
+        print(f"| {key[0]} | {key[1]} | {len(fv)} | {fk:.0f} | {wk:.0f} | {fk * 1024 * factors['FETCH_SIZE']:.4g} | "
+              f"{wk * 1024 * factors['WRITE_SIZE']:.4g} |")
+    print(f"copy factors: {factors}; library sha {_lib_sha(os.path.join(ROOT, 'agent_handoff_amd', 'libkvcodec.so'))}")
 
 
 def _lib_sha(path):
