@@ -208,13 +208,7 @@ int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int6
     if (!aligned(k_in, 16) || !aligned(k_out, 16)) return KVC_E_ALIGN;
     const uint64_t kb = kv_bytes(shape);
     if (k_in != k_out && overlap(k_in, kb, k_out, kb)) return KVC_E_ALIAS;
-    double c[kvc::kMaxRealignPairs], s[kvc::kMaxRealignPairs];
-    for (uint32_t j = 0; j < shape->head_dim / 2; ++j) {
-        const double phi = (double)delta * (double)inv_freq[j];
-        c[j] = cos(phi);
-        s[j] = sin(phi);
-    }
-    const hipError_t e = kvc::launch_realign_keys(to_shape(shape), k_in, k_out, c, s, pairing, stream);
+    const hipError_t e = kvc::launch_realign_keys(to_shape(shape), k_in, k_out, delta, inv_freq, pairing, stream);
     return e == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 

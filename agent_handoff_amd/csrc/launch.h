@@ -51,11 +51,11 @@ hipError_t launch_card_transcode(const Shape& s, const void* card_in, uint64_t c
                                  const uint8_t* new_widths, void* card_out, uint64_t capacity,
                                  uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, hipStream_t stream);
 
-// Key re-alignment: at most 64 channel pairs (d <= 128); cos and sin of
-// delta * f_j per pair, binary64.
+// Key re-alignment: at most 64 channel pairs (d <= 128); inv_freq is a host
+// array of d/2 inverse frequencies, delta the positions to move by.
 constexpr int kMaxRealignPairs = 64;
-hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, const double* cos_tab,
-                               const double* sin_tab, uint32_t pairing, hipStream_t stream);
+hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, int64_t delta, const float* inv_freq,
+                               uint32_t pairing, hipStream_t stream);
 
 // Low-rank anchor materialisation over M matrices of T x (H*d); r is 32 or
 // 64, V <= 32 (the weights sit one per lane), and V anchors' R rows for one

@@ -6,19 +6,20 @@
 // this. Rotary keys at position p hold each channel pair j rotated by
 // p * f_j, so moving them by delta positions rotates pair j by delta * f_j
 // more. The pairing of channels and the inverse frequencies f_j belong to
-// the model and are inputs; cos and sin of delta * f_j arrive from the host
-// in binary64 as kernel arguments. Each rotated value is a*c - b*s (or
-// a*s + b*c) in binary64, two products and a difference, then rounded once
-// to bf16: binary32 cos and sin lose too much when the two products nearly
-// cancel.
+// the model and are inputs. Each workgroup takes cos and sin of
+// delta * f_j (the product in binary64, exact as the host's) in binary64
+// with the device math library, one pair per thread, into LDS. Each
+// rotated value is a*c - b*s (or a*s + b*c) in binary64, two products and
+// a difference, then rounded once to bf16: binary32 cos and sin lose too
+// much when the two products nearly cancel.
 //
 // Work mapping: a lane rotates 8 channel pairs of one vector, so d/16 lanes
 // cover a vector (8 vectors per wave at d = 128); every access is a 16-byte
 // load or store, in place allowed (a lane reads its chunks before writing
 // them, and no chunk is shared between lanes). A lane always handles the
 // same 8 pairs, so the grid is persistent: each lane takes its 16 cos and
-// sin values from the kernel arguments once, into registers, and then
-// streams vector groups, two at a time.
+// sin values from LDS once, into registers, and then streams vector groups,
+// two at a time.
 #include "kernels_common.h"
 #include "launch.h"
 
@@ -32,8 +33,8 @@ struct RealignParams {
     uint16_t* k_out;
     uint64_t vecs;      // L * H * T
     uint32_t pairing;   // 0: (j, j + d/2); 1: (2j, 2j + 1)
-    double c[kMaxRealignPairs];
-    double s[kMaxRealignPairs];
+    int64_t delta;      // positions to move by
+    float f[kMaxRealignPairs];  // inverse frequency of each pair
 };
 
 // Binary64 to bf16, round to nearest even, with one correct rounding: the
@@ -100,12 +101,20 @@ __global__ __launch_bounds__(kBlockThreads) void realign_keys_kernel(RealignPara
     const uint64_t nwaves = (uint64_t)gridDim.x * (kBlockThreads / kWave);
     const uint64_t groups = (p.vecs + VPW - 1) / VPW;  // VPW vectors each
     const uint32_t i = lane % LPV;           // pairs 8i .. 8i + 7
+    // cos and sin of every pair's angle, once per workgroup
+    __shared__ double cs_lds[D / 2], sn_lds[D / 2];
+    if (threadIdx.x < D / 2) {
+        const double phi = (double)p.delta * (double)p.f[threadIdx.x];
+        cs_lds[threadIdx.x] = cos(phi);
+        sn_lds[threadIdx.x] = sin(phi);
+    }
+    __syncthreads();
     // pair set 8i .. 8i + 7 in both pairings
     double c[8], sn[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        c[u] = p.c[8 * i + u];
-        sn[u] = p.s[8 * i + u];
+        c[u] = cs_lds[8 * i + u];
+        sn[u] = sn_lds[8 * i + u];
     }
     const uint32_t oa = p.pairing == 0 ? 8 * i : 16 * i;
     const uint32_t ob = p.pairing == 0 ? D / 2 + 8 * i : 16 * i + 8;
@@ -126,17 +135,15 @@ __global__ __launch_bounds__(kBlockThreads) void realign_keys_kernel(RealignPara
 
 }  // namespace
 
-hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, const double* cos_tab,
-                               const double* sin_tab, uint32_t pairing, hipStream_t stream) {
+hipError_t launch_realign_keys(const Shape& s, const void* k_in, void* k_out, int64_t delta, const float* inv_freq,
+                               uint32_t pairing, hipStream_t stream) {
     RealignParams p{};
     p.k_in = static_cast<const uint16_t*>(k_in);
     p.k_out = static_cast<uint16_t*>(k_out);
     p.vecs = (uint64_t)s.L * s.H * s.T;
     p.pairing = pairing;
-    for (uint32_t j = 0; j < s.d / 2; ++j) {
-        p.c[j] = cos_tab[j];
-        p.s[j] = sin_tab[j];
-    }
+    p.delta = delta;
+    for (uint32_t j = 0; j < s.d / 2; ++j) p.f[j] = inv_freq[j];
     const uint32_t vpw = kWave / (s.d / 16);
     const uint64_t groups = (p.vecs + vpw - 1) / vpw;
     // persistent: 8 workgroups of 4 waves per CU, fewer for small inputs

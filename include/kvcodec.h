@@ -293,9 +293,9 @@ int cachecard_transcode(const kvc_shape* shape, const void* card_in, size_t card
  *   delta        target position minus source position
  *   inv_freq     host, d/2 floats: the model's rotary inverse frequencies
  *   pairing      KVC_ROPE_HALVES or KVC_ROPE_ADJACENT
- * cos and sin of delta * inv_freq[j] are taken in binary64 on the host; each
- * rotated value is a*c - b*s or a*s + b*c in binary64 (two products, then
- * the sum), rounded once to bf16, ties to even.
+ * cos and sin of delta * inv_freq[j] (the product in binary64) are taken in
+ * binary64 on the device; each rotated value is a*c - b*s or a*s + b*c in
+ * binary64 (two products, then the sum), rounded once to bf16, ties to even.
  * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_RANGE (pairing), KVC_E_ALIGN,
  * KVC_E_ALIAS, KVC_E_HIP. */
 int kvc_realign_keys(const kvc_shape* shape, const void* k_in, void* k_out, int64_t delta,
