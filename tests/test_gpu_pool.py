@@ -125,11 +125,13 @@ def test_encode_value_scale_near_binary16_midpoints():
     assert_pool_equal(gpu_encode(shape, k, v).cpu().numpy(), oracle.pool_encode(k, v), shape)
 
 
-def test_encode_non_finite_inputs_bit_exact():
+@pytest.mark.parametrize("shape", [(3, 2, 40, 128), (3, 8, 4112, 128)])
+def test_encode_non_finite_inputs_bit_exact(shape):
     """The stated rule for Inf and NaN inputs, on the GPU as in the oracle:
     a layer with an Inf or NaN key gets a NaN scale and zero codes; value
-    vectors with Inf or NaN get the saturated scale and comparison codes."""
-    shape = (3, 2, 40, 128)
+    vectors with Inf or NaN get the saturated scale and comparison codes.
+    The second shape takes the layered encode (2056 blocks per layer), whose
+    key-maximum workgroups and layer word carry the non-finite maxima."""
     k, v = _inputs(shape, 3, 8)
     k[0, 1, 3, 7] = 0x7FC1   # NaN
     k[1, 0, 9, 2] = 0xFF80   # -Inf
