@@ -174,6 +174,7 @@ int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const u
                    int32_t* dev_status, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!shape || !k || !v || !widths || !meta || !card || !ws) return KVC_E_NULL;
     if (!card_shape(shape)) return KVC_E_SHAPE;
+    if (meta->group_size != 0 && meta->group_size != 32) return KVC_E_RANGE;
     const uint64_t ws_need = card_ws_bytes(shape);
     if (ws_bytes < ws_need || card_capacity < kvc::card_payload_offset(shape->num_tokens)) return KVC_E_SIZE;
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(card, 256) || !aligned(ws, 16) ||

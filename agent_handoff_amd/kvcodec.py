@@ -41,7 +41,8 @@ class kvc_shape(ctypes.Structure):
 
 
 class kvc_card_meta(ctypes.Structure):
-    _fields_ = [("model_id", ctypes.c_char * 64), ("position_offset", ctypes.c_int64)]
+    _fields_ = [("model_id", ctypes.c_char * 64), ("position_offset", ctypes.c_int64),
+                ("group_size", ctypes.c_uint32)]
 
 
 def _load():
@@ -232,6 +233,7 @@ def cachecard_pack(shape, k, v, widths, card, ws, model_id=b"", position_offset=
     mid = model_id.encode() if isinstance(model_id, str) else bytes(model_id)
     meta.model_id = mid[:63]
     meta.position_offset = int(position_offset)
+    meta.group_size = 32
     n = _kv_numel(shape)
     args = (_want(k, torch.bfloat16, n, "k"), _want(v, torch.bfloat16, n, "v"),
             _want(widths, torch.uint8, int(shape[2]), "widths"))

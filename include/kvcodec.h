@@ -66,6 +66,8 @@ typedef struct kvc_shape {
 typedef struct kvc_card_meta {
     char model_id[64];       /* NUL-terminated, at most 63 characters kept */
     int64_t position_offset; /* position of token 0 in the sender's sequence */
+    uint32_t group_size;     /* channels per quantisation group: 32, the only
+                                size (0 is taken as 32; others are refused) */
 } kvc_card_meta;
 
 enum {
@@ -215,7 +217,8 @@ size_t cachecard_workspace_bytes(const kvc_shape* shape);
  *   k, v            device bf16 [L][H][T][d]; d a multiple of 32 (64 or 128)
  *   widths          device u8[T], each 2, 4, 8 or 16; one width per token,
  *                   shared by every layer, head, K and V
- *   meta            host; model_id and position_offset copied into the header
+ *   meta            host; model_id and position_offset copied into the header;
+ *                   group_size 32 (or 0)
  *   card            device, card_capacity bytes, 256-byte aligned
  *   dev_card_bytes  device u64 or NULL; receives the card's exact size
  *   dev_status      device int32 or NULL; KVC_DEV_BAD_WIDTH, KVC_DEV_CAPACITY
@@ -223,8 +226,8 @@ size_t cachecard_workspace_bytes(const kvc_shape* shape);
  *   ws              device workspace, >= cachecard_workspace_bytes(shape)
  * Per group of 32 channels at width b < 16: mn, mx = group min and max,
  * s = fp16((mx - mn) / (2^b - 1)), q = min(rint((x - mn) / s), 2^b - 1).
- * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_SIZE, KVC_E_ALIGN, KVC_E_ALIAS,
- * KVC_E_HIP. */
+ * Errors: KVC_E_NULL, KVC_E_SHAPE, KVC_E_RANGE (group_size), KVC_E_SIZE,
+ * KVC_E_ALIGN, KVC_E_ALIAS, KVC_E_HIP. */
 int cachecard_pack(const kvc_shape* shape, const void* k, const void* v, const uint8_t* widths,
                    const kvc_card_meta* meta, void* card, size_t card_capacity,
                    uint64_t* dev_card_bytes, int32_t* dev_status, void* ws, size_t ws_bytes,

@@ -197,6 +197,11 @@ def test_card_argument_errors():
 
     assert pack(m=None) == kv.KVC_E_NULL
     assert pack(shape=kv.kvc_shape(1, 1, 4, 48)) == kv.KVC_E_SHAPE
+    assert ctypes.sizeof(kv.kvc_card_meta) == 80  # char[64], int64, uint32, padding
+    for gs, rc in ((16, kv.KVC_E_RANGE), (64, kv.KVC_E_RANGE), (1, kv.KVC_E_RANGE)):
+        bad = kv.kvc_card_meta()
+        bad.group_size = gs
+        assert pack(m=bad) == rc
     assert pack(ws_bytes=8) == kv.KVC_E_SIZE
     assert pack(capacity=256) == kv.KVC_E_SIZE
     assert pack(card=3 * A + 128) == kv.KVC_E_ALIGN
