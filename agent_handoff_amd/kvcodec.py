@@ -368,3 +368,104 @@ def kvc_codebook():
     th = np.zeros(7, np.float32)
     _lib.kvc_codebook(lv.ctypes.data_as(ctypes.c_void_p), th.ctypes.data_as(ctypes.c_void_p))
     return lv, th
+
+
+# ------------------------------------------------------------------ object wrappers
+
+class SharedKVPool:
+    """The shared pool of the write-once, read-many cache (PolyKV §2.A: the
+    shared document's K/V compressed once into one object that every agent
+    decodes layer by layer into its own cache). Holds the pool bytes and
+    the shape; allocates buffers on the inputs' device and calls
+    kvpool_encode / kvpool_decode on torch's current stream."""
+
+    def __init__(self, shape, pool):
+        self.shape = tuple(int(x) for x in shape)
+        self.pool = pool
+
+    @classmethod
+    def encode(cls, k, v, ws=None, dev_status=None):
+        """k, v: bf16 [L, H, T, d] device tensors. ws: a zeroed workspace to
+        reuse across encodes, or None for a new one."""
+        shape = tuple(k.shape)
+        pool = torch.empty(kvpool_bytes(shape), dtype=torch.uint8, device=k.device)
+        if ws is None:
+            ws = torch.zeros(kvpool_workspace_bytes(shape), dtype=torch.uint8, device=k.device)
+        kvpool_encode(shape, k, v, pool, ws, dev_status)
+        return cls(shape, pool)
+
+    def decode_layers(self, layer_begin=0, layer_end=None, k_outs=None, v_outs=None, n_agents=1, dev_status=None):
+        """Layers [layer_begin, layer_end) into each agent's K and V buffers
+        (new bf16 tensors for n_agents agents when k_outs / v_outs are None);
+        returns (k_outs, v_outs)."""
+        L, H, T, d = self.shape
+        layer_end = L if layer_end is None else int(layer_end)
+        n = max(layer_end - int(layer_begin), 0)
+        if k_outs is None:
+            k_outs = [torch.empty((n, H, T, d), dtype=torch.bfloat16, device=self.pool.device) for _ in range(n_agents)]
+        if v_outs is None:
+            v_outs = [torch.empty((n, H, T, d), dtype=torch.bfloat16, device=self.pool.device) for _ in range(n_agents)]
+        kvpool_decode(self.shape, self.pool, layer_begin, layer_end, k_outs, v_outs, dev_status)
+        return k_outs, v_outs
+
+
+class CacheCard:
+    """A CacheCard (QKVShare: quantised groups, per-token widths and
+    metadata in one buffer). Holds the card bytes, their exact size and the
+    shape; allocates buffers on the inputs' device and calls
+    cachecard_pack / cachecard_unpack / cachecard_transcode on torch's
+    current stream. Data errors (a width outside {2, 4, 8, 16}, a refused
+    header) land in the status word, read by status()."""
+
+    def __init__(self, shape, card, nbytes, dev_status):
+        self.shape = tuple(int(x) for x in shape)
+        self.card = card
+        self.nbytes = int(nbytes)
+        self.dev_status = dev_status
+
+    @staticmethod
+    def _widths(widths, device, T):
+        w_host = widths.cpu().numpy() if isinstance(widths, torch.Tensor) else np.asarray(widths, np.uint8)
+        w_host = np.ascontiguousarray(w_host, np.uint8).reshape(-1)
+        if w_host.size != T:
+            raise ValueError(f"widths: expected {T} values, got {w_host.size}")
+        return w_host, torch.from_numpy(w_host).to(device)
+
+    @classmethod
+    def pack(cls, k, v, widths, model_id=b"", position_offset=0):
+        """k, v: bf16 [L, H, T, d] device tensors; widths: T values in
+        {2, 4, 8, 16} (host array or tensor)."""
+        shape = tuple(k.shape)
+        w_host, w_dev = cls._widths(widths, k.device, shape[2])
+        n = cachecard_bytes_host(shape, w_host)
+        card = torch.empty(max(n, 1), dtype=torch.uint8, device=k.device)
+        ws = torch.empty(cachecard_workspace_bytes(shape), dtype=torch.uint8, device=k.device)
+        status = torch.zeros(1, dtype=torch.int32, device=k.device)
+        cachecard_pack(shape, k, v, w_dev, card, ws, model_id, position_offset, None, status)
+        return cls(shape, card, n, status)
+
+    def unpack(self, k_out=None, v_out=None):
+        """Full-width bf16 K and V (new tensors when k_out / v_out are None)."""
+        dev = self.card.device
+        if k_out is None:
+            k_out = torch.empty(self.shape, dtype=torch.bfloat16, device=dev)
+        if v_out is None:
+            v_out = torch.empty(self.shape, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(cachecard_workspace_bytes(self.shape), dtype=torch.uint8, device=dev)
+        cachecard_unpack(self.shape, self.card, k_out, v_out, ws, self.nbytes, self.dev_status)
+        return k_out, v_out
+
+    def transcode(self, new_widths):
+        """The card at new per-token widths (one hop), as a new CacheCard."""
+        dev = self.card.device
+        w_host, w_dev = self._widths(new_widths, dev, self.shape[2])
+        n = cachecard_bytes_host(self.shape, w_host)
+        card = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        ws = torch.empty(cachecard_transcode_workspace_bytes(self.shape), dtype=torch.uint8, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        cachecard_transcode(self.shape, self.card, w_dev, card, ws, self.nbytes, None, status)
+        return CacheCard(self.shape, card, n, status)
+
+    def status(self):
+        """The card's device status word (synchronises): 0, or KVC_DEV_* bits."""
+        return int(self.dev_status.item())
