@@ -354,3 +354,30 @@ def test_transcode_output_after_refused_input_is_refused():
     torch.cuda.synchronize()
     assert int(status.item()) & kv.KVC_DEV_BAD_HEADER
     _assert_refused_by_unpack(shape, out, prev.size)
+
+
+@pytest.mark.parametrize("T", LONG_T)
+def test_concurrent_unpacks_on_streams(T):
+    """One card read by four unpacks at once on four streams (each with its
+    own workspace): the card is read-many, every output equals a lone
+    unpack's."""
+    shape = (2, 3, T, 128)
+    k, v = synth.kv_bits(synth.WORKLOADS[4], 3, shape=shape)
+    w = _widths("runs", T, 3)
+    card, n, st = gpu_pack(shape, k, v, w)
+    assert st == 0
+    ref_k, ref_v, st = gpu_unpack(shape, card, n)
+    assert st == 0
+    outs = []
+    for s in [torch.cuda.Stream() for _ in range(4)]:
+        ko = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        vo = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        ws = dev_bytes(kv.cachecard_workspace_bytes(shape))
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        torch.cuda.synchronize()
+        kv.cachecard_unpack(shape, card, ko, vo, ws, card_bytes=n, dev_status=status, stream=s)
+        outs.append((ko, vo, status, ws))
+    torch.cuda.synchronize()
+    for ko, vo, status, _ in outs:
+        assert int(status.item()) == 0
+        assert np.array_equal(to_host(ko), to_host(ref_k)) and np.array_equal(to_host(vo), to_host(ref_v))
