@@ -23,15 +23,21 @@
 // lane-contiguous ds_read_b128. A wave owns NJ token blocks of 16 tokens
 // per tile and all d channels, computed transposed: out^T block = R_block
 // (16 channels x r) * A_block^T (r x 16 tokens). At r = 32, where the LDS
-// has room, 12 waves own one block each (192-token tiles, 168 VGPRs, three
-// waves per SIMD); otherwise 8 waves own two (256-token tiles, two waves per
-// SIMD, each R fragment read from LDS serving two blocks). MFMA row i of
+// has room, a workgroup runs 12 waves (three per SIMD): 8 compute waves own
+// one block each (128-token tiles) and hand each finished block, through a
+// double-buffered LDS staging area and a pair of flags, to one of 4 store
+// waves, which write it out with non-temporal stores. The compute waves
+// then never wait behind their own output stores (a wave's memory counter
+// retires in order, so a store in flight delays the wait for the next A
+// fragments). Otherwise 8 waves own two blocks each and store their own
+// output (256-token tiles, two waves per SIMD, each R fragment read from
+// LDS serving two blocks). MFMA row i of
 // channel block cb is channel (d/4)(i/4) + 4cb + i%4, which leaves lane l
 // holding token l%16 and the d/4 consecutive channels from (d/4)(l/16) on,
 // so source loads are 16-byte accesses. The (tile, anchor) steps of a chunk
 // form one pipeline: A fragments are requested five steps ahead (at r = 32),
 // a tile's source at the last step of the tile before, its output staged
-// and stored at its last. Matrices are dealt to XCDs (workgroup b runs on
+// (and, without store waves, stored) at its last. Matrices are dealt to XCDs (workgroup b runs on
 // XCD b % 8) so that the 8 heads sharing one matrix's A factors run on one
 // XCD and re-read them from its L2.
 #include "kernels_common.h"
@@ -68,12 +74,18 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 
 // waves per workgroup with NJ token blocks per wave
 constexpr int lr_waves(int nj) { return nj == 2 ? 8 : 12; }
+// the store-wave split at one token block per wave: 8 waves compute, 4
+// write the output
+constexpr int kSwCompute = 8, kSwStore = 4;
+constexpr uint64_t kFlagWaitTicks = 50000000;  // 0.5 s
+static_assert(kSwCompute + kSwStore == lr_waves(1) && kSwCompute == 2 * kSwStore, "store waves serve two compute waves each");
 
-template <int D, int KC, int NJ>
+template <int D, int KC, int NJ, bool SW = false>
 __global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kernel(LowrankParams p) {
     constexpr int W = lr_waves(NJ);
     constexpr int THR = W * kWave;
-    constexpr int TT = W * NJ * 16;  // tile tokens
+    constexpr int WC = SW ? kSwCompute : W;   // compute waves
+    constexpr int TT = WC * NJ * 16;  // tile tokens
     constexpr int NCB = D / 16;   // channel blocks of 16
     constexpr int CPL = D / 4;    // channels per lane in the output layout
     constexpr int SQ = CPL / 8;   // 16-byte source chunks per lane and token
@@ -119,6 +131,10 @@ __global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kern
                 }
             }
         }
+    }
+    if (SW) {
+        uint32_t* fl = reinterpret_cast<uint32_t*>(frag + p.V * KC * NCB * kWave + WC * 2 * 16 * p.stage_row);
+        if (threadIdx.x < 4 * WC) fl[threadIdx.x] = 0;
     }
     __syncthreads();
 
@@ -202,10 +218,81 @@ __global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kern
     constexpr uint32_t CR = D / 8;  // 16-byte chunks per token row
     constexpr uint32_t TPS = kWave / CR;  // token rows per store instruction
     const uint32_t SR = p.stage_row;
-    u32x4* stg = frag + p.V * KC * NCB * kWave + wave * 16 * SR;
+    u32x4* stage_base = frag + p.V * KC * NCB * kWave;
+    u32x4* stg = stage_base + wave * 16 * SR;
     u32x4* stg_w = stg + (lane % 16) * SR + g * SQ;       // this lane's chunks
     u32x4* stg_r = stg + (lane / CR) * SR + lane % CR;    // chunk lane of rows 0, TPS, ...
+    // With store waves: compute wave c stages the k-th tile of its chunk in
+    // buffer k % 2 and sets f_ready[c][k % 2] = k + 1; its store wave writes
+    // the block out and sets f_done[c][k % 2] = k + 1, after which the buffer
+    // may take tile k + 2. Both flags only grow. Every wait is bounded
+    // (kFlagWaitTicks of the 100 MHz clock, far beyond any tile's time), so
+    // the grid drains whatever happens.
+    uint32_t* flags = reinterpret_cast<uint32_t*>(stage_base + (SW ? WC * 2 : 0) * 16 * SR);
+    uint32_t* f_ready = flags;            // [WC][2]
+    uint32_t* f_done = flags + 2 * WC;    // [WC][2]
+    if (SW && wave >= (uint32_t)WC) {
+        // store wave sw serves compute waves 2 sw and 2 sw + 1, tile after tile
+        const uint32_t sw = wave - WC;
+        for (uint32_t k = 0; k < n_tiles; ++k) {
+            const uint32_t tile = tile0 + k, buf = k & 1;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const uint32_t c = 2 * sw + cc;
+                const uint64_t t0c = wall_clock64();
+                while (__hip_atomic_load(&f_ready[c * 2 + buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1) {
+                    if (wall_clock64() - t0c > kFlagWaitTicks) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                const u32x4* sr = stage_base + (c * 2 + buf) * 16 * SR + (lane / CR) * SR + lane % CR;
+                u32x4 x[SQ];
+#pragma unroll
+                for (int u = 0; u < SQ; ++u) x[u] = sr[u * TPS * SR];
+                const uint32_t tb = tile * TT + c * 16;
+                u32x4* dst = reinterpret_cast<u32x4*>(out + (uint64_t)tb * D) + lane;
+#pragma unroll
+                for (int u = 0; u < SQ; ++u)
+                    if (tb + (kWave * u + lane) / CR < p.T) __builtin_nontemporal_store(x[u], dst + kWave * u);
+                // the staging reads are complete before the buffer is handed back
+                // (the clobber keeps the flag store below the wait)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane == 0) __hip_atomic_store(&f_done[c * 2 + buf], k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        return;
+    }
     auto store_tile = [&](uint32_t tile) {
+        if (SW) {
+            const uint32_t k = tile - tile0, buf = k & 1;
+            u32x4* sb = stage_base + (wave * 2 + buf) * 16 * SR + (lane % 16) * SR + g * SQ;
+            if (k >= 2) {
+                const uint64_t t0c = wall_clock64();
+                while (__hip_atomic_load(&f_done[wave * 2 + buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k - 1) {
+                    if (wall_clock64() - t0c > kFlagWaitTicks) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < SQ; ++q) {
+                const uint32_t sw[4] = {sv[0][q].x, sv[0][q].y, sv[0][q].z, sv[0][q].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int cb = 2 * q + e2 / 2, e = 2 * (e2 % 2);
+                    o[e2] = pack_bf16x2(bf16_lo(sw[e2]) + acc[0][cb][e], bf16_hi(sw[e2]) + acc[0][cb][e + 1]);
+                }
+                sb[q] = u32x4{o[0], o[1], o[2], o[3]};
+            }
+            if (kEarlySrc) load_src_block(tile + 1, 0);
+            // the staged rows are in LDS before the flag says so
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) __hip_atomic_store(&f_ready[wave * 2 + buf], k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[0][cb][e] = 0.0f;
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const uint32_t tb = tile * TT + wave * 16 * NJ + 16 * j;  // the block's first token
@@ -309,9 +396,9 @@ __global__ __launch_bounds__(lr_waves(NJ) * kWave) void lowrank_materialize_kern
 
 uint64_t lowrank_lds_bytes(uint32_t d, uint32_t V, uint32_t r) { return (uint64_t)V * d * r * 2; }
 
-// the waves' output staging beside the R fragments: 16 token rows of
+// the output staging beside the R fragments, per buffer 16 token rows of
 // row_chunks 16-byte chunks each (d / 8, or one more where it fits)
-static uint64_t lowrank_stage_bytes(uint32_t row_chunks, uint32_t waves) { return (uint64_t)waves * 16 * row_chunks * 16; }
+static uint64_t lowrank_stage_bytes(uint32_t row_chunks, uint32_t buffers) { return (uint64_t)buffers * 16 * row_chunks * 16; }
 
 hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32_t d, uint32_t V, uint32_t r,
                                       const void* src, const void* a, const void* rf, const float* w, void* out,
@@ -327,11 +414,14 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     p.T = T;
     p.V = V;
     p.r = r;
-    // one token block per wave (12 waves) at r = 32 where its staging fits
-    // beside the R fragments, else two (8 waves)
+    // at r = 32, where the double-buffered staging of the 8 compute waves
+    // and the flags fit beside the R fragments, one token block per compute
+    // wave and 4 store waves; else two blocks per wave (8 waves, each
+    // staging and storing its own output)
     const uint64_t rb = lowrank_lds_bytes(d, V, r);
-    const bool nj1 = r == 32 && rb + lowrank_stage_bytes(d / 8, lr_waves(1)) <= kLdsBytes;
-    const uint32_t waves = lr_waves(nj1 ? 1 : 2), tt = waves * (nj1 ? 1 : 2) * 16;
+    const uint64_t flag_bytes = 4 * sizeof(uint32_t) * kSwCompute;
+    const bool nj1 = r == 32 && rb + lowrank_stage_bytes(d / 8, 2 * kSwCompute) + flag_bytes <= kLdsBytes;
+    const uint32_t waves = lr_waves(nj1 ? 1 : 2), tt = (nj1 ? kSwCompute : waves * 2) * 16;
     p.tiles = (T + tt - 1) / tt;
     // enough (matrix, head, chunk) items to give every CU one workgroup
     const uint64_t mh = (uint64_t)M * H;
@@ -342,11 +432,13 @@ hipError_t launch_lowrank_materialize(uint32_t M, uint32_t H, uint32_t T, uint32
     const uint64_t groups = (M + kXcds - 1) / kXcds;
     const uint64_t nblocks = groups * kXcds * p.chunks * H;
     if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    p.stage_row = rb + lowrank_stage_bytes(d / 8 + 1, waves) <= kLdsBytes ? d / 8 + 1 : d / 8;
-    const uint32_t lds = (uint32_t)(rb + lowrank_stage_bytes(p.stage_row, waves));
+    const uint32_t stage_buffers = nj1 ? 2 * kSwCompute : waves;
+    const uint64_t fb = nj1 ? flag_bytes : 0;
+    p.stage_row = rb + lowrank_stage_bytes(d / 8 + 1, stage_buffers) + fb <= kLdsBytes ? d / 8 + 1 : d / 8;
+    const uint32_t lds = (uint32_t)(rb + lowrank_stage_bytes(p.stage_row, stage_buffers) + fb);
     void (*kernel)(LowrankParams) =
-        d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2, 2> : (nj1 ? lowrank_materialize_kernel<64, 1, 1> : lowrank_materialize_kernel<64, 1, 2>))
-                : (r == 64 ? lowrank_materialize_kernel<128, 2, 2> : (nj1 ? lowrank_materialize_kernel<128, 1, 1> : lowrank_materialize_kernel<128, 1, 2>));
+        d == 64 ? (r == 64 ? lowrank_materialize_kernel<64, 2, 2> : (nj1 ? lowrank_materialize_kernel<64, 1, 1, true> : lowrank_materialize_kernel<64, 1, 2>))
+                : (r == 64 ? lowrank_materialize_kernel<128, 2, 2> : (nj1 ? lowrank_materialize_kernel<128, 1, 1, true> : lowrank_materialize_kernel<128, 1, 2>));
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return report_launch(e, "lowrank_materialize (LDS attribute)");
