@@ -79,14 +79,16 @@ def run(shape, V, r, seed, weights=None, in_place=False, cfg=3):
 
 
 @pytest.mark.parametrize("shape,V,r", [
-    ((2, 3, 300, 128), 3, 32),     # ragged tail: 300 = 256 + 2 blocks of 16 + 12
+    ((2, 3, 300, 128), 3, 32),     # ragged tail: 300 = 2 tiles of 128 + 2 blocks of 16 + 12
     ((1, 2, 40, 64), 2, 64),       # d = 64, r = 64, less than one tile
     ((9, 1, 17, 128), 1, 32),      # 9 matrices over 8 XCD groups, one anchor
     ((3, 2, 513, 128), 16, 32),    # most anchors at d = 128, r = 32
     ((2, 2, 64, 64), 32, 32),      # most anchors at d = 64 (one weight per lane)
     ((1, 1, 16, 128), 8, 64),      # most anchors at d = 128, r = 64
     ((2, 8, 1024, 128), 10, 32),   # the pages' defaults, Llama-3-8B heads
-    ((16, 8, 700, 64), 3, 32),     # chunks of two tiles per workgroup, ragged last chunk
+    ((16, 8, 700, 64), 3, 32),     # chunks of three tiles per workgroup (a staging buffer reused), ragged last tile
+    ((1, 2, 200, 128), 11, 32),    # the most anchors with store waves at d = 128, r = 32
+    ((1, 2, 200, 128), 12, 32),    # one more: two blocks per wave, no store waves
 ])
 def test_materialize_matches_oracle(shape, V, r):
     *_, exact = run(shape, V, r, seed=11)
