@@ -357,29 +357,12 @@ def main():
         kv.kvc_lowrank_materialize(shape, rank, n_anc, v, *fv, v_rt, stream=stream)
 
     tl = timed(lowrank, 10)
-    # the same pair timed after the GPU has idled for 20 ms: ten pairs back
-    # to back run long enough for the engine clock to drop (about 1.96 to
-    # 1.23 GHz within two milliseconds of this load), an idle pair does not
-
-    idle_s = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        time.sleep(0.02)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        lowrank()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        idle_s.append(e0.elapsed_time(e1) * 1e-3)
-    tl_idle = med(idle_s)
     bl = 2 * (2 * kv_bytes + sum(t.numel() * t.element_size() for t in fk))
     fl = 2 * (2.0 * L * n_anc * T * H * d * rank)
     ops_out["lowrank_materialize"] = {"us": round(tl * 1e6, 2), "bytes": bl, "GB/s": round(bl / tl / 1e9, 1),
                                       "frac_hbm_peak": round(bl / tl / 1e9 / HBM_PEAK_GBS, 4),
                                       "TFLOP/s": round(fl / tl / 1e12, 1),
                                       "frac_mfma_bf16_peak": round(fl / tl / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                                      "us_after_idle": round(tl_idle * 1e6, 2),
-                                      "frac_hbm_peak_after_idle": round(bl / tl_idle / 1e9 / HBM_PEAK_GBS, 4),
                                       "anchors": n_anc, "rank": rank}
     del fk, fv
     # the write-once side of the anchors: the rank-32 truncated SVD of the K
