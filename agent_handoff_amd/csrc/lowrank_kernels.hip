@@ -31,15 +31,15 @@
 // retires in order, so a store in flight delays the wait for the next A
 // fragments). Otherwise 8 waves own two blocks each and store their own
 // output (256-token tiles, two waves per SIMD, each R fragment read from
-// LDS serving two blocks). MFMA row i of
-// channel block cb is channel (d/4)(i/4) + 4cb + i%4, which leaves lane l
-// holding token l%16 and the d/4 consecutive channels from (d/4)(l/16) on,
-// so source loads are 16-byte accesses. The (tile, anchor) steps of a chunk
-// form one pipeline: A fragments are requested five steps ahead (at r = 32),
-// a tile's source at the last step of the tile before, its output staged
-// (and, without store waves, stored) at its last. Matrices are dealt to XCDs (workgroup b runs on
-// XCD b % 8) so that the 8 heads sharing one matrix's A factors run on one
-// XCD and re-read them from its L2.
+// LDS serving two blocks). MFMA row i of channel block cb is channel
+// (d/4)(i/4) + 4cb + i%4, which leaves lane l holding token l%16 and the
+// d/4 consecutive channels from (d/4)(l/16) on, so source loads are 16-byte
+// accesses. The (tile, anchor) steps of a chunk form one pipeline: A
+// fragments are requested five steps ahead (at r = 32), a tile's source at
+// the last step of the tile before, its output staged (and, without store
+// waves, stored) at its last. Matrices are dealt to XCDs (workgroup b runs
+// on XCD b % 8) so that the 8 heads sharing one matrix's A factors run on
+// one XCD and re-read them from its L2.
 #include "kernels_common.h"
 #include "launch.h"
 
