@@ -151,3 +151,33 @@ def test_materialize_full_size_sampled():
         got_m = lowrank.as_matrix(first[l])[rows]
         a_rows = to_host(A[l])[:, rows]
         check_matrix(got_m, src_m, a_rows, to_host(R[l]), wh[l], r, f"full size layer {l}")
+
+
+def test_materialize_back_to_back_calls_agree():
+    """Eight calls queued back to back at the benchmark's launch (compute
+    waves handing staged blocks to store waves through LDS flags), each into
+    its own output, with no synchronisation between them: all eight are
+    byte-identical to a call made alone, and its rows match the oracle."""
+    w8 = synth.WORKLOADS[3]
+    L, H, T, d = w8.shape
+    shape = (4, H, T, d)
+    V, r = 10, 32
+    kd, _ = synth.kv_tensors_torch(w8, 1, DEV)
+    kd = kd[:4].contiguous()
+    A, R, wt = synth.anchor_factors_torch(1, 6, 4, V, T, H * d, r, device=DEV)
+    alone = torch.empty_like(kd)
+    say("lowrank back to back", shape, V, r)
+    kv.kvc_lowrank_materialize(shape, r, V, kd, A, R, wt, alone)
+    torch.cuda.synchronize()
+    outs = [torch.full_like(kd, float("nan")) for _ in range(8)]
+    for o in outs:
+        kv.kvc_lowrank_materialize(shape, r, V, kd, A, R, wt, o)
+    torch.cuda.synchronize()
+    ref = to_host(alone)
+    for i, o in enumerate(outs):
+        assert np.array_equal(to_host(o), ref), f"call {i}"
+    g = np.random.default_rng(1)
+    rows = np.sort(g.choice(T, 64, replace=False))
+    rows[:2] = [0, T - 1]
+    check_matrix(lowrank.as_matrix(ref[2])[rows], lowrank.as_matrix(to_host(kd[2]))[rows],
+                 to_host(A[2])[:, rows], to_host(R[2]), wt.cpu().numpy()[2], r, "back to back layer 2")
